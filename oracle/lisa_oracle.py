@@ -1,0 +1,372 @@
+"""Plain float64 CPU oracle for one LISA attention layer.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It shares no code with the HIP
+library and the library never calls it.
+
+Source: "LISA: Linear-Indexed Sparse Attention for Efficient Long-Context
+Reasoning" (arXiv 2607.19358v1), cited below as [LISA] with its section or
+equation.
+
+Everything is computed in float64 from the exact values of the inputs
+(bf16 or fp32 storage values upcast without rounding).  The code follows the
+plain definitions one row at a time; numpy matrix products serve as single
+steps.  Conventions fixed where the paper is silent are listed next to the
+function that uses them:
+
+* Indexer score of key j for query t: sum over index heads h of
+  ``w_h * ReLU(q_I[t,h] . k_I[j, h*H_Ik//H_I])`` ([LISA] §3.2 Stage 2, the
+  ReLU dot-product score under Eq. 2, summed over the K indexer heads).
+* Candidate keys of query t are positions 0..t (the current token included).
+* Top-M keeps the min(M, t+1) largest scores; equal scores are ordered by
+  position, the larger position first; -0.0 equals +0.0.  The index set is
+  returned in ascending order.
+* Sparse attention is softmax attention with scale 1/sqrt(d) over the
+  selected keys, query head h reading KV head h*H_kv//H_q ([LISA] §3.1
+  Softmax Attention; §3.2 Stage 2).
+* Linear branch: feature map phi(x) = elu(x)+1, state
+  ``S_t = S_0 + sum_{i<=t} phi(k_i)^T v_i``, normaliser
+  ``z_t = z_0 + sum_{i<=t} phi(k_i)``, output
+  ``phi(q_t) S_t / (phi(q_t) . z_t)`` ([LISA] §3.1 Linear Attention; §3.3
+  Eqs. 3-4, read as inclusive of the current token).  With
+  ``normalized=False`` the output is ``phi(q_t) S_t`` (Eq. 4 literally).
+* Gate ``g = sigmoid(x . W_g[:, h])``, one scalar per token and query head,
+  and ``out = g * O_sparse + (1-g) * O_linear`` ([LISA] §3.2 Eq. 1 and §3.3
+  Eq. 5; the gate weights the sparse branch here, which is Eq. 1 with W_g
+  negated).
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "phi", "index_scores", "select_topm", "sparse_attention", "gate",
+    "linear_recurrent", "linear_rows", "linear_chunked", "linear_state_update",
+    "prefill", "prefill_rows", "decode_step", "dense_decode",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# elementwise pieces
+# ----------------------------------------------------------------------------
+def phi(x) -> np.ndarray:
+    """elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise."""
+    x = _f64(x)
+    return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def gate(x, w_gate) -> np.ndarray:
+    """g[..., h] = 1 / (1 + exp(-(x . W_g[:, h]))).  [LISA] §3.3 Eq. 5.
+
+    x: [..., hidden]; w_gate: [hidden, H_q].
+    """
+    a = _f64(x) @ _f64(w_gate)
+    return 1.0 / (1.0 + np.exp(-a))
+
+
+# ----------------------------------------------------------------------------
+# indexer and selection ([LISA] §3.2 Stage 2)
+# ----------------------------------------------------------------------------
+def index_scores(q_idx, k_idx, w_idx) -> np.ndarray:
+    """Scores of every key for one query.
+
+    q_idx: [H_I, d_I]; k_idx: [L, H_Ik, d_I]; w_idx: [H_I].
+    Returns s[j] = sum_h w_h * max(0, q_idx[h] . k_idx[j, h*H_Ik//H_I]).
+    """
+    q = _f64(q_idx)
+    k = _f64(k_idx)
+    w = _f64(w_idx)
+    H_I = q.shape[0]
+    H_Ik = k.shape[1]
+    s = np.zeros(k.shape[0], dtype=np.float64)
+    for h in range(H_I):
+        dots = k[:, (h * H_Ik) // H_I, :] @ q[h]
+        s += w[h] * np.maximum(dots, 0.0)
+    return s
+
+
+def select_topm(scores, M: int) -> np.ndarray:
+    """Ascending positions of the min(M, L) largest scores.
+
+    Order: score descending, then position descending (a tie goes to the
+    later token).  Comparison is numeric, so -0.0 and +0.0 tie.
+    """
+    s = np.asarray(scores)
+    L = s.shape[0]
+    m = min(int(M), L)
+    if m <= 0:
+        return np.zeros((0,), dtype=np.int64)
+    pos = np.arange(L, dtype=np.int64)
+    # np.lexsort: the last key is the primary key, each sorted ascending.
+    order = np.lexsort((-pos, -s.astype(np.float64)))
+    return np.sort(order[:m])
+
+
+# ----------------------------------------------------------------------------
+# sparse softmax attention ([LISA] §3.1 Softmax Attention, §3.2 SA_M)
+# ----------------------------------------------------------------------------
+def sparse_attention(q, K, V, P) -> np.ndarray:
+    """Softmax attention of one token's query heads over the keys in P.
+
+    q: [H_q, d]; K, V: [L, H_kv, d]; P: positions (any order, no repeats).
+    Query head h reads KV head h*H_kv//H_q; scale 1/sqrt(d).
+    """
+    q = _f64(q)
+    H_q, d = q.shape
+    H_kv = K.shape[1]
+    P = np.asarray(P, dtype=np.int64)
+    out = np.zeros((H_q, d), dtype=np.float64)
+    if P.size == 0:
+        return out
+    for g in range(H_kv):
+        heads = [h for h in range(H_q) if (h * H_kv) // H_q == g]
+        Kg = _f64(K[P, g, :])            # [m, d]
+        Vg = _f64(V[P, g, :])
+        a = q[heads] @ Kg.T / np.sqrt(d)   # [heads, m]
+        a -= a.max(axis=1, keepdims=True)
+        p = np.exp(a)
+        p /= p.sum(axis=1, keepdims=True)
+        out[heads] = p @ Vg
+    return out
+
+
+# ----------------------------------------------------------------------------
+# linear-attention branch ([LISA] §3.1 Linear Attention, §3.3 Eqs. 3-4)
+# ----------------------------------------------------------------------------
+def _linear_out(fq, S, z, normalized: bool) -> np.ndarray:
+    num = np.einsum("hd,hde->he", fq, S)
+    if not normalized:
+        return num
+    den = np.einsum("hd,hd->h", fq, z)
+    return num / den[:, None]
+
+
+def linear_recurrent(q_lin, k_lin, v_lin, S0, z0, normalized: bool = True):
+    """Token-by-token recurrence: update with token t, then read with q_t.
+
+    q_lin, k_lin, v_lin: [n, H, d]; S0: [H, d, d] (rows index phi(k),
+    columns index v); z0: [H, d].  Returns (O [n, H, d], S_n, z_n).
+    """
+    S = _f64(S0).copy()
+    z = _f64(z0).copy()
+    n, H, d = np.shape(q_lin)
+    out = np.zeros((n, H, d), dtype=np.float64)
+    for t in range(n):
+        fk = phi(k_lin[t])
+        v = _f64(v_lin[t])
+        S += fk[:, :, None] * v[:, None, :]
+        z += fk
+        out[t] = _linear_out(phi(q_lin[t]), S, z, normalized)
+    return out, S, z
+
+
+def linear_rows(q_lin, k_lin, v_lin, S0, z0, rows: Iterable[int],
+                normalized: bool = True):
+    """Outputs of selected rows from the closed form of Eq. 3.
+
+    ``S_t = S_0 + phi(K[:t+1])^T V[:t+1]``, accumulated over the gaps
+    between consecutive requested rows.  Returns (dict row -> [H, d],
+    S_n, z_n) where S_n, z_n cover all n tokens.
+    """
+    rows = sorted(set(int(r) for r in rows))
+    n = np.shape(k_lin)[0]
+    S = _f64(S0).copy()
+    z = _f64(z0).copy()
+    done = 0
+    res: Dict[int, np.ndarray] = {}
+
+    def absorb(lo, hi):
+        if hi <= lo:
+            return
+        fk = phi(k_lin[lo:hi])            # [m, H, d]
+        v = _f64(v_lin[lo:hi])
+        S[...] += np.einsum("mhd,mhe->hde", fk, v, optimize=True)
+        z[...] += fk.sum(axis=0)
+
+    for t in rows:
+        absorb(done, t + 1)
+        done = t + 1
+        res[t] = _linear_out(phi(q_lin[t]), S, z, normalized)
+    absorb(done, n)
+    return res, S, z
+
+
+def linear_chunked(q_lin, k_lin, v_lin, S0, z0, chunk: int = 64,
+                   normalized: bool = True):
+    """Chunked-parallel form of the same recurrence (self-check only).
+
+    Per chunk: A = (phi(Q_c) phi(K_c)^T) masked to j <= i (diagonal kept);
+    numerator A V_c + phi(Q_c) S, denominator A 1 + phi(Q_c) z; then the
+    chunk's phi(K_c)^T V_c and phi(K_c)^T 1 are added to S and z.
+    """
+    S = _f64(S0).copy()
+    z = _f64(z0).copy()
+    n, H, d = np.shape(q_lin)
+    out = np.zeros((n, H, d), dtype=np.float64)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        fq = phi(q_lin[c0:c1]).transpose(1, 0, 2)   # [H, c, d]
+        fk = phi(k_lin[c0:c1]).transpose(1, 0, 2)
+        v = _f64(v_lin[c0:c1]).transpose(1, 0, 2)
+        A = fq @ fk.transpose(0, 2, 1)               # [H, c, c]
+        A = np.tril(A)
+        num = A @ v + fq @ S
+        if normalized:
+            den = A.sum(axis=2) + np.einsum("hcd,hd->hc", fq, z)
+            o = num / den[:, :, None]
+        else:
+            o = num
+        out[c0:c1] = o.transpose(1, 0, 2)
+        S += fk.transpose(0, 2, 1) @ v
+        z += fk.sum(axis=1)
+    return out, S, z
+
+
+def linear_state_update(k_lin, v_lin, S0, z0):
+    """S += sum_t phi(k_t)^T v_t, z += sum_t phi(k_t).  k_lin, v_lin: [n, H, d]."""
+    fk = phi(k_lin)
+    v = _f64(v_lin)
+    S = _f64(S0) + np.einsum("nhd,nhe->hde", fk, v, optimize=True)
+    z = _f64(z0) + fk.sum(axis=0)
+    return S, z
+
+
+# ----------------------------------------------------------------------------
+# whole layer
+# ----------------------------------------------------------------------------
+def _row_select(q_idx_t, k_idx, w_idx, t: int, M: int, scores_dtype=None):
+    s = index_scores(q_idx_t, k_idx[: t + 1], w_idx)
+    if scores_dtype is not None:
+        s = s.astype(scores_dtype)
+    return select_topm(s, M), s
+
+
+def prefill_rows(inp: Dict[str, np.ndarray], M: int, rows: Sequence[int],
+                 b: int = 0, normalized: bool = True,
+                 select_on=None) -> Dict[str, object]:
+    """Outputs of chosen query rows of a causal prefill of sequence ``b``.
+
+    ``inp`` holds the arrays of a prefill input set (shapes [B, n, ...]).
+    ``select_on``: None selects on float64 scores; np.float32 selects on the
+    scores rounded to float32 (as a GPU select kernel sees them).
+    Returns dict with 'out' {row: [H_q, d]}, 'idx' {row: positions},
+    'scores' {row: float64 scores}, 'S', 'z' (state after all n tokens).
+    """
+    q, K, V = inp["q"][b], inp["k"][b], inp["v"][b]
+    q_idx, k_idx, w_idx = inp["q_idx"][b], inp["k_idx"][b], inp["w_idx"]
+    rows = sorted(set(int(r) for r in rows))
+    lin, S, z = linear_rows(inp["q_lin"][b], inp["k_lin"][b], inp["v_lin"][b],
+                            inp["S0"][b], inp["z0"][b], rows, normalized)
+    g = gate(inp["x"][b][rows], inp["w_gate"])      # [r, H_q]
+    out, idx, sc = {}, {}, {}
+    for i, t in enumerate(rows):
+        P, s = _row_select(q_idx[t], k_idx, w_idx, t, M, select_on)
+        o_s = sparse_attention(q[t], K, V, P)
+        o_l = lin[t]
+        out[t] = g[i][:, None] * o_s + (1.0 - g[i][:, None]) * o_l
+        idx[t] = P
+        sc[t] = s
+    return {"out": out, "idx": idx, "scores": sc, "S": S, "z": z}
+
+
+def prefill(inp: Dict[str, np.ndarray], M: int, normalized: bool = True,
+            select_on=None) -> Dict[str, object]:
+    """Full causal prefill of every sequence (small sizes).
+
+    Returns 'out' [B, n, H_q, d], 'idx' list (per b) of lists of arrays,
+    'S' [B, H, d, d], 'z' [B, H, d], plus 'o_sparse', 'o_linear', 'g'.
+    """
+    B, n = inp["q"].shape[:2]
+    H_q, d = inp["q"].shape[2:]
+    out = np.zeros((B, n, H_q, d))
+    o_sp = np.zeros((B, n, H_q, d))
+    o_li = np.zeros((B, n, H_q, d))
+    gs = np.zeros((B, n, H_q))
+    S_all, z_all, idx_all = [], [], []
+    for b in range(B):
+        o_l, S, z = linear_recurrent(inp["q_lin"][b], inp["k_lin"][b], inp["v_lin"][b],
+                                     inp["S0"][b], inp["z0"][b], normalized)
+        g = gate(inp["x"][b], inp["w_gate"])
+        idx_b = []
+        for t in range(n):
+            P, _ = _row_select(inp["q_idx"][b][t], inp["k_idx"][b], inp["w_idx"], t, M,
+                               select_on)
+            o_s = sparse_attention(inp["q"][b][t], inp["k"][b], inp["v"][b], P)
+            o_sp[b, t] = o_s
+            idx_b.append(P)
+        o_li[b] = o_l
+        gs[b] = g
+        out[b] = g[:, :, None] * o_sp[b] + (1.0 - g[:, :, None]) * o_l
+        S_all.append(S)
+        z_all.append(z)
+        idx_all.append(idx_b)
+    return {"out": out, "idx": idx_all, "S": np.stack(S_all), "z": np.stack(z_all),
+            "o_sparse": o_sp, "o_linear": o_li, "g": gs}
+
+
+def decode_step(inp: Dict[str, np.ndarray], M: int, normalized: bool = True,
+                select_on=None, batch: Optional[Iterable[int]] = None) -> Dict[str, object]:
+    """One decode step for every sequence (or those in ``batch``).
+
+    The caches hold rows 0..L_b-2; the new token's k, v, k_I become row
+    L_b-1 ([LISA] §3.2 Stage 2: the KV cache covers the full context).
+    The indexer then scores rows 0..L_b-1, the top-M rows feed the sparse
+    attention, the linear state absorbs the new token before it is read,
+    and the gate mixes the two branches.
+    Returns 'out' [B', H_q, d], 'idx' list, 'scores' list, 'S', 'z'.
+    """
+    seq_lens = np.asarray(inp["seq_lens"])
+    bs = list(range(len(seq_lens))) if batch is None else list(batch)
+    outs, idxs, scs, Ss, zs, osp, oli, gg = [], [], [], [], [], [], [], []
+    for b in bs:
+        L = int(seq_lens[b])
+        k_idx = np.array(inp["k_idx_cache"][b, :L], dtype=np.float64)
+        k_idx[L - 1] = inp["k_idx_new"][b]
+        K = np.array(inp["k_cache"][b, :L], dtype=np.float64)
+        V = np.array(inp["v_cache"][b, :L], dtype=np.float64)
+        K[L - 1] = inp["k_new"][b]
+        V[L - 1] = inp["v_new"][b]
+        s = index_scores(inp["q_idx"][b], k_idx, inp["w_idx"])
+        P = select_topm(s if select_on is None else s.astype(select_on), M)
+        o_s = sparse_attention(inp["q"][b], K, V, P)
+        fk = phi(inp["k_lin"][b])
+        S = _f64(inp["S0"][b]) + fk[:, :, None] * _f64(inp["v_lin"][b])[:, None, :]
+        z = _f64(inp["z0"][b]) + fk
+        o_l = _linear_out(phi(inp["q_lin"][b]), S, z, normalized)
+        g = gate(inp["x"][b], inp["w_gate"])          # [H_q]
+        outs.append(g[:, None] * o_s + (1.0 - g[:, None]) * o_l)
+        idxs.append(P)
+        scs.append(s)
+        Ss.append(S)
+        zs.append(z)
+        osp.append(o_s)
+        oli.append(o_l)
+        gg.append(g)
+    return {"out": np.stack(outs), "idx": idxs, "scores": scs, "S": np.stack(Ss),
+            "z": np.stack(zs), "o_sparse": np.stack(osp), "o_linear": np.stack(oli),
+            "g": np.stack(gg)}
+
+
+def dense_decode(inp: Dict[str, np.ndarray], batch: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Full causal softmax attention of the new token over rows 0..L_b-1.
+
+    Caches as in ``decode_step`` (the new k, v appended at row L_b-1).
+    Returns [B', H_q, d].
+    """
+    seq_lens = np.asarray(inp["seq_lens"])
+    bs = list(range(len(seq_lens))) if batch is None else list(batch)
+    outs = []
+    for b in bs:
+        L = int(seq_lens[b])
+        K = np.array(inp["k_cache"][b, :L], dtype=np.float64)
+        V = np.array(inp["v_cache"][b, :L], dtype=np.float64)
+        K[L - 1] = inp["k_new"][b]
+        V[L - 1] = inp["v_new"][b]
+        outs.append(sparse_attention(inp["q"][b], K, V, np.arange(L)))
+    return np.stack(outs)
