@@ -1,0 +1,490 @@
+// C-ABI host layer of the LISA library: argument validation, workspace
+// layout, launch sequencing, error state and the kernel timing hook.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "lisa.h"
+#include "lisa_kernels.h"
+#include "lisa_prefill.h"
+
+using namespace lisa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(LISA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int MAX_ROW = 65536;  // longest score row the select kernel holds
+
+// ---------------------------------------------------------------------------
+// shape validation
+// ---------------------------------------------------------------------------
+int check_shape(const lisa_shape* s, Shape& o) {
+  if (!s) return fail(LISA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->dtype != LISA_F32 && s->dtype != LISA_BF16) return fail(LISA_ERR_INVALID_ARG, "dtype %d", s->dtype);
+  if (s->flags & ~LISA_LINEAR_UNNORMALIZED) return fail(LISA_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
+  if (s->B < 1 || s->H_q < 1 || s->H_kv < 1 || s->d < 1 || s->H_I < 1 || s->H_Ik < 1 || s->d_I < 1 ||
+      s->H_L < 1 || s->hidden < 1 || s->M < 1 || s->cap < 1)
+    return fail(LISA_ERR_INVALID_ARG, "every count must be >= 1");
+  if (s->H_q % s->H_kv) return fail(LISA_ERR_INVALID_ARG, "H_q %% H_kv != 0");
+  if (s->H_I % s->H_Ik) return fail(LISA_ERR_INVALID_ARG, "H_I %% H_Ik != 0");
+  if (s->H_L != s->H_q) return fail(LISA_ERR_INVALID_ARG, "H_L (%d) must equal H_q (%d)", s->H_L, s->H_q);
+  if (s->chunk != 0 && s->chunk != 64) return fail(LISA_ERR_UNSUPPORTED, "chunk %d (64 only)", s->chunk);
+  if (s->d != 32 && s->d != 64 && s->d != 128) return fail(LISA_ERR_UNSUPPORTED, "head dim %d", s->d);
+  if (s->H_q / s->H_kv > 8) return fail(LISA_ERR_UNSUPPORTED, "more than 8 query heads per KV head");
+  if (s->H_q > 64) return fail(LISA_ERR_UNSUPPORTED, "more than 64 query heads");
+  const int R = s->H_I / s->H_Ik;
+  if (R != 1 && R != 2 && R != 4) return fail(LISA_ERR_UNSUPPORTED, "H_I / H_Ik = %d", R);
+  const int VEC = s->dtype == LISA_F32 ? 4 : 8;
+  if (s->d_I % VEC || !is_pow2(s->d_I / VEC) || !is_pow2(s->H_Ik) || s->H_Ik * s->d_I / VEC > 64)
+    return fail(LISA_ERR_UNSUPPORTED, "index key row H_Ik*d_I = %d", s->H_Ik * s->d_I);
+  o.B = s->B; o.H_q = s->H_q; o.H_kv = s->H_kv; o.d = s->d; o.H_I = s->H_I; o.H_Ik = s->H_Ik;
+  o.d_I = s->d_I; o.H_L = s->H_L; o.hidden = s->hidden; o.M = s->M; o.cap = s->cap;
+  o.max_len = s->max_len; o.chunk = s->chunk ? s->chunk : 64; o.dtype = s->dtype; o.flags = s->flags;
+  return LISA_OK;
+}
+
+int check_decode_len(const Shape& sh) {
+  if (sh.max_len < 1 || sh.max_len > sh.cap)
+    return fail(LISA_ERR_INVALID_ARG, "max_len %d outside [1, cap=%d]", sh.max_len, sh.cap);
+  if (sh.max_len > MAX_ROW) return fail(LISA_ERR_UNSUPPORTED, "max_len %d > %d", sh.max_len, MAX_ROW);
+  return LISA_OK;
+}
+
+int check_prefill_len(const Shape& sh, int n) {
+  if (n < 1 || n > sh.cap) return fail(LISA_ERR_INVALID_ARG, "n %d outside [1, cap=%d]", n, sh.cap);
+  if (n > MAX_ROW) return fail(LISA_ERR_UNSUPPORTED, "n %d > %d", n, MAX_ROW);
+  return LISA_OK;
+}
+
+#define REQUIRE_PTR(p)                                                                   \
+  do {                                                                                   \
+    if (!(p)) return fail(LISA_ERR_INVALID_ARG, "%s is NULL", #p);                      \
+    if (!aligned16(p)) return fail(LISA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+#define OPTIONAL_PTR(p)                                                                      \
+  do {                                                                                       \
+    if ((p) && !aligned16(p)) return fail(LISA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// workspace layouts
+// ---------------------------------------------------------------------------
+int64_t decode_scores_ld(const Shape& sh) { return (int64_t)align_up((size_t)sh.max_len, 64); }
+
+void decode_split(const Shape& sh, int positions, int& nsplit, int& split_len) {
+  int sl = 64;
+  while ((positions + sl - 1) / sl > 32) sl *= 2;
+  while ((size_t)sh.B * sh.H_kv * ((positions + sl - 1) / sl) > 4096 && sl < positions) sl *= 2;
+  split_len = sl;
+  nsplit = (positions + sl - 1) / sl;
+}
+
+int decode_gate_chunks(const Shape& sh) { return (sh.hidden + 255) / 256; }
+
+struct DecodeWs {
+  size_t scores, idx, o_lin, lin_den, gate, part, counters, total;
+  int nsplit, split_len;
+};
+
+DecodeWs decode_ws(const Shape& sh) {
+  DecodeWs w;
+  Layout L;
+  decode_split(sh, sh.M < sh.max_len ? sh.M : sh.max_len, w.nsplit, w.split_len);
+  w.scores = L.take((size_t)sh.B * decode_scores_ld(sh) * 4);
+  w.idx = L.take((size_t)sh.B * sh.M * 4);
+  w.o_lin = L.take((size_t)sh.B * sh.H_L * sh.d * 4);
+  w.lin_den = L.take((size_t)sh.B * sh.H_L * 4);
+  w.gate = L.take((size_t)sh.B * decode_gate_chunks(sh) * sh.H_q * 4);
+  w.part = L.take(attention_partial_floats(sh, sh.B, w.nsplit) * 4);
+  w.counters = L.take((size_t)sh.B * sh.H_kv * 4);
+  w.total = L.off;
+  return w;
+}
+
+struct DenseWs {
+  size_t part, counters, total;
+  int nsplit, split_len;
+};
+
+DenseWs dense_ws(const Shape& sh) {
+  DenseWs w;
+  Layout L;
+  decode_split(sh, sh.max_len, w.nsplit, w.split_len);
+  w.part = L.take(attention_partial_floats(sh, sh.B, w.nsplit) * 4);
+  w.counters = L.take((size_t)sh.B * sh.H_kv * 4);
+  w.total = L.off;
+  return w;
+}
+
+int64_t prefill_scores_ld(int n) { return (int64_t)align_up((size_t)n, 64); }
+
+struct PrefillWs {
+  size_t scores, idx, o_lin, gate, z_tmp, total;
+};
+
+PrefillWs prefill_ws(const Shape& sh, int n) {
+  PrefillWs w;
+  Layout L;
+  const int srows = n > sh.M ? n - sh.M : 0;
+  w.scores = L.take((size_t)sh.B * srows * prefill_scores_ld(n) * 4);
+  w.idx = L.take((size_t)sh.B * n * sh.M * 4);
+  w.o_lin = L.take((size_t)sh.B * n * sh.H_L * sh.d * 4);
+  w.gate = L.take((size_t)sh.B * n * sh.H_q * 4);
+  w.z_tmp = L.take((size_t)sh.B * sh.H_L * sh.d * 4);
+  w.total = L.off;
+  return w;
+}
+
+struct TopkWs {
+  size_t scores, total;
+};
+
+TopkWs topk_ws(const Shape& sh, int rows_mode, int n) {
+  TopkWs w;
+  Layout L;
+  if (rows_mode == LISA_ROWS_DECODE) {
+    w.scores = L.take((size_t)sh.B * decode_scores_ld(sh) * 4);
+  } else {
+    const int srows = n > sh.M ? n - sh.M : 0;
+    w.scores = L.take((size_t)sh.B * srows * prefill_scores_ld(n) * 4);
+  }
+  w.total = L.off;
+  return w;
+}
+
+template <typename P> P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(ws) + off); }
+
+// ---------------------------------------------------------------------------
+// timing hook
+// ---------------------------------------------------------------------------
+struct Timing {
+  int kid = -1;
+  hipEvent_t* starts = nullptr;
+  hipEvent_t* stops = nullptr;
+  int n = 0;
+  int count = 0;
+} g_timing;
+
+const char* const kKernelNames[KID_COUNT] = {
+    "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
+    "prefill_linear", "prefill_attention", "linear_state_update", "zero_counters"};
+
+bool timing_on(int kid) { return g_timing.kid == kid && g_timing.count < g_timing.n; }
+
+#define LAUNCH(kid, st, call)                                                       \
+  do {                                                                              \
+    const bool timed_ = timing_on(kid);                                             \
+    if (timed_) (void)hipEventRecord(g_timing.starts[g_timing.count], (st));        \
+    const hipError_t e_ = (call);                                                   \
+    if (timed_) {                                                                   \
+      (void)hipEventRecord(g_timing.stops[g_timing.count], (st));                   \
+      ++g_timing.count;                                                             \
+    }                                                                               \
+    if (e_ != hipSuccess) return fail_hip(e_, kKernelNames[kid]);                   \
+  } while (0)
+
+}  // namespace
+
+// ===========================================================================
+// exported entry points
+// ===========================================================================
+extern "C" {
+
+const char* lisa_status_string(int status) {
+  switch (status) {
+    case LISA_OK: return "ok";
+    case LISA_ERR_INVALID_ARG: return "invalid argument";
+    case LISA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LISA_ERR_WORKSPACE: return "workspace too small";
+    case LISA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* lisa_last_error(void) { return g_err.c_str(); }
+
+const char* lisa_kernel_name(int kernel_id) {
+  if (kernel_id < 0 || kernel_id >= KID_COUNT) return nullptr;
+  return kKernelNames[kernel_id];
+}
+
+int lisa_timing_enable(int kernel_id, void** start_events, void** stop_events, int n) {
+  if (n == 0) {
+    g_timing = Timing();
+    return LISA_OK;
+  }
+  if (kernel_id < 0 || kernel_id >= KID_COUNT || !start_events || !stop_events || n < 0)
+    return fail(LISA_ERR_INVALID_ARG, "bad timing request");
+  g_timing.kid = kernel_id;
+  g_timing.starts = reinterpret_cast<hipEvent_t*>(start_events);
+  g_timing.stops = reinterpret_cast<hipEvent_t*>(stop_events);
+  g_timing.n = n;
+  g_timing.count = 0;
+  return LISA_OK;
+}
+
+int lisa_timing_count(void) { return g_timing.count; }
+
+size_t lisa_workspace_bytes(const lisa_shape* shape, int op, int32_t n) {
+  Shape sh;
+  if (check_shape(shape, sh) != LISA_OK) return 0;
+  switch (op) {
+    case LISA_OP_DECODE:
+      if (check_decode_len(sh) != LISA_OK) return 0;
+      return decode_ws(sh).total;
+    case LISA_OP_DENSE_DECODE:
+      if (check_decode_len(sh) != LISA_OK) return 0;
+      return dense_ws(sh).total;
+    case LISA_OP_PREFILL:
+      if (check_prefill_len(sh, n) != LISA_OK) return 0;
+      return prefill_ws(sh, n).total;
+    case LISA_OP_TOPK_DECODE:
+      if (check_decode_len(sh) != LISA_OK) return 0;
+      return topk_ws(sh, LISA_ROWS_DECODE, 0).total;
+    case LISA_OP_TOPK_PREFILL:
+      if (check_prefill_len(sh, n) != LISA_OK) return 0;
+      return topk_ws(sh, LISA_ROWS_PREFILL, n).total;
+    case LISA_OP_LINEAR_UPDATE:
+      return 256;  // no workspace is used; a nonzero size marks a valid shape
+    default:
+      fail(LISA_ERR_INVALID_ARG, "unknown op %d", op);
+      return 0;
+  }
+}
+
+int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const void* q, const void* k_new,
+                     const void* v_new, const void* q_idx, const void* k_idx_new, const void* q_lin,
+                     const void* k_lin, const void* v_lin, const void* x, const void* w_gate,
+                     const float* w_idx, void* k_cache, void* v_cache, void* k_idx_cache, float* S, float* z,
+                     void* out, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if ((rc = check_decode_len(sh))) return rc;
+  REQUIRE_PTR(seq_lens); REQUIRE_PTR(q); REQUIRE_PTR(k_new); REQUIRE_PTR(v_new); REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(k_idx_new); REQUIRE_PTR(q_lin); REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate); REQUIRE_PTR(w_idx); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(k_idx_cache); REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(out); OPTIONAL_PTR(idx_out);
+  REQUIRE_PTR(ws);
+  const DecodeWs w = decode_ws(sh);
+  if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  hipStream_t st = (hipStream_t)stream;
+
+  PhaseAArgs pa{};
+  pa.sh = sh;
+  pa.seq_lens = seq_lens;
+  pa.q_idx = q_idx; pa.k_idx_new = k_idx_new; pa.k_new = k_new; pa.v_new = v_new;
+  pa.q_lin = q_lin; pa.k_lin = k_lin; pa.v_lin = v_lin; pa.x = x; pa.w_gate = w_gate; pa.w_idx = w_idx;
+  pa.k_cache = k_cache; pa.v_cache = v_cache; pa.k_idx_cache = k_idx_cache; pa.S = S; pa.z = z;
+  pa.scores = at<float>(ws, w.scores); pa.scores_ld = decode_scores_ld(sh);
+  pa.o_lin = at<float>(ws, w.o_lin); pa.lin_den = at<float>(ws, w.lin_den);
+  pa.gate_part = at<float>(ws, w.gate); pa.gate_chunks = decode_gate_chunks(sh);
+  pa.counters = at<uint32_t>(ws, w.counters); pa.n_counters = sh.B * sh.H_kv;
+  pa.append = 1; pa.do_scores = 1; pa.do_linear = 1; pa.do_gate = 1; pa.linear_output = 1;
+  LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
+
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, w.idx);
+  SelectArgs sa{};
+  sa.n_rows = sh.B; sa.rows_per_seq = 1; sa.prefill = 0; sa.seq_lens = seq_lens;
+  sa.scores = pa.scores; sa.ld = pa.scores_ld; sa.first_row = 0; sa.stored_rows = 1;
+  sa.M = sh.M; sa.max_len = sh.max_len; sa.idx = idx; sa.idx_ld = sh.M; sa.mask = nullptr;
+  LAUNCH(KID_SELECT, st, launch_select(sa, st));
+
+  AttnArgs aa{};
+  aa.sh = sh; aa.n_rows = sh.B; aa.rows_per_seq = 1; aa.prefill = 0; aa.dense = 0; aa.seq_lens = seq_lens;
+  aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = idx; aa.idx_ld = sh.M;
+  aa.nsplit = w.nsplit; aa.split_len = w.split_len; aa.part = at<float>(ws, w.part);
+  aa.counters = pa.counters; aa.gate_part = pa.gate_part; aa.gate_chunks = pa.gate_chunks;
+  aa.o_lin = pa.o_lin; aa.lin_den = (sh.flags & LISA_LINEAR_UNNORMALIZED) ? nullptr : pa.lin_den; aa.out = out;
+  LAUNCH(KID_ATTN, st, launch_attention(aa, st));
+  return LISA_OK;
+}
+
+int lisa_dense_decode(const lisa_shape* shape, const int32_t* seq_lens, const void* q, const void* k_cache,
+                      const void* v_cache, void* out, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if ((rc = check_decode_len(sh))) return rc;
+  REQUIRE_PTR(seq_lens); REQUIRE_PTR(q); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(out);
+  REQUIRE_PTR(ws);
+  const DenseWs w = dense_ws(sh);
+  if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  hipStream_t st = (hipStream_t)stream;
+  uint32_t* counters = at<uint32_t>(ws, w.counters);
+  LAUNCH(KID_ZERO, st, launch_zero_u32(counters, sh.B * sh.H_kv, st));
+  AttnArgs aa{};
+  aa.sh = sh; aa.n_rows = sh.B; aa.rows_per_seq = 1; aa.prefill = 0; aa.dense = 1; aa.seq_lens = seq_lens;
+  aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = nullptr; aa.idx_ld = 0;
+  aa.nsplit = w.nsplit; aa.split_len = w.split_len; aa.part = at<float>(ws, w.part);
+  aa.counters = counters; aa.gate_part = nullptr; aa.gate_chunks = 0; aa.o_lin = nullptr; aa.lin_den = nullptr;
+  aa.out = out;
+  LAUNCH(KID_ATTN, st, launch_attention(aa, st));
+  return LISA_OK;
+}
+
+int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n, const int32_t* seq_lens,
+                      const void* q_idx, const void* k_idx_cache, const float* w_idx, const float* scores_in,
+                      int64_t scores_ld, float* scores_out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if (rows_mode != LISA_ROWS_DECODE && rows_mode != LISA_ROWS_PREFILL)
+    return fail(LISA_ERR_INVALID_ARG, "rows_mode %d", rows_mode);
+  const bool dec = rows_mode == LISA_ROWS_DECODE;
+  if (dec) {
+    if ((rc = check_decode_len(sh))) return rc;
+    REQUIRE_PTR(seq_lens);
+  } else if ((rc = check_prefill_len(sh, n))) {
+    return rc;
+  }
+  const int longest = dec ? sh.max_len : n;
+  REQUIRE_PTR(idx_out);
+  OPTIONAL_PTR(scores_in);
+  OPTIONAL_PTR(scores_out);
+  if ((scores_in || scores_out) && scores_ld < longest)
+    return fail(LISA_ERR_INVALID_ARG, "scores_ld %lld < longest row %d", (long long)scores_ld, longest);
+  if (!scores_in) {
+    REQUIRE_PTR(q_idx); REQUIRE_PTR(k_idx_cache); REQUIRE_PTR(w_idx);
+  }
+  const TopkWs w = topk_ws(sh, rows_mode, n);
+  if (!scores_in && !scores_out) {
+    REQUIRE_PTR(ws);
+    if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  }
+  hipStream_t st = (hipStream_t)stream;
+
+  SelectArgs sa{};
+  sa.M = sh.M; sa.idx = idx_out; sa.idx_ld = sh.M; sa.mask = nullptr; sa.max_len = longest;
+  if (dec) {
+    sa.n_rows = sh.B; sa.rows_per_seq = 1; sa.prefill = 0; sa.seq_lens = seq_lens;
+    sa.first_row = 0; sa.stored_rows = 1;
+    if (scores_in) {
+      sa.scores = scores_in; sa.ld = scores_ld;
+    } else {
+      PhaseAArgs pa{};
+      pa.sh = sh; pa.seq_lens = seq_lens; pa.q_idx = q_idx; pa.k_idx_new = nullptr; pa.w_idx = w_idx;
+      pa.k_idx_cache = const_cast<void*>(k_idx_cache);
+      pa.scores = scores_out ? scores_out : at<float>(ws, w.scores);
+      pa.scores_ld = scores_out ? scores_ld : decode_scores_ld(sh);
+      pa.do_scores = 1;
+      LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
+      sa.scores = pa.scores; sa.ld = pa.scores_ld;
+    }
+  } else {
+    sa.n_rows = sh.B * n; sa.rows_per_seq = n; sa.prefill = 1; sa.seq_lens = nullptr;
+    if (scores_in) {
+      sa.scores = scores_in; sa.ld = scores_ld; sa.first_row = 0; sa.stored_rows = n;
+    } else {
+      IndexScoreArgs ia{};
+      ia.sh = sh; ia.n = n; ia.q_idx = q_idx; ia.k_idx = k_idx_cache; ia.w_idx = w_idx;
+      if (scores_out) {
+        ia.row0 = 0; ia.stored_rows = n; ia.scores = scores_out; ia.ld = scores_ld;
+      } else {
+        ia.row0 = n > sh.M ? sh.M : n; ia.stored_rows = n > sh.M ? n - sh.M : 0;
+        ia.scores = at<float>(ws, w.scores); ia.ld = prefill_scores_ld(n);
+      }
+      LAUNCH(KID_PREFILL_INDEX, st, launch_index_scores(ia, st));
+      sa.scores = ia.scores; sa.ld = ia.ld; sa.first_row = ia.row0; sa.stored_rows = ia.stored_rows;
+    }
+  }
+  LAUNCH(KID_SELECT, st, launch_select(sa, st));
+  return LISA_OK;
+}
+
+int lisa_linear_state_update(const lisa_shape* shape, int32_t n_tokens, const void* k_lin, const void* v_lin,
+                             float* S, float* z, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if (n_tokens < 1) return fail(LISA_ERR_INVALID_ARG, "n_tokens %d", n_tokens);
+  REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(S); REQUIRE_PTR(z);
+  hipStream_t st = (hipStream_t)stream;
+  LinearArgs la{};
+  la.sh = sh; la.n = n_tokens; la.q_lin = nullptr; la.k_lin = k_lin; la.v_lin = v_lin;
+  la.S = S; la.z_in = z; la.z_out = z; la.o_lin = nullptr;  // without outputs only slice 0 touches z
+  LAUNCH(KID_LINEAR_UPDATE, st, launch_linear_recurrent(la, st));
+  return LISA_OK;
+}
+
+int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* k_cache, const void* v_cache,
+                 const void* k_idx_cache, const void* q_idx, const void* q_lin, const void* k_lin,
+                 const void* v_lin, const void* x, const void* w_gate, const float* w_idx, float* S, float* z,
+                 void* out, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if ((rc = check_prefill_len(sh, n))) return rc;
+  REQUIRE_PTR(q); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(k_idx_cache); REQUIRE_PTR(q_idx);
+  REQUIRE_PTR(q_lin); REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(x); REQUIRE_PTR(w_gate);
+  REQUIRE_PTR(w_idx); REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(out); OPTIONAL_PTR(idx_out); REQUIRE_PTR(ws);
+  const PrefillWs w = prefill_ws(sh, n);
+  if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  hipStream_t st = (hipStream_t)stream;
+
+  GateArgs ga{};
+  ga.sh = sh; ga.n_rows = sh.B * n; ga.x = x; ga.w_gate = w_gate; ga.gate_part = at<float>(ws, w.gate);
+  LAUNCH(KID_PREFILL_GATE, st, launch_gate_logits(ga, st));
+
+  LinearArgs la{};
+  la.sh = sh; la.n = n; la.q_lin = q_lin; la.k_lin = k_lin; la.v_lin = v_lin; la.S = S;
+  la.z_in = z; la.z_out = at<float>(ws, w.z_tmp); la.o_lin = at<float>(ws, w.o_lin);
+  LAUNCH(KID_PREFILL_LINEAR, st, launch_linear_recurrent(la, st));
+  LAUNCH(KID_PREFILL_LINEAR, st, launch_copy_f32(z, la.z_out, (size_t)sh.B * sh.H_L * sh.d, st));
+
+  IndexScoreArgs ia{};
+  ia.sh = sh; ia.n = n; ia.q_idx = q_idx; ia.k_idx = k_idx_cache; ia.w_idx = w_idx;
+  ia.row0 = n > sh.M ? sh.M : n; ia.stored_rows = n > sh.M ? n - sh.M : 0;
+  ia.scores = at<float>(ws, w.scores); ia.ld = prefill_scores_ld(n);
+  LAUNCH(KID_PREFILL_INDEX, st, launch_index_scores(ia, st));
+
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, w.idx);
+  SelectArgs sa{};
+  sa.n_rows = sh.B * n; sa.rows_per_seq = n; sa.prefill = 1; sa.seq_lens = nullptr;
+  sa.scores = ia.scores; sa.ld = ia.ld; sa.first_row = ia.row0; sa.stored_rows = ia.stored_rows;
+  sa.M = sh.M; sa.max_len = n; sa.idx = idx; sa.idx_ld = sh.M; sa.mask = nullptr;
+  LAUNCH(KID_SELECT, st, launch_select(sa, st));
+
+  AttnArgs aa{};
+  aa.sh = sh; aa.n_rows = sh.B * n; aa.rows_per_seq = n; aa.prefill = 1; aa.dense = 0; aa.seq_lens = nullptr;
+  aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = idx; aa.idx_ld = sh.M;
+  aa.nsplit = 1; aa.split_len = sh.M; aa.part = nullptr; aa.counters = nullptr;
+  aa.gate_part = ga.gate_part; aa.gate_chunks = 1; aa.o_lin = la.o_lin; aa.lin_den = nullptr; aa.out = out;
+  LAUNCH(KID_PREFILL_ATTN, st, launch_attention(aa, st));
+  return LISA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Launch interface between the C-ABI host layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lisa {
+
+struct Shape {
+  int B, H_q, H_kv, d, H_I, H_Ik, d_I, H_L, hidden, M, cap, max_len, chunk, dtype;
+  unsigned flags;
+};
+
+enum KernelId {
+  KID_DECODE_PHASE_A = 0,
+  KID_SELECT = 1,
+  KID_ATTN = 2,
+  KID_PREFILL_INDEX = 3,
+  KID_PREFILL_GATE = 4,
+  KID_PREFILL_LINEAR = 5,
+  KID_PREFILL_ATTN = 6,
+  KID_LINEAR_UPDATE = 7,
+  KID_ZERO = 8,
+  KID_COUNT = 9
+};
+
+// ---------------------------------------------------------------------------
+// decode phase A: indexer scan + cache append + linear state + gate partials
+// ---------------------------------------------------------------------------
+struct PhaseAArgs {
+  Shape sh;
+  const int32_t* seq_lens;
+  const void *q_idx, *k_idx_new, *k_new, *v_new;
+  const void *q_lin, *k_lin, *v_lin, *x, *w_gate;
+  const float* w_idx;
+  void *k_cache, *v_cache, *k_idx_cache;
+  float *S, *z;
+  float* scores;       // [B, scores_ld]
+  int64_t scores_ld;
+  float* o_lin;        // [B, H_L, d] numerators phi(q) S_new
+  float* lin_den;      // [B, H_L] denominators phi(q) . z_new (normalised mode)
+  float* gate_part;    // [B, gate_chunks, H_q]  (pre-sigmoid partial dots)
+  int gate_chunks;
+  uint32_t* counters;  // zeroed by this kernel
+  int n_counters;
+  int append;          // write the new token into the caches
+  int do_scores, do_linear, do_gate;
+  int linear_output;   // write o_lin
+};
+hipError_t launch_decode_phase_a(const PhaseAArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// top-M selection of score rows
+// ---------------------------------------------------------------------------
+struct SelectArgs {
+  int n_rows;               // rows to process (decode: B; prefill: B*n)
+  int rows_per_seq;         // decode: 1; prefill: n
+  int prefill;              // row t of a sequence has length t+1
+  const int32_t* seq_lens;  // decode lengths
+  const float* scores;      // row (b, t) at scores + (b*stored_rows + t - first_row)*ld
+  int64_t ld;
+  int first_row;            // first stored score row per sequence (prefill)
+  int stored_rows;          // stored score rows per sequence (prefill)
+  int M;
+  int max_len;              // longest row
+  int32_t* idx;             // [n_rows, idx_ld]
+  int64_t idx_ld;
+  uint32_t* mask;           // nullable [n_rows, mask_ld] selection bitmask
+  int64_t mask_ld;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// gathered GQA softmax attention over selected rows, split + combine + gate
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+  Shape sh;
+  int n_rows;               // query rows (decode: B; prefill: B*n)
+  int rows_per_seq;         // decode: 1; prefill: n
+  int prefill;              // row length t+1 instead of seq_lens[b]
+  int dense;                // positions 0..len-1, no idx
+  const int32_t* seq_lens;
+  const void* q;            // [n_rows, H_q, d]
+  const void *k_cache, *v_cache;
+  const int32_t* idx;       // [n_rows, idx_ld]
+  int64_t idx_ld;
+  int nsplit, split_len;    // positions per split
+  float* part;              // partials
+  uint32_t* counters;       // [n_rows, H_kv] when nsplit > 1
+  const float* gate_part;   // nullable [n_rows, gate_chunks, H_q] pre-sigmoid
+  int gate_chunks;
+  const float* o_lin;       // [n_rows, H_q, d] (with gate)
+  const float* lin_den;     // nullable [n_rows, H_q]: o_lin is divided by it
+  void* out;                // [n_rows, H_q, d] T
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit);
+
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t st);
+
+}  // namespace lisa

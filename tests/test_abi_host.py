@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function declared in include/lisa.h,
+size its workspaces, and reject bad arguments on the host with a status code
+before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_lightning_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from long_context_attention_lightning_amd import build as B
+        B.build()
+    return L.library()
+
+
+def _declared():
+    txt = open(os.path.join(ROOT, "include", "lisa.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lisa_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+    assert set(names) == set(L.EXPORTED_SYMBOLS)
+
+
+def _c1(**kw):
+    base = dict(B=1, H_q=28, H_kv=4, d=128, H_I=4, H_Ik=4, d_I=64, hidden=3584, M=2048,
+                cap=16384, max_len=16384)
+    base.update(kw)
+    return L.make_shape(**base)
+
+
+def test_workspace_sizes(lib):
+    sh = _c1()
+    dec = L.lisa_workspace_bytes(sh, L.LISA_OP_DECODE)
+    assert dec > 16384 * 4          # holds at least one score row
+    pre = L.lisa_workspace_bytes(sh, L.LISA_OP_PREFILL, 16384)
+    assert pre > (16384 - 2048) * 16384 * 4
+    assert L.lisa_workspace_bytes(_c1(B=32), L.LISA_OP_DECODE) > 30 * dec // 2
+    assert L.lisa_workspace_bytes(sh, L.LISA_OP_DENSE_DECODE) > 0
+    assert L.lisa_workspace_bytes(sh, L.LISA_OP_TOPK_PREFILL, 4096) > 0
+    assert L.lisa_workspace_bytes(sh, 99) == 0
+    assert "op" in L.lisa_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H_kv=5), L.LisaError),
+    (dict(H_L=27), L.LisaError),
+    (dict(M=0), L.LisaError),
+    (dict(d=96), L.LisaError),
+    (dict(max_len=20000), L.LisaError),
+    (dict(H_Ik=3), L.LisaError),
+    (dict(dtype=7), L.LisaError),
+])
+def test_bad_shapes_are_rejected(lib, kw, code):
+    sh = _c1(**{k: v for k, v in kw.items() if k != "dtype"})
+    if "dtype" in kw:
+        sh.dtype = kw["dtype"]
+    assert L.lisa_workspace_bytes(sh, L.LISA_OP_DECODE) == 0
+    assert L.lisa_last_error() != ""
+
+
+def test_unsupported_vs_invalid_codes(lib):
+    f = lib.lisa_workspace_bytes
+    sh = _c1(d=96)
+    assert f(ctypes.byref(sh), 0, 0) == 0
+    assert "head dim" in L.lisa_last_error()
+    assert L.lisa_status_string(-2) == "unsupported configuration"
+    assert L.lisa_status_string(-1) == "invalid argument"
+    assert L.lisa_status_string(-3) == "workspace too small"
+    assert L.lisa_status_string(-4) == "HIP error"
+
+
+def _call_decode(sh, ptr=16, ws_bytes=1 << 40, **over):
+    args = dict(seq_lens=ptr, q=ptr, k_new=ptr, v_new=ptr, q_idx=ptr, k_idx_new=ptr, q_lin=ptr,
+                k_lin=ptr, v_lin=ptr, x=ptr, w_gate=ptr, w_idx=ptr, k_cache=ptr, v_cache=ptr,
+                k_idx_cache=ptr, S=ptr, z=ptr, out=ptr, idx_out=None, ws=ptr)
+    args.update(over)
+    lib = L.library()
+    return lib.lisa_decode_step(ctypes.byref(sh), *args.values(), ws_bytes, None)
+
+
+def test_decode_rejects_null_misaligned_and_small_workspace(lib):
+    sh = _c1()
+    assert _call_decode(sh, q=None) == -1
+    assert "q is NULL" in L.lisa_last_error()
+    assert _call_decode(sh, k_cache=24) == -1
+    assert "aligned" in L.lisa_last_error()
+    assert _call_decode(sh, ws_bytes=100) == -3
+    assert _call_decode(_c1(H_q=27, H_kv=4)) == -1
+    assert _call_decode(_c1(H_q=72, H_kv=8)) == -2
+
+
+def test_prefill_and_topk_reject_bad_lengths(lib):
+    sh = _c1()
+    p = 16
+    rc = lib.lisa_prefill(ctypes.byref(sh), 0, *([p] * 16), 1 << 40, None)
+    assert rc == -1 and "n 0" in L.lisa_last_error()
+    rc = lib.lisa_prefill(ctypes.byref(sh), 20000, *([p] * 16), 1 << 40, None)
+    assert rc == -1
+    rc = lib.lisa_indexer_topk(ctypes.byref(sh), 7, 10, p, p, p, p, None, 0, None, p, p, 1 << 40, None)
+    assert rc == -1 and "rows_mode" in L.lisa_last_error()
+    rc = lib.lisa_indexer_topk(ctypes.byref(sh), L.LISA_ROWS_DECODE, 0, p, p, p, p, p, 100, None, p, p,
+                               1 << 40, None)
+    assert rc == -1 and "scores_ld" in L.lisa_last_error()
+    rc = lib.lisa_linear_state_update(ctypes.byref(sh), 0, p, p, p, p, None)
+    assert rc == -1
+
+
+def test_kernel_names(lib):
+    names = [L.lisa_kernel_name(i) for i in range(9)]
+    assert names[0] == "decode_phase_a" and None not in names
+    assert L.lisa_kernel_name(99) is None

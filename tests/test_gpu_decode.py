@@ -1,0 +1,114 @@
+"""Decode-step parity of the HIP path (lisa_decode_step, lisa_dense_decode)
+against the fp64 oracle on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from lisa_inputs import CONFIGS, decode_inputs
+from gpu_helpers import (RECALL_MIN, assert_out_close, assert_state_close, check_idx_format,
+                         gpu_decode, gpu_dense_decode, out_errors, recall, host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(cfg, inp, M, label, flags=0):
+    g = gpu_decode(cfg, inp, M=M, flags=flags)
+    ref = oracle.decode_step(inp, M, normalized=not flags)
+    check_idx_format(g["idx"], inp["seq_lens"], M)
+    rc = recall(g["idx"], ref["idx"])
+    print(f"[{label}] recall={rc:.6f}", flush=True)
+    assert rc >= RECALL_MIN
+    assert_out_close(cfg, g["out"], ref["out"], label)
+    assert_state_close(g["S"], g["z"], ref["S"], ref["z"], label)
+    # the new token is appended to every cache
+    for b, L in enumerate(inp["seq_lens"]):
+        assert torch.equal(g["k_cache"][b, L - 1].float().cpu(), torch.from_numpy(inp["k_new"][b]))
+        assert torch.equal(g["v_cache"][b, L - 1].float().cpu(), torch.from_numpy(inp["v_new"][b]))
+        assert torch.equal(g["k_idx_cache"][b, L - 1].float().cpu(), torch.from_numpy(inp["k_idx_new"][b]))
+    return g, ref
+
+
+def test_decode_c1_qwen7b_16k():
+    cfg = CONFIGS[1]
+    _parity(cfg, decode_inputs(cfg, 1), cfg.M, "C1")
+
+
+def test_decode_c2_ragged_batch32():
+    cfg = CONFIGS[2]
+    inp = decode_inputs(cfg, 2)
+    assert inp["seq_lens"].min() >= 4096 and inp["seq_lens"].max() <= 16384
+    _parity(cfg, inp, cfg.M, "C2")
+
+
+@pytest.mark.slow
+def test_decode_c4_qwen14b_m_sweep_and_dense():
+    cfg = CONFIGS[4]
+    inp = decode_inputs(cfg, 4)
+    for M in cfg.M_sweep:
+        g, ref = _parity(cfg, inp, M, f"C4 M={M}")
+    # M = L: the sparse branch is full causal attention; compare the dense kernel
+    dense_gpu = gpu_dense_decode(cfg, inp, g["k_cache"], g["v_cache"])
+    dense_ref = oracle.dense_decode(inp)
+    assert_out_close(cfg, dense_gpu, dense_ref, "C4 dense kernel")
+    np.testing.assert_allclose(ref["o_sparse"], dense_ref, rtol=1e-10, atol=1e-12)
+
+
+SMALL = [
+    # (label, overrides, seq_lens, M)
+    ("fp32 G2 d32", dict(dtype="f32", H_q=2, H_kv=1, d=32, H_I=1, H_Ik=1, d_I=16, H_L=2, hidden=64),
+     [1, 2, 31, 32, 33, 300], 32),
+    ("bf16 G7 d128", dict(), [1, 2, 127, 128, 129, 700, 1500], 128),
+    ("bf16 G5 shared key", dict(H_q=10, H_kv=2, H_L=10, H_I=4, H_Ik=1, hidden=200), [5, 64, 65, 999], 64),
+    ("bf16 G4 d64 R2", dict(H_q=8, H_kv=2, H_L=8, d=64, H_I=4, H_Ik=2, d_I=32, hidden=96),
+     [3, 255, 256, 257, 1024], 256),
+    ("fp32 G7 d128", dict(dtype="f32"), [1, 100, 600], 64),
+    ("bf16 M=1", dict(), [1, 2, 50], 1),
+]
+
+
+@pytest.mark.parametrize("label,over,lens,M", SMALL, ids=[s[0] for s in SMALL])
+def test_decode_small_shapes(label, over, lens, M):
+    base = CONFIGS[1].replace(B=len(lens), L=0, cap=max(lens) + 3, **over)
+    inp = decode_inputs(base, 11, seq_lens=np.array(lens, np.int32))
+    _parity(base, inp, M, label)
+
+
+def test_decode_signed_head_weights():
+    cfg = CONFIGS[1].replace(B=3, L=0, cap=3000)
+    inp = decode_inputs(cfg, 12, seq_lens=np.array([100, 2048, 2999], np.int32))
+    inp["w_idx"] = np.array([1.0, -0.5, 0.0, 2.0], np.float32)
+    _parity(cfg, inp, 256, "signed w")
+
+
+def test_decode_unnormalized_linear():
+    cfg = CONFIGS[1].replace(B=2, L=0, cap=600, hidden=64)
+    inp = decode_inputs(cfg, 13, seq_lens=np.array([10, 500], np.int32))
+    inp["S0"] = inp["S0"] * 0.01
+    g = gpu_decode(cfg, inp, M=64, flags=1)
+    ref = oracle.decode_step(inp, 64, normalized=False)
+    _, _, nrm = out_errors(g["out"], ref["out"])
+    print(f"[unnormalized] rel_rms={nrm:.3e}")
+    assert nrm < 1e-2
+
+
+def test_decode_gate_saturated_equals_dense_at_full_budget():
+    cfg = CONFIGS[1].replace(B=3, L=0, cap=5000)
+    inp = decode_inputs(cfg, 14, seq_lens=np.array([1, 777, 4999], np.int32))
+    inp["x"] = np.zeros_like(inp["x"])
+    inp["x"][:, 0] = 1.0
+    inp["w_gate"] = np.zeros_like(inp["w_gate"])
+    inp["w_gate"][0, :] = 200.0                     # g = 1 exactly: output = sparse branch
+    g = gpu_decode(cfg, inp, M=5000)
+    dense_gpu = gpu_dense_decode(cfg, inp, g["k_cache"], g["v_cache"])
+    ref = oracle.dense_decode(inp)
+    assert_out_close(cfg, g["out"], ref, "g=1 sparse")
+    assert_out_close(cfg, dense_gpu, ref, "dense")
+
+
+def test_decode_is_deterministic():
+    cfg = CONFIGS[2].replace(B=4, L_lo=2000, L_hi=9000, cap=9000)
+    inp = decode_inputs(cfg, 15)
+    a, b = gpu_decode(cfg, inp, repeat=2)
+    assert torch.equal(a["out_t"], b["out_t"])
+    assert np.array_equal(a["S"], b["S"]) and np.array_equal(a["idx"], b["idx"])

@@ -1,0 +1,152 @@
+"""Prefill parity of the HIP path (lisa_prefill, lisa_indexer_topk,
+lisa_linear_state_update) against the fp64 oracle on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_lightning_amd as L
+import oracle
+from lisa_inputs import CONFIGS, prefill_inputs, decode_inputs, row_sample
+from gpu_helpers import (RECALL_MIN, assert_out_close, assert_state_close, check_idx_format,
+                         dev, gpu_decode, gpu_prefill, host, recall, shape_of, tdtype)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_parity(cfg, inp, M, label):
+    g = gpu_prefill(cfg, inp, M=M)
+    ref = oracle.prefill(inp, M)
+    B, n = inp["q"].shape[:2]
+    for b in range(B):
+        check_idx_format(g["idx"][b], np.arange(1, n + 1), M)
+        rc = recall(g["idx"][b], ref["idx"][b])
+        print(f"[{label}] b={b} recall={rc:.6f}", flush=True)
+        assert rc >= RECALL_MIN
+    assert_out_close(cfg, g["out"], ref["out"], label)
+    assert_state_close(g["S"], g["z"], ref["S"], ref["z"], label)
+    return g, ref
+
+
+def test_prefill_c0_tiny_fp32():
+    cfg = CONFIGS[0]
+    _full_parity(cfg, prefill_inputs(cfg, 0), cfg.M, "C0")
+
+
+def test_prefill_c0_selection_bit_exact_on_oracle_scores():
+    cfg = CONFIGS[0]
+    inp = prefill_inputs(cfg, 0)
+    n = cfg.n
+    res = oracle.prefill_rows(inp, cfg.M, range(n))
+    ld = n
+    sc = np.zeros((1, n, ld), np.float32)
+    for t in range(n):
+        sc[0, t, : t + 1] = res["scores"][t]
+    sh = shape_of(cfg)
+    idx = torch.full((1, n, cfg.M), -7, dtype=torch.int32, device="cuda")
+    L.lisa_indexer_topk(sh, L.LISA_ROWS_PREFILL, n, None, None, None, None, dev(sc, torch.float32), ld,
+                        None, idx, None)
+    torch.cuda.synchronize()
+    got = host(idx)[0]
+    for t in range(n):
+        exp = oracle.select_topm(sc[0, t, : t + 1].astype(np.float64), cfg.M)
+        assert got[t, : len(exp)].tolist() == exp.tolist() and np.all(got[t, len(exp):] == -1), t
+
+
+@pytest.mark.parametrize("n,M,B", [(700, 128, 2), (129, 128, 1), (64, 256, 1), (333, 1, 1)])
+def test_prefill_small_bf16(n, M, B):
+    cfg = CONFIGS[3].replace(B=B, n=n, cap=n + 5)
+    _full_parity(cfg, prefill_inputs(cfg, 3, n=n, salt=n), M, f"bf16 n={n} M={M}")
+
+
+def test_prefill_fp32_shared_key_small_heads():
+    cfg = CONFIGS[0].replace(H_q=6, H_kv=2, H_L=6, H_I=2, H_Ik=1, n=300, cap=300, d=64, d_I=16)
+    _full_parity(cfg, prefill_inputs(cfg, 0, n=300, salt=5), 40, "fp32 shared key")
+
+
+def test_prefill_scores_out_and_topk_match_oracle():
+    cfg = CONFIGS[3].replace(n=600, cap=600)
+    n, M = 600, 100
+    inp = prefill_inputs(cfg, 3, n=n, salt=2)
+    sh = shape_of(cfg, M=M, cap=n)
+    T = tdtype(cfg)
+    kic = dev(inp["k_idx"], T)
+    sc = torch.zeros((1, n, n), dtype=torch.float32, device="cuda")
+    idx = torch.full((1, n, M), -7, dtype=torch.int32, device="cuda")
+    L.lisa_indexer_topk(sh, L.LISA_ROWS_PREFILL, n, None, dev(inp["q_idx"], T), kic,
+                        dev(inp["w_idx"], torch.float32), None, n, sc, idx, None)
+    torch.cuda.synchronize()
+    sc_h, idx_h = host(sc)[0], host(idx)[0]
+    res = oracle.prefill_rows(inp, M, range(n))
+    worst = 0.0
+    for t in range(n):
+        ref = res["scores"][t]
+        worst = max(worst, float(np.max(np.abs(sc_h[t, : t + 1] - ref) / (1.0 + np.abs(ref)))))
+        # the GPU selection of the GPU's own fp32 scores is exact
+        exp = oracle.select_topm(sc_h[t, : t + 1].astype(np.float64), M)
+        assert idx_h[t, : len(exp)].tolist() == exp.tolist(), t
+    print(f"[scores_out] worst rel err {worst:.3e}")
+    assert worst < 1e-5
+    assert recall(idx_h, res["idx"].values()) >= RECALL_MIN
+
+
+def test_linear_state_update_matches_oracle():
+    cfg = CONFIGS[3].replace(B=2)
+    n = 333
+    inp = prefill_inputs(cfg, 3, n=n, salt=9)
+    r = np.random.default_rng(4)
+    S0 = (r.standard_normal(inp["S0"].shape) * 30).astype(np.float32)
+    z0 = (np.abs(r.standard_normal(inp["z0"].shape)) * 100 + 1).astype(np.float32)
+    T = tdtype(cfg)
+    S, z = dev(S0, torch.float32), dev(z0, torch.float32)
+    sh = shape_of(cfg, B=2)
+    L.lisa_linear_state_update(sh, n, dev(inp["k_lin"], T), dev(inp["v_lin"], T), S, z)
+    torch.cuda.synchronize()
+    for b in range(2):
+        rS, rz = oracle.linear_state_update(inp["k_lin"][b], inp["v_lin"][b], S0[b], z0[b])
+        assert_state_close(host(S)[b], host(z)[b], rS, rz, f"update b={b}")
+
+
+def test_prefill_then_decode_continues_the_sequence():
+    cfg = CONFIGS[3].replace(n=401, cap=410)
+    n, M = 400, 64
+    full = prefill_inputs(cfg, 3, n=n + 1, salt=7)
+    part = {k: (v[:, :n] if v.ndim >= 3 and v.shape[1] == n + 1 else v) for k, v in full.items()}
+    g = gpu_prefill(cfg, part, M=M)
+    ref_full = oracle.prefill(full, M)
+    T = tdtype(cfg)
+
+    def cache(a):
+        c = np.zeros((1, cfg.cap) + a.shape[2:], np.float32)
+        c[:, :n] = a[:, :n]
+        return c
+
+    dec = {
+        "seq_lens": np.array([n + 1], np.int32),
+        "k_cache": cache(full["k"]), "v_cache": cache(full["v"]), "k_idx_cache": cache(full["k_idx"]),
+        "q": full["q"][:, n], "k_new": full["k"][:, n], "v_new": full["v"][:, n],
+        "q_idx": full["q_idx"][:, n], "k_idx_new": full["k_idx"][:, n],
+        "q_lin": full["q_lin"][:, n], "k_lin": full["k_lin"][:, n], "v_lin": full["v_lin"][:, n],
+        "x": full["x"][:, n], "w_gate": full["w_gate"], "w_idx": full["w_idx"],
+        "S0": g["S"], "z0": g["z"],
+    }
+    d = gpu_decode(cfg.replace(B=1), dec, M=M)
+    assert_out_close(cfg, d["out"][0], ref_full["out"][0, n], "prefill+decode")
+    assert_state_close(d["S"], d["z"], ref_full["S"], ref_full["z"], "prefill+decode")
+    assert recall(d["idx"], [ref_full["idx"][0][n]]) >= RECALL_MIN
+
+
+@pytest.mark.slow
+def test_prefill_c3_qwen7b_16k_sampled_rows():
+    cfg = CONFIGS[3]
+    inp = prefill_inputs(cfg, 3)
+    g = gpu_prefill(cfg, inp)
+    rows = row_sample(cfg.n, cfg.M, stride=256)
+    ref = oracle.prefill_rows(inp, cfg.M, rows)
+    got = np.stack([g["out"][0, t] for t in rows])
+    exp = np.stack([ref["out"][t] for t in rows])
+    assert_out_close(cfg, got, exp, f"C3 {len(rows)} rows")
+    check_idx_format(g["idx"][0][rows], np.array(rows) + 1, cfg.M)
+    rc = recall(g["idx"][0][rows], [ref["idx"][t] for t in rows])
+    print(f"[C3] recall={rc:.6f}")
+    assert rc >= RECALL_MIN
+    assert_state_close(g["S"][0], g["z"][0], ref["S"], ref["z"], "C3 state")

@@ -1,0 +1,77 @@
+"""Top-M selection on the GPU, bit-exact against the oracle's selection of the
+same fp32 score rows ("LISA", arXiv 2607.19358v1, Section 3.2 Stage 2; ties
+to the later position, -0.0 equal to +0.0, ascending output, -1 padding)."""
+import numpy as np
+import pytest
+
+import oracle
+from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs, row_sample
+from gpu_helpers import gpu_select_rows, padded
+
+pytestmark = pytest.mark.gpu
+
+
+def _expect(rows, M):
+    return np.stack([padded(oracle.select_topm(r.astype(np.float64), M), M) for r in rows])
+
+
+def _check(rows, M, label):
+    got = gpu_select_rows(rows, M)
+    exp = _expect(rows, M)
+    bad = np.nonzero(np.any(got != exp, axis=1))[0]
+    print(f"[{label}] rows={len(rows)} M={M} mismatched_rows={len(bad)}", flush=True)
+    assert len(bad) == 0, (label, bad[:5])
+
+
+@pytest.mark.parametrize("L,M", [(1, 1), (2, 1), (5, 3), (1023, 64), (1024, 1024), (1025, 1024),
+                                 (4096, 100), (4097, 4096), (16384, 2048), (16385, 2048),
+                                 (32768, 8192), (65536, 2048), (3000, 1)])
+def test_select_edge_lengths(L, M):
+    r = np.random.default_rng(L * 7 + M)
+    rows = [
+        r.standard_normal(L).astype(np.float32),
+        (np.round(r.standard_normal(L) * 2) / 2).astype(np.float32),          # heavy ties
+        np.zeros(L, np.float32),                                              # sliding window
+        np.where(r.random(L) < 0.5, np.float32(-0.0), np.float32(0.0)),     # signed zeros
+        np.abs(r.standard_normal(L)).astype(np.float32) * (r.random(L) < 0.1),  # ReLU-like
+        -np.abs(r.standard_normal(L)).astype(np.float32),                     # all negative
+    ]
+    _check(rows, M, f"edge L={L}")
+
+
+def test_select_mixed_lengths_one_launch():
+    r = np.random.default_rng(3)
+    lens = [1, 7, 64, 2047, 2048, 2049, 9000, 16384, 4096, 12345]
+    rows = [(np.round(r.standard_normal(n) * 4) / 4).astype(np.float32) for n in lens]
+    _check(rows, 2048, "mixed")
+
+
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_select_on_oracle_decode_scores(cid):
+    cfg = CONFIGS[cid]
+    inp = decode_inputs(cfg, cid)
+    Ms = cfg.M_sweep or (cfg.M,)
+    for M in Ms:
+        ref = oracle.decode_step(inp, M)
+        rows = [s.astype(np.float32) for s in ref["scores"]]
+        _check(rows, M, f"C{cid} M={M}")
+
+
+def test_select_on_oracle_prefill_scores_c0():
+    cfg = CONFIGS[0]
+    inp = prefill_inputs(cfg, 0)
+    res = oracle.prefill_rows(inp, cfg.M, range(cfg.n))
+    rows = [res["scores"][t].astype(np.float32) for t in range(cfg.n)]
+    _check(rows, cfg.M, "C0 all rows")
+
+
+@pytest.mark.slow
+def test_select_on_oracle_prefill_scores_c3_rows():
+    cfg = CONFIGS[3]
+    inp = prefill_inputs(cfg, 3)
+    rows_t = row_sample(cfg.n, cfg.M, stride=16)
+    rows = []
+    for t in rows_t:
+        s = oracle.index_scores(inp["q_idx"][0, t], inp["k_idx"][0, : t + 1], inp["w_idx"])
+        rows.append(s.astype(np.float32))
+    _check(rows, cfg.M, f"C3 {len(rows)} rows")
