@@ -1,0 +1,356 @@
+#!/usr/bin/env python3
+"""Throughput of one LISA attention layer on one MI355X.
+
+A step is one lisa_decode_step of the Qwen-7B-shaped layer (batch 1, 16384
+cached tokens including the new one, 28/4 heads, head dim 128, indexer 4 x 64,
+top-M 2048): cache append, indexer scan, top-M select, sparse GQA attention,
+linear-state update and gate, all in the library's HIP kernels.  Steps are
+replayed from a HIP graph that cycles over NBUF independent buffer sets
+(caches, state, outputs), so consecutive steps never reuse a working set
+that could still sit in the 256 MB Infinity Cache.
+
+Printed JSON (one line): decode tokens/s of the layer as ``value``; the
+dominant kernel's roofline fraction measured with HIP events recorded
+around that kernel inside the timed graph; the fp64 CPU oracle timed on a
+bounded sample on the host; and, under ``extra``, the per-kernel times, the
+dense-attention decode baseline on the same GPU and the prefill rate.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "decode tok/s/layer @16K ctx, M=2048 (+prefill tok/s); % HBM/MFMA roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=640)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--nbuf", type=int, default=32, help="rotating buffer sets (>= 512 MB total)")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--prefill-iters", type=int, default=5)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# algorithmic traffic (bytes the method must move), per launch
+# ----------------------------------------------------------------------------
+def decode_bytes(cfg, L, M, B):
+    """Per-step bytes of the whole decode step (all sequences)."""
+    m = min(M, L)
+    per_tok = (L * cfg.H_Ik * cfg.d_I * 2                       # index keys
+               + m * cfg.H_kv * cfg.d * 4                        # gathered K and V
+               + 8 * cfg.H_L * cfg.d * (cfg.d + 1)               # S and z, read + write
+               + 2 * (2 * cfg.H_q * cfg.d + 3 * cfg.H_L * cfg.d + cfg.H_I * cfg.d_I
+                      + 2 * cfg.H_kv * cfg.d + cfg.H_Ik * cfg.d_I + cfg.hidden))
+    return B * per_tok + 2 * cfg.hidden * cfg.H_q
+
+
+def phase_a_bytes(cfg, L, B):
+    per = (L * cfg.H_Ik * cfg.d_I * 2 + 8 * cfg.H_L * cfg.d * (cfg.d + 1)
+           + 2 * (3 * cfg.H_L * cfg.d + cfg.H_I * cfg.d_I + cfg.hidden)
+           + 2 * 2 * (2 * cfg.H_kv * cfg.d + cfg.H_Ik * cfg.d_I))   # new rows read + appended
+    return B * per + 2 * cfg.hidden * cfg.H_q
+
+
+def attention_bytes(cfg, L, M, B, dense=False):
+    m = L if dense else min(M, L)
+    return B * (m * cfg.H_kv * cfg.d * 4 + 2 * 2 * cfg.H_q * cfg.d)
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer runs on a single "
+              "MI355X and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_attention_lightning_amd as Lb
+    from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    Lb.library()
+    cid = 1
+    cfg = CONFIGS[cid]
+    B, Lctx, M = cfg.B, cfg.L, cfg.M
+    T = torch.bfloat16
+    print(f"# bench: {cfg.name} B={B} L={Lctx} M={M} nbuf={args.nbuf}", file=sys.stderr, flush=True)
+
+    inp = decode_inputs(cfg, cid)
+
+    def up(a, dt=T):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt).contiguous()
+
+    base = {k: up(inp[k]) for k in ("q", "k_new", "v_new", "q_idx", "k_idx_new", "q_lin", "k_lin",
+                                    "v_lin", "x", "w_gate", "k_cache", "v_cache", "k_idx_cache")}
+    base["S"] = up(inp["S0"], torch.float32)
+    base["z"] = up(inp["z0"], torch.float32)
+    seq = torch.from_numpy(inp["seq_lens"].astype(np.int32)).cuda()
+    w_idx = up(inp["w_idx"], torch.float32)
+    sh = Lb.make_shape(B=B, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, H_I=cfg.H_I, H_Ik=cfg.H_Ik,
+                       d_I=cfg.d_I, hidden=cfg.hidden, M=M, cap=cfg.cap, max_len=Lctx)
+    sets = []
+    per_set = ("q", "k_new", "v_new", "q_idx", "k_idx_new", "q_lin", "k_lin", "v_lin", "x",
+               "k_cache", "v_cache", "k_idx_cache", "S", "z")
+    for i in range(args.nbuf):
+        s = {k: base[k].clone() for k in per_set}
+        s["out"] = torch.empty((B, cfg.H_q, cfg.d), dtype=T, device="cuda")
+        s["out_dense"] = torch.empty((B, cfg.H_q, cfg.d), dtype=T, device="cuda")
+        s["idx"] = torch.empty((B, M), dtype=torch.int32, device="cuda")
+        s["ws"] = Lb.workspace(sh, Lb.LISA_OP_DECODE)
+        s["ws_dense"] = Lb.workspace(sh, Lb.LISA_OP_DENSE_DECODE)
+        sets.append(s)
+    set_bytes = sum(t.numel() * t.element_size() for t in sets[0].values())
+    print(f"# {args.nbuf} buffer sets of {set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
+
+    def step(s):
+        Lb.lisa_decode_step(sh, seq, s["q"], s["k_new"], s["v_new"], s["q_idx"], s["k_idx_new"],
+                            s["q_lin"], s["k_lin"], s["v_lin"], s["x"], base["w_gate"], w_idx,
+                            s["k_cache"], s["v_cache"], s["k_idx_cache"], s["S"], s["z"], s["out"],
+                            s["idx"], s["ws"])
+
+    def dense_step(s):
+        Lb.lisa_dense_decode(sh, seq, s["q"], s["k_cache"], s["v_cache"], s["out_dense"], s["ws_dense"])
+
+    cap_stream = torch.cuda.Stream()
+
+    def capture(fn):
+        """HIP graph of one pass of fn over every buffer set."""
+        with torch.cuda.stream(cap_stream):       # eager warm-up pass on the capture stream
+            for s in sets:
+                fn(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap_stream):
+            for s in sets:
+                fn(s)
+        return g
+
+    def run(g, n_steps):
+        reps = max(1, (n_steps + len(sets) - 1) // len(sets))
+        for _ in range(reps):
+            g.replay()
+        return reps * len(sets)
+
+    def time_graph(g):
+        run(g, args.warmup)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        n = run(g, args.steps)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n, n
+
+    def kernel_times(fn, kids):
+        """Average duration of each kernel from HIP events recorded by the
+        library around its launches, over eager (not graph) steps."""
+        res = {}
+        for kid in kids:
+            st = [torch.cuda.Event(enable_timing=True) for _ in sets]
+            sp = [torch.cuda.Event(enable_timing=True) for _ in sets]
+            for e in st + sp:
+                e.record()
+            torch.cuda.synchronize()
+            Lb.lisa_timing_enable(kid, st, sp)
+            for s in sets:
+                fn(s)
+            torch.cuda.synchronize()
+            cnt = Lb.lisa_timing_count()
+            Lb.lisa_timing_enable(0)
+            res[kid] = float(np.mean([a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])])) if cnt else 0.0
+        return res
+
+    # ---------------- timed region: graph replays of whole decode steps
+    g_main = capture(step)
+    ms_step, done = time_graph(g_main)
+    print(f"# timed {done} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    # ---------------- per-kernel durations (HIP events on the launch stream)
+    dec_kids = (0, 1, 2, 8)
+    kt = kernel_times(step, dec_kids)
+    per_kernel_ms = {Lb.lisa_kernel_name(k): v for k, v in kt.items()}
+    dom = max(dec_kids, key=lambda k: kt[k])
+    dom_ms = kt[dom]
+    print(f"# kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in per_kernel_ms.items()),
+          file=sys.stderr, flush=True)
+
+    # dense baseline over the same caches
+    g_dense = capture(dense_step)
+    ms_dense, _ = time_graph(g_dense)
+    kd = kernel_times(dense_step, (2, 8))
+    dense_kernel_us = {Lb.lisa_kernel_name(k): round(v * 1e3, 3) for k, v in kd.items()}
+
+    tok_s = B / (ms_step * 1e-3)
+    dname = Lb.lisa_kernel_name(dom)
+    algo = {0: phase_a_bytes(cfg, Lctx, B), 1: None, 2: attention_bytes(cfg, Lctx, M, B), 8: None}
+    if algo[dom] is not None:
+        achieved = algo[dom] / (dom_ms * 1e-3) / 1e9
+        roof = {"kernel": dname, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(dname), "algorithmic_bytes": algo[dom],
+                "avg_launch_us": round(dom_ms * 1e3, 3)}
+    else:
+        roof = {"kernel": dname, "bound": "alu", "achieved": None, "peak": None,
+                "unit": None, "frac": None, "traffic": None, "avg_launch_us": round(dom_ms * 1e3, 3)}
+    step_bytes = decode_bytes(cfg, Lctx, M, B)
+    extra = {
+        "us_per_step": round(ms_step * 1e3, 3),
+        "kernel_us": {k: round(v * 1e3, 3) for k, v in per_kernel_ms.items()},
+        "kernel_timing": "HIP events around each kernel, eager steps over the same buffer sets",
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_roofline_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "dense_decode_us_per_step": round(ms_dense * 1e3, 3),
+        "dense_decode_kernel_us": dense_kernel_us,
+        "dense_decode_tok_s": round(B / (ms_dense * 1e-3), 1),
+        "speedup_vs_dense_decode": round(ms_dense / ms_step, 3),
+        "pages_context": "about 50% end-to-end inference speedup at 16K context (other hardware, whole model)",
+    }
+    del g_main, g_dense
+    sets.clear()
+    torch.cuda.empty_cache()
+
+    if not args.no_prefill:
+        extra.update(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs))
+
+    cpu = None if args.no_cpu else cpu_baseline(args, inp, M)
+
+    rec = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": done, "warmup": args.warmup, "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 caches and activations; no trained weights)",
+        "config": {"workload": cfg.name, "batch": B, "context": Lctx, "M": M, "H_q": cfg.H_q,
+                   "H_kv": cfg.H_kv, "head_dim": cfg.d, "hidden": cfg.hidden,
+                   "indexer": f"{cfg.H_I}x{cfg.d_I}", "buffer_sets": args.nbuf},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data.get(kernel)
+        if not ent or ent.get("source_sha256") != source_hash():
+            return None
+        return ent.get("bytes_per_launch")
+    except Exception:
+        return None
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_attention_lightning_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
+    cid = 3
+    cfg = CONFIGS[cid]
+    n, M = cfg.n, cfg.M
+    T = torch.bfloat16
+    print(f"# prefill: {cfg.name} n={n}", file=sys.stderr, flush=True)
+    inp = prefill_inputs(cfg, cid)
+
+    def up(a, dt=T):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt).contiguous()
+
+    sh = Lb.make_shape(B=1, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, H_I=cfg.H_I, H_Ik=cfg.H_Ik,
+                       d_I=cfg.d_I, hidden=cfg.hidden, M=M, cap=n)
+    t = {k: up(inp[k]) for k in ("q", "k", "v", "k_idx", "q_idx", "q_lin", "k_lin", "v_lin", "x",
+                                 "w_gate")}
+    S = up(inp["S0"], torch.float32)
+    z = up(inp["z0"], torch.float32)
+    w_idx = up(inp["w_idx"], torch.float32)
+    out = torch.empty((1, n, cfg.H_q, cfg.d), dtype=T, device="cuda")
+    ws = Lb.workspace(sh, Lb.LISA_OP_PREFILL, n)
+
+    def call():
+        Lb.lisa_prefill(sh, n, t["q"], t["k"], t["v"], t["k_idx"], t["q_idx"], t["q_lin"], t["k_lin"],
+                        t["v_lin"], t["x"], t["w_gate"], w_idx, S, z, out, None, ws)
+
+    kern = {}
+    call()
+    torch.cuda.synchronize()
+    for kid in (4, 5, 3, 1, 6):
+        st = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        sp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for e in st + sp:
+            e.record()
+        Lb.lisa_timing_enable(kid, st, sp)
+        call()
+        torch.cuda.synchronize()
+        cnt = Lb.lisa_timing_count()
+        Lb.lisa_timing_enable(0)
+        kern[Lb.lisa_kernel_name(kid)] = round(sum(a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])) * 1e3, 1)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.prefill_iters):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.prefill_iters
+    idx_flops = 2.0 * cfg.H_I * cfg.d_I * (n * (n + 1) / 2)
+    res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
+           "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
+           "prefill_indexer_mfma_frac": round(idx_flops / (kern["prefill_index_scores"] * 1e-6) / 1e12
+                                              / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del ws, t, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(args, inp, M):
+    """The fp64 oracle's decode step on the host, over a bounded sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = None
+    cores = len(os.sched_getaffinity(0))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode_step(inp, M)
+        n += 1
+        if time.perf_counter() - t0 > args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    B = len(inp["seq_lens"])
+    return {"value": round(n * B / dt, 3), "unit": "tok/s", "cores": blas or cores,
+            "kind": "oracle", "sample": f"{n} decode steps of the same workload (fp64 NumPy), {dt:.1f} s",
+            "affinity_cores": cores}
+
+
+if __name__ == "__main__":
+    main()

@@ -173,7 +173,8 @@ int lisa_prefill(const lisa_shape* shape, int32_t n,
  *            fp32 rows (q_idx, k_idx_cache and w_idx may then be NULL).
  * scores_out nullable: when set (and scores_in is NULL), receives the fp32
  *            scores of each row's positions 0..len-1; other entries untouched.
- * scores_ld  row stride in elements of scores_in/out, >= the longest row.
+ * scores_ld  row stride in elements of scores_in/out: a multiple of 4 and
+ *            >= the longest row.
  * idx_out    ascending selected positions, -1 padded.
  * ws         workspace of lisa_workspace_bytes(shape, LISA_OP_TOPK_DECODE or
  *            LISA_OP_TOPK_PREFILL, n) bytes.

@@ -8,7 +8,7 @@
 //   * linear slices: S += phi(k)^T v, z += phi(k), and the branch output
 //     phi(q) S / (phi(q) . z) for a 32-column slice of S (Section 3.3
 //     Eqs. 3-4, phi = elu + 1);
-//   * gate chunks: partial dot products x . W_g[:, h] over 256 hidden rows
+//   * gate chunks: partial dot products x . W_g[:, h] over 64 hidden rows
 //     (Section 3.3 Eq. 5); the attention epilogue sums them.
 // Attention: gathered GQA softmax attention over the selected rows, split
 //   over the selected set, with an in-kernel combine by the last split block
@@ -20,23 +20,23 @@
 namespace lisa {
 
 constexpr int PA_THREADS = 256;
-constexpr int IDX_TILE = 64;     // positions per indexer block
+constexpr int IDX_ROWS_IN_FLIGHT = 8;  // index-key rows each lane loads at once
 constexpr int LIN_COLS = 32;     // columns of S per linear block
-constexpr int GATE_ROWS = 256;   // hidden rows per gate block
+constexpr int GATE_ROWS = 64;    // hidden rows per gate block
 
 // ---------------------------------------------------------------------------
 // indexer tile
 // ---------------------------------------------------------------------------
 template <typename T, int R>
-__device__ __forceinline__ void index_tile(const PhaseAArgs& a, int b, int tile) {
+__device__ __forceinline__ void index_tile(const PhaseAArgs& a, int b, int tile, int tile_rows) {
   using V = Vec<T>;
   constexpr int VEC = V::N;
-  constexpr int U = 4;  // rows in flight per lane
+  constexpr int U = IDX_ROWS_IN_FLIGHT;
   const Shape& sh = a.sh;
   const int L = a.seq_lens[b];
-  const int j0 = tile * IDX_TILE;
+  const int j0 = tile * tile_rows;
   if (j0 >= L) return;
-  const int j1 = min(L, j0 + IDX_TILE);
+  const int j1 = min(L, j0 + tile_rows);
   const int E = sh.H_Ik * sh.d_I;
   const int LPR = E / VEC;       // lanes per row
   const int LPH = sh.d_I / VEC;  // lanes per key head
@@ -45,7 +45,19 @@ __device__ __forceinline__ void index_tile(const PhaseAArgs& a, int b, int tile)
   const int rw = lane / LPR, li = lane % LPR;
   const int e0 = li * VEC;
   const int kh = e0 / sh.d_I, c0 = e0 % sh.d_I;
+  const int step = RPW * (PA_THREADS / WAVE);  // tile_rows == U * step
 
+  const T* kc = (const T*)a.k_idx_cache + (size_t)b * sh.cap * E;
+  const T* knew = (const T*)a.k_idx_new + (size_t)b * E;
+  // every lane loads U rows at once; rows past the tile end re-read the last
+  // row (no branch around the loads, so they are all in flight together)
+  float kv[U][VEC];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int j = min(j0 + u * step + wave * RPW + rw, j1 - 1);
+    const T* src = (j == L - 1 && a.k_idx_new) ? knew : kc + (size_t)j * E;
+    V::load(src + e0, kv[u]);
+  }
   float qv[R][VEC];
   float wv[R];
   const T* qb = (const T*)a.q_idx + (size_t)b * sh.H_I * sh.d_I;
@@ -55,40 +67,22 @@ __device__ __forceinline__ void index_tile(const PhaseAArgs& a, int b, int tile)
     V::load(qb + (size_t)h * sh.d_I + c0, qv[r]);
     wv[r] = a.w_idx[h];
   }
-  const T* kc = (const T*)a.k_idx_cache + (size_t)b * sh.cap * E;
-  const T* knew = (const T*)a.k_idx_new + (size_t)b * E;
   float* srow = a.scores + (size_t)b * a.scores_ld;
-  const int step = RPW * (PA_THREADS / WAVE);
-
-  for (int base = j0; base < j1; base += U * step) {
-    float kv[U][VEC];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = base + u * step + wave * RPW + rw;
-      if (j < j1) {
-        const T* src = (j == L - 1 && a.k_idx_new) ? knew : kc + (size_t)j * E;
-        V::load(src + e0, kv[u]);
-      } else {
+  for (int u = 0; u < U; ++u) {
+    float sc = 0.f;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) kv[u][v] = 0.f;
-      }
+    for (int r = 0; r < R; ++r) {
+      float dot = 0.f;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) dot = fmaf(qv[r][v], kv[u][v], dot);
+      dot = group_sum(dot, LPH);
+      sc = fmaf(wv[r], fmaxf(dot, 0.f), sc);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float sc = 0.f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float dot = 0.f;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) dot = fmaf(qv[r][v], kv[u][v], dot);
-        dot = group_sum(dot, LPH);
-        sc = fmaf(wv[r], fmaxf(dot, 0.f), sc);
-      }
-      // sum over key heads: lanes li, li+LPH, ... of the row group
-      for (int off = LPH; off < LPR; off <<= 1) sc += __shfl_xor(sc, off, WAVE);
-      const int j = base + u * step + wave * RPW + rw;
-      if (li == 0 && j < j1) srow[j] = sc;
-    }
+    // sum over the key heads of the row (values are uniform per head group)
+    sc = group_sum_range(sc, LPH, LPR);
+    const int j = j0 + u * step + wave * RPW + rw;
+    if (li == 0 && j < j1) srow[j] = sc;
   }
 
   // append the new token (the tile that holds row L-1)
@@ -119,57 +113,68 @@ __device__ __forceinline__ void linear_slice(const PhaseAArgs& a, int b, int h, 
   // and forms the denominator phi(q) . z_new, so no block reads a z that
   // another block of the same launch has already advanced.  The numerator
   // phi(q) S_new of the slice's columns goes to o_lin; the epilogue divides.
-  __shared__ float fk[256], fq[256], fq_z[256], vv[LIN_COLS], red[PA_THREADS / WAVE][LIN_COLS];
+  constexpr int NF = 4;  // float4 of S per thread: d * 8 / 256 <= 4 for d <= 128
+  __shared__ float fk[128], fq[128], fq_z[128], vv[LIN_COLS], red[PA_THREADS / WAVE][LIN_COLS];
   const Shape& sh = a.sh;
   const int d = sh.d;
   const int c0 = slice * LIN_COLS;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const size_t hv = ((size_t)b * sh.H_L + h) * d;
-  for (int i = tid; i < d; i += PA_THREADS) {
-    const float k = phi(ld1<T>((const T*)a.k_lin + hv + i));
-    fk[i] = k;
-    float q = 0.f;
-    if (a.linear_output) {
-      q = phi(ld1<T>((const T*)a.q_lin + hv + i));
-      fq[i] = q;
-    }
+  float* Sh = a.S + hv * d;  // [d, d]
+  const int c4 = tid & 7;    // float4 column of this thread, constant over k
+  // issue the S loads first; rows past d (d < 128) re-read row d-1
+  float4 sv[NF];
+#pragma unroll
+  for (int k = 0; k < NF; ++k) {
+    const int row = min((tid + PA_THREADS * k) >> 3, d - 1);
+    sv[k] = reinterpret_cast<const float4*>(Sh + (size_t)row * d + c0)[c4];
+  }
+  // the per-head vectors, loaded unconditionally (clamped) so that they are
+  // in flight together with the S loads; z is only used (and rewritten) by
+  // slice 0, and q only when the output is wanted
+  const int ti = min(tid, d - 1);
+  const float kr = ld1<T>((const T*)a.k_lin + hv + ti);
+  const float qr = ld1<T>((const T*)(a.linear_output ? a.q_lin : a.k_lin) + hv + ti);
+  const float zr = a.z[hv + ti];
+  const float vr = ld1<T>((const T*)a.v_lin + hv + c0 + (tid & (LIN_COLS - 1)));
+  if (tid < d) {
+    const float k = phi(kr);
+    const float q = a.linear_output ? phi(qr) : 0.f;
+    fk[tid] = k;
+    fq[tid] = q;
     if (slice == 0) {
-      const float zn = a.z[hv + i] + k;
-      a.z[hv + i] = zn;
-      fq_z[i] = q * zn;
+      const float zn = zr + k;
+      a.z[hv + tid] = zn;
+      fq_z[tid] = q * zn;
     }
   }
-  if (tid < LIN_COLS) vv[tid] = ld1<T>((const T*)a.v_lin + hv + c0 + tid);
+  if (tid < LIN_COLS) vv[tid] = vr;
   __syncthreads();
 
-  float* Sh = a.S + hv * d;  // [d, d]
-  const int c4 = tid & 7;    // float4 column of this thread, constant over f
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int f = tid; f < d * 8; f += PA_THREADS) {
-    const int row = f >> 3;
-    float4* p = reinterpret_cast<float4*>(Sh + (size_t)row * d + c0) + c4;
-    float4 s = *p;
-    const float k = fk[row];
-    s.x = fmaf(k, vv[c4 * 4 + 0], s.x);
-    s.y = fmaf(k, vv[c4 * 4 + 1], s.y);
-    s.z = fmaf(k, vv[c4 * 4 + 2], s.z);
-    s.w = fmaf(k, vv[c4 * 4 + 3], s.w);
-    *p = s;
-    if (a.linear_output) {
-      const float q = fq[row];
-      acc[0] = fmaf(q, s.x, acc[0]);
-      acc[1] = fmaf(q, s.y, acc[1]);
-      acc[2] = fmaf(q, s.z, acc[2]);
-      acc[3] = fmaf(q, s.w, acc[3]);
+#pragma unroll
+  for (int k = 0; k < NF; ++k) {
+    const int rr = (tid + PA_THREADS * k) >> 3;
+    if (rr < d) {
+      float4 s = sv[k];
+      const float kk = fk[rr];
+      s.x = fmaf(kk, vv[c4 * 4 + 0], s.x);
+      s.y = fmaf(kk, vv[c4 * 4 + 1], s.y);
+      s.z = fmaf(kk, vv[c4 * 4 + 2], s.z);
+      s.w = fmaf(kk, vv[c4 * 4 + 3], s.w);
+      reinterpret_cast<float4*>(Sh + (size_t)rr * d + c0)[c4] = s;
+      if (a.linear_output) {
+        const float q = fq[rr];
+        acc[0] = fmaf(q, s.x, acc[0]);
+        acc[1] = fmaf(q, s.y, acc[1]);
+        acc[2] = fmaf(q, s.z, acc[2]);
+        acc[3] = fmaf(q, s.w, acc[3]);
+      }
     }
   }
   if (!a.linear_output) return;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    acc[k] += __shfl_xor(acc[k], 8, WAVE);
-    acc[k] += __shfl_xor(acc[k], 16, WAVE);
-    acc[k] += __shfl_xor(acc[k], 32, WAVE);
-  }
+  for (int k = 0; k < 4; ++k) acc[k] = sum_lanes_mod8(acc[k]);  // lanes with equal c4
   if (lane < 8) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) red[wave][lane * 4 + k] = acc[k];
@@ -190,10 +195,11 @@ __device__ __forceinline__ void linear_slice(const PhaseAArgs& a, int b, int h, 
 }
 
 // ---------------------------------------------------------------------------
-// gate partial dot products over 256 hidden rows
+// gate partial dot products over 64 hidden rows
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void gate_chunk(const PhaseAArgs& a, int b, int chunk) {
+  constexpr int KMAX = GATE_ROWS / 4;  // rows per thread for 64 head lanes x 4 row groups
   __shared__ float gred[PA_THREADS];
   const Shape& sh = a.sh;
   const int HP = sh.H_q <= 32 ? 32 : 64;
@@ -201,13 +207,21 @@ __device__ __forceinline__ void gate_chunk(const PhaseAArgs& a, int b, int chunk
   const int tid = threadIdx.x;
   const int h = tid % HP, rg = tid / HP;
   const int r0 = chunk * GATE_ROWS, r1 = min(sh.hidden, r0 + GATE_ROWS);
+  const int hc = min(h, sh.H_q - 1);
   const T* x = (const T*)a.x + (size_t)b * sh.hidden;
   const T* w = (const T*)a.w_gate;
-  float acc = 0.f;
-  if (h < sh.H_q) {
-#pragma unroll 8
-    for (int r = r0 + rg; r < r1; r += RG) acc = fmaf(ld1<T>(x + r), ld1<T>(w + (size_t)r * sh.H_q + h), acc);
+  // all loads first (rows past the chunk re-read its last row), then the sum
+  float xv[KMAX], wv[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int r = min(r0 + rg + RG * k, r1 - 1);
+    xv[k] = ld1<T>(x + r);
+    wv[k] = ld1<T>(w + (size_t)r * sh.H_q + hc);
   }
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+    if (r0 + rg + RG * k < r1) acc = fmaf(xv[k], wv[k], acc);
   gred[tid] = acc;
   __syncthreads();
   if (tid < sh.H_q) {
@@ -219,13 +233,10 @@ __device__ __forceinline__ void gate_chunk(const PhaseAArgs& a, int b, int chunk
 
 template <typename T, int R>
 __global__ __launch_bounds__(PA_THREADS) void k_decode_phase_a(PhaseAArgs a, int n_idx, int tiles_per_seq,
-                                                               int n_lin, int slices) {
-  if (blockIdx.x == 0 && a.counters) {
-    for (int i = threadIdx.x; i < a.n_counters; i += PA_THREADS) a.counters[i] = 0u;
-  }
+                                                               int tile_rows, int n_lin, int slices) {
   int blk = blockIdx.x;
   if (blk < n_idx) {
-    index_tile<T, R>(a, blk / tiles_per_seq, blk % tiles_per_seq);
+    index_tile<T, R>(a, blk / tiles_per_seq, blk % tiles_per_seq, tile_rows);
     return;
   }
   blk -= n_idx;
@@ -242,15 +253,17 @@ __global__ __launch_bounds__(PA_THREADS) void k_decode_phase_a(PhaseAArgs a, int
 template <typename T, int R>
 static hipError_t launch_pa(const PhaseAArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
-  const int tiles = a.do_scores ? (sh.max_len + IDX_TILE - 1) / IDX_TILE : 0;
+  const int VEC = Vec<T>::N;
+  const int tile_rows = IDX_ROWS_IN_FLIGHT * (WAVE / (sh.H_Ik * sh.d_I / VEC)) * (PA_THREADS / WAVE);
+  const int tiles = a.do_scores ? (sh.max_len + tile_rows - 1) / tile_rows : 0;
   const int n_idx = tiles * sh.B;
   const int slices = sh.d / LIN_COLS;
   const int n_lin = a.do_linear ? sh.B * sh.H_L * slices : 0;
   const int n_gate = a.do_gate ? sh.B * a.gate_chunks : 0;
   const int grid = n_idx + n_lin + n_gate;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_decode_phase_a<T, R>), dim3(grid), dim3(PA_THREADS), 0, st, a, n_idx, tiles, n_lin,
-                     slices);
+  hipLaunchKernelGGL((k_decode_phase_a<T, R>), dim3(grid), dim3(PA_THREADS), 0, st, a, n_idx, tiles, tile_rows,
+                     n_lin, slices);
   return hipGetLastError();
 }
 
@@ -269,27 +282,35 @@ hipError_t launch_decode_phase_a(const PhaseAArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // gathered GQA attention
 // ---------------------------------------------------------------------------
+// Block = (row, KV head, split).  A "slot" of D/VEC lanes owns one gathered
+// row of K (then V) at a time; each slot keeps its own online-softmax state
+// (max, sum, accumulator) for the GT query heads of the group and loads the
+// K and V rows of AT_RP positions at once, so one round costs two dependent
+// memory trips (the index, then the rows).  Slots are merged with xor
+// shuffles inside the wave and through LDS across the four waves.
 constexpr int AT_THREADS = 256;
-constexpr int GMAX = 8;       // query heads per KV head
-constexpr int AT_CHUNK = 128; // positions per softmax chunk
+constexpr int AT_RP = 4;        // positions per slot per round
+constexpr int AT_MAX_SPLITS = 32;
 
 size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit) {
   const int G = sh.H_q / sh.H_kv;
   return (size_t)n_rows * sh.H_kv * nsplit * (size_t)(G * sh.d + 2 * G);
 }
 
-template <typename T, int D>
+__device__ __forceinline__ float scale_from(float m_old, float m_new) {
+  return m_old == -INFINITY ? 0.f : exp2f(m_old - m_new);
+}
+
+template <typename T, int D, int GT>
 __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
   using V = Vec<T>;
   constexpr int VEC = V::N;
-  constexpr int LG = D / VEC;            // lanes per head row
-  constexpr int NG = AT_THREADS / LG;    // position slots
+  constexpr int LG = D / VEC;            // lanes per row of one head
+  constexpr int NG = AT_THREADS / LG;    // slots
   constexpr int NW = AT_THREADS / WAVE;
-  __shared__ int pos[AT_CHUNK];
-  __shared__ float logit[AT_CHUNK][GMAX];
-  __shared__ float run_m[GMAX], run_l[GMAX], fac[GMAX];
-  __shared__ float red[NW][GMAX * D];
-  __shared__ int is_last;
+  constexpr int ROUND = NG * AT_RP;      // positions per round
+  __shared__ float wm[NW][GT], wl[NW][GT];
+  __shared__ float wacc[NW][GT * D];
 
   const Shape& sh = a.sh;
   const int G = sh.H_q / sh.H_kv;
@@ -302,189 +323,150 @@ __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
   const int len = a.prefill ? t + 1 : a.seq_lens[b];
   const int m = a.dense ? len : min(sh.M, len);
   const int i0 = s * a.split_len;
-  if (i0 >= m) return;  // empty split: takes no part in the combine
+  if (i0 >= m) return;  // empty split: the combine skips it
   const int i1 = min(m, i0 + a.split_len);
-  const int nvalid = (m + a.split_len - 1) / a.split_len;
 
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int ps = tid / LG, li = tid % LG;
   const float scale = 1.4426950408889634f * rsqrtf((float)D);
 
-  float q[GMAX][VEC];
+  float q[GT][VEC];
   const T* qrow = (const T*)a.q + ((size_t)r * sh.H_q + (size_t)g * G) * D + li * VEC;
 #pragma unroll
-  for (int hh = 0; hh < GMAX; ++hh) {
-    if (hh < G) {
-      V::load(qrow + (size_t)hh * D, q[hh]);
+  for (int hh = 0; hh < GT; ++hh) {
+    V::unpack(ld16(qrow + (size_t)min(hh, G - 1) * D), q[hh]);
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) q[hh][v] *= scale;
-    } else {
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) q[hh][v] = 0.f;
-    }
+    for (int v = 0; v < VEC; ++v) q[hh][v] *= scale;
   }
-  float acc[GMAX][VEC];
+  float mrun[GT], lrun[GT], acc[GT][VEC];
 #pragma unroll
-  for (int hh = 0; hh < GMAX; ++hh)
+  for (int hh = 0; hh < GT; ++hh) {
+    mrun[hh] = -INFINITY;
+    lrun[hh] = 0.f;
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[hh][v] = 0.f;
-  if (tid < GMAX) {
-    run_m[tid] = -INFINITY;
-    run_l[tid] = 0.f;
   }
-  const size_t kv_b = (size_t)b * sh.cap;
-  const T* kc = (const T*)a.k_cache;
-  const T* vc = (const T*)a.v_cache;
+  const size_t row_stride = (size_t)sh.H_kv * D;
+  const T* kb = (const T*)a.k_cache + ((size_t)b * sh.cap * sh.H_kv + g) * D + li * VEC;
+  const T* vb = (const T*)a.v_cache + ((size_t)b * sh.cap * sh.H_kv + g) * D + li * VEC;
   const int32_t* irow = a.idx ? a.idx + (size_t)r * a.idx_ld : nullptr;
 
-  for (int c0 = i0; c0 < i1; c0 += AT_CHUNK) {
-    const int cnt = min(AT_CHUNK, i1 - c0);
-    __syncthreads();  // previous chunk fully consumed
-    for (int p = tid; p < cnt; p += AT_THREADS) {
-      const int pp = a.dense ? c0 + p : irow[c0 + p];
-      pos[p] = min(max(pp, 0), len - 1);  // defensive: never read outside the row
+  for (int c0 = i0; c0 < i1; c0 += ROUND) {
+    int pos[AT_RP];
+    bool valid[AT_RP];
+#pragma unroll
+    for (int k = 0; k < AT_RP; ++k) {
+      const int i = c0 + ps + NG * k;
+      valid[k] = i < i1;
+      const int ii = min(i, i1 - 1);
+      const int pp = a.dense ? ii : irow[ii];
+      pos[k] = min(max(pp, 0), len - 1);  // defensive: never read outside the row
     }
-    __syncthreads();
-    // logits
-    for (int p = ps; p < cnt; p += NG) {
-      float kv[VEC];
-      V::load(kc + ((kv_b + pos[p]) * sh.H_kv + g) * D + li * VEC, kv);
+    uint4 kr[AT_RP], vr[AT_RP];
 #pragma unroll
-      for (int hh = 0; hh < GMAX; ++hh) {
-        if (hh < G) {
-          float dot = 0.f;
+    for (int k = 0; k < AT_RP; ++k) {
+      kr[k] = ld16(kb + (size_t)pos[k] * row_stride);
+      vr[k] = ld16(vb + (size_t)pos[k] * row_stride);
+    }
+    float lg[AT_RP][GT];
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) dot = fmaf(q[hh][v], kv[v], dot);
-          dot = group_sum(dot, LG);
-          if (li == 0) logit[p][hh] = dot;
-        }
+    for (int k = 0; k < AT_RP; ++k) {
+      float kf[VEC];
+      V::unpack(kr[k], kf);
+#pragma unroll
+      for (int hh = 0; hh < GT; ++hh) {
+        float dot = 0.f;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) dot = fmaf(q[hh][v], kf[v], dot);
+        lg[k][hh] = group_sum(dot, LG);
       }
     }
-    __syncthreads();
-    // chunk max / probabilities / sums: 32 lanes per head
-    {
-      const int hh = tid / 32, part = tid % 32;
-      if (hh < G) {
-        float mx = -INFINITY;
-        for (int p = part; p < cnt; p += 32) mx = fmaxf(mx, logit[p][hh]);
-        mx = group_max(mx, 32);
-        const float m_old = run_m[hh];
-        const float m_new = fmaxf(m_old, mx);
-        float sum = 0.f;
-        for (int p = part; p < cnt; p += 32) {
-          const float e = exp2f(logit[p][hh] - m_new);
-          logit[p][hh] = e;
-          sum += e;
-        }
-        sum = group_sum(sum, 32);
-        if (part == 0) {
-          const float f = exp2f(m_old - m_new);  // 0 on the first chunk
-          fac[hh] = f;
-          run_l[hh] = run_l[hh] * f + sum;
-          run_m[hh] = m_new;
-        }
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) {
+      float mx = mrun[hh];
+#pragma unroll
+      for (int k = 0; k < AT_RP; ++k)
+        if (valid[k]) mx = fmaxf(mx, lg[k][hh]);
+      const float f = scale_from(mrun[hh], mx);
+      float psum = 0.f;
+#pragma unroll
+      for (int k = 0; k < AT_RP; ++k) {
+        const float p = valid[k] ? exp2f(lg[k][hh] - mx) : 0.f;
+        lg[k][hh] = p;
+        psum += p;
       }
+      lrun[hh] = lrun[hh] * f + psum;
+      mrun[hh] = mx;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[hh][v] *= f;
     }
-    __syncthreads();
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh) {
-      if (hh < G) {
-        const float f = fac[hh];
+    for (int k = 0; k < AT_RP; ++k) {
+      float vf[VEC];
+      V::unpack(vr[k], vf);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[hh][v] *= f;
-      }
-    }
-    for (int p = ps; p < cnt; p += NG) {
-      float vv[VEC];
-      V::load(vc + ((kv_b + pos[p]) * sh.H_kv + g) * D + li * VEC, vv);
+      for (int hh = 0; hh < GT; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < GMAX; ++hh) {
-        if (hh < G) {
-          const float pr = logit[p][hh];
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) acc[hh][v] = fmaf(pr, vv[v], acc[hh][v]);
-        }
-      }
+        for (int v = 0; v < VEC; ++v) acc[hh][v] = fmaf(lg[k][hh], vf[v], acc[hh][v]);
     }
   }
-  // reduce the position slots: first inside the wave, then across waves
+
+  // merge the slots of the wave (xor partners hold the same dimensions)
 #pragma unroll
-  for (int hh = 0; hh < GMAX; ++hh) {
-    if (hh < G) {
+  for (int off = LG; off < WAVE; off <<= 1) {
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) {
+      const float mo = __shfl_xor(mrun[hh], off, WAVE);
+      const float lo = __shfl_xor(lrun[hh], off, WAVE);
+      const float mn = fmaxf(mrun[hh], mo);
+      const float f1 = scale_from(mrun[hh], mn), f2 = scale_from(mo, mn);
+      lrun[hh] = lrun[hh] * f1 + lo * f2;
+      mrun[hh] = mn;
 #pragma unroll
       for (int v = 0; v < VEC; ++v) {
-        float x = acc[hh][v];
-        for (int off = LG; off < WAVE; off <<= 1) x += __shfl_xor(x, off, WAVE);
-        acc[hh][v] = x;
+        const float ao = __shfl_xor(acc[hh][v], off, WAVE);
+        acc[hh][v] = acc[hh][v] * f1 + ao * f2;
       }
     }
   }
   if (lane < LG) {
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh)
-      if (hh < G)
+    for (int hh = 0; hh < GT; ++hh) {
+      if (lane == 0) {
+        wm[wave][hh] = mrun[hh];
+        wl[wave][hh] = lrun[hh];
+      }
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) red[wave][hh * D + li * VEC + v] = acc[hh][v];
+      for (int v = 0; v < VEC; ++v) wacc[wave][hh * D + li * VEC + v] = acc[hh][v];
+    }
   }
   __syncthreads();
 
   const int GD = G * D;
-  if (a.nsplit == 1) {
-    for (int e = tid; e < GD; e += AT_THREADS) {
-      const int hh = e / D, dim = e % D;
-      float o = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) o += red[w][e];
-      o = o / run_l[hh];
-      const int h = g * G + hh;
-      const size_t oi = ((size_t)r * sh.H_q + h) * D + dim;
-      if (a.gate_part) {
-        float gl = 0.f;
-        for (int c = 0; c < a.gate_chunks; ++c) gl += a.gate_part[((size_t)r * a.gate_chunks + c) * sh.H_q + h];
-        const float gv = sigmoidf(gl);
-        float ol = a.o_lin[oi];
-        if (a.lin_den) ol = ol / a.lin_den[(size_t)r * sh.H_q + h];
-        o = gv * o + (1.f - gv) * ol;
-      }
-      st1<T>((T*)a.out + oi, o);
-    }
-    return;
-  }
-
-  // split partial: unnormalised accumulator, running max and sum
   const int PS = GD + 2 * G;
-  float* mypart = a.part + (((size_t)r * sh.H_kv + g) * a.nsplit + s) * PS;
-  for (int e = tid; e < GD; e += AT_THREADS) {
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) o += red[w][e];
-    mypart[e] = o;
-  }
-  if (tid < G) {
-    mypart[GD + tid] = run_m[tid];
-    mypart[GD + G + tid] = run_l[tid];
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = atomicAdd(&a.counters[(size_t)r * sh.H_kv + g], 1u);
-    is_last = (prev == (unsigned)(nvalid - 1));
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  if (tid == 0) a.counters[(size_t)r * sh.H_kv + g] = 0u;  // ready for the next call
-  const float* p0 = a.part + ((size_t)r * sh.H_kv + g) * a.nsplit * PS;
+  float* mypart = a.nsplit > 1 ? a.part + (((size_t)r * sh.H_kv + g) * a.nsplit + s) * PS : nullptr;
   for (int e = tid; e < GD; e += AT_THREADS) {
     const int hh = e / D, dim = e % D;
     float mx = -INFINITY;
-    for (int sp = 0; sp < nvalid; ++sp) mx = fmaxf(mx, p0[(size_t)sp * PS + GD + hh]);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, wm[w][hh]);
     float l = 0.f, o = 0.f;
-    for (int sp = 0; sp < nvalid; ++sp) {
-      const float* ps_ = p0 + (size_t)sp * PS;
-      const float f = exp2f(ps_[GD + hh] - mx);
-      l = fmaf(ps_[GD + G + hh], f, l);
-      o = fmaf(ps_[e], f, o);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = scale_from(wm[w][hh], mx);
+      l = fmaf(wl[w][hh], f, l);
+      o = fmaf(wacc[w][e], f, o);
+    }
+    if (mypart) {
+      // split partial: unnormalised accumulator, max and sum; the combine
+      // kernel merges the splits (the kernel boundary orders the writes
+      // before its reads, with no device-scope fence here)
+      mypart[e] = o;
+      if (dim == 0) {
+        mypart[GD + hh] = mx;
+        mypart[GD + G + hh] = l;
+      }
+      continue;
     }
     o = o / l;
     const int h = g * G + hh;
@@ -501,15 +483,91 @@ __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
   }
 }
 
+// Merge the split partials of one (row, query head) and apply the epilogue.
+// Lane sp of every wave loads split sp's max and sum (vector loads; the
+// values are block-uniform and would otherwise become serialized scalar
+// loads); every thread loads its dimension of all split accumulators at once.
+template <typename T>
+__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
+  static_assert(AT_MAX_SPLITS <= WAVE, "one lane per split");
+  const Shape& sh = a.sh;
+  const int D = sh.d;
+  const int G = sh.H_q / sh.H_kv;
+  const int h = blockIdx.x % sh.H_q;
+  const int r = blockIdx.x / sh.H_q;
+  const int g = h / G, hh = h % G;
+  const int b = r / a.rows_per_seq, t = r % a.rows_per_seq;
+  const int len = a.prefill ? t + 1 : a.seq_lens[b];
+  const int m = a.dense ? len : min(sh.M, len);
+  const int nvalid = (m + a.split_len - 1) / a.split_len;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int dim = min(tid, D - 1);
+  const int GD = G * D, PS = GD + 2 * G;
+  const float* p0 = a.part + ((size_t)r * sh.H_kv + g) * a.nsplit * PS;
+  float ov[AT_MAX_SPLITS];
+#pragma unroll
+  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) ov[sp] = p0[(size_t)min(sp, nvalid - 1) * PS + hh * D + dim];
+  const int ls = min(lane, nvalid - 1);
+  const float m_l = p0[(size_t)ls * PS + GD + hh];
+  const float l_l = p0[(size_t)ls * PS + GD + G + hh];
+  float g_l = 0.f;
+  if (a.gate_part) {
+    const float* gp = a.gate_part + (size_t)r * a.gate_chunks * sh.H_q + h;
+    const float g0 = gp[(size_t)min(lane, a.gate_chunks - 1) * sh.H_q];
+    const float g1 = gp[(size_t)min(lane + WAVE, a.gate_chunks - 1) * sh.H_q];
+    g_l = (lane < a.gate_chunks ? g0 : 0.f) + (lane + WAVE < a.gate_chunks ? g1 : 0.f);
+    for (int c = lane + 2 * WAVE; c < a.gate_chunks; c += WAVE) g_l += gp[(size_t)c * sh.H_q];
+  }
+  const bool live = lane < nvalid;
+  const float mx = group_max(live ? m_l : -INFINITY, WAVE);
+  const float f_l = live ? scale_from(m_l, mx) : 0.f;  // weight of split `lane`
+  const float l = group_sum(l_l * f_l, WAVE);
+  float o = 0.f;
+#pragma unroll
+  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) {
+    const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_l), sp));
+    o = fmaf(ov[sp], f, o);
+  }
+  if (tid >= D) return;
+  o = o / l;
+  const size_t oi = ((size_t)r * sh.H_q + h) * D + tid;
+  if (a.gate_part) {
+    const float gv = sigmoidf(group_sum(g_l, WAVE));
+    float ol = a.o_lin[oi];
+    if (a.lin_den) ol = ol / a.lin_den[(size_t)r * sh.H_q + h];
+    o = gv * o + (1.f - gv) * ol;
+  }
+  st1<T>((T*)a.out + oi, o);
+}
+
+template <typename T, int D>
+static hipError_t launch_attn_td(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  const int G = a.sh.H_q / a.sh.H_kv;
+  if (G <= 2) hipLaunchKernelGGL((k_attention<T, D, 2>), grid, dim3(AT_THREADS), 0, st, a);
+  else if (G <= 4) hipLaunchKernelGGL((k_attention<T, D, 4>), grid, dim3(AT_THREADS), 0, st, a);
+  else if (G <= 5) hipLaunchKernelGGL((k_attention<T, D, 5>), grid, dim3(AT_THREADS), 0, st, a);
+  else if (G <= 7) hipLaunchKernelGGL((k_attention<T, D, 7>), grid, dim3(AT_THREADS), 0, st, a);
+  else hipLaunchKernelGGL((k_attention<T, D, 8>), grid, dim3(AT_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
+  if (a.nsplit > AT_MAX_SPLITS) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((size_t)a.n_rows * a.sh.H_kv * a.nsplit));
   switch (a.sh.d) {
-    case 32: hipLaunchKernelGGL((k_attention<T, 32>), grid, dim3(AT_THREADS), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_attention<T, 64>), grid, dim3(AT_THREADS), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((k_attention<T, 128>), grid, dim3(AT_THREADS), 0, st, a); break;
+    case 32: return launch_attn_td<T, 32>(a, grid, st);
+    case 64: return launch_attn_td<T, 64>(a, grid, st);
+    case 128: return launch_attn_td<T, 128>(a, grid, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename T>
+static hipError_t launch_combine_t(const AttnArgs& a, hipStream_t st) {
+  if (a.nsplit == 1) return hipSuccess;
+  const dim3 grid((unsigned)((size_t)a.n_rows * a.sh.H_q));
+  hipLaunchKernelGGL((k_attn_combine<T>), grid, dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
@@ -517,15 +575,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   return a.sh.dtype == 0 ? launch_attn_t<float>(a, st) : launch_attn_t<bf16_t>(a, st);
 }
 
-__global__ void k_zero_u32(uint32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
-hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_u32, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
-  return hipGetLastError();
+hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t st) {
+  return a.sh.dtype == 0 ? launch_combine_t<float>(a, st) : launch_combine_t<bf16_t>(a, st);
 }
 
 }  // namespace lisa

@@ -1,46 +1,142 @@
 // Top-M selection of indexer score rows ("LISA", arXiv 2607.19358v1,
 // Section 3.2 Stage 2: the M positions with the largest summed score).
 //
-// One 1024-thread block per row.  Each score becomes a 32-bit
-// order-preserving key; appending the position below it gives a composite key
-// that is unique per row, so "the M largest composites" is exactly "largest
-// score first, later position first on ties".  A most-significant-digit radix
-// select (8-bit digits, histograms in LDS) narrows the composite prefix until
-// the digit bin at the boundary is taken whole; the keys stay in registers.
-// The selected positions are then written in ascending order with a
-// block-wide prefix count of ballots, and optionally as a bitmask.
+// One block per row; each thread keeps the scores of its run of ITEMS
+// consecutive positions in registers.  The order is (score descending,
+// position descending) with -0.0 equal to +0.0; with the score mapped to an
+// order-preserving 32-bit key, the pair (key, position) is unique per row,
+// so the selected set is the set of pairs at or above one threshold pair.
+//
+// A row fits on one CU, whose SIMDs issue about one wave64 instruction per
+// cycle in total, so the kernel is built to issue few instructions per score
+// and few per wave:
+//   1. block min/max of the scores;
+//   2. one histogram pass with 2048 LDS bins of equal width in score value
+//      between min and max (bin(v) is monotone in v, so every higher bin is
+//      taken whole and every lower bin dropped); the boundary bin holds a
+//      few elements for realistic score distributions;
+//   3. the boundary bin's elements (at most 1024) are gathered and ranked
+//      exactly against each other, which gives the threshold pair; a larger
+//      boundary set (heavy ties, extreme outliers) gets further histogram
+//      passes over key bits and then positions until it is small enough;
+//   4. one block scan of per-thread selected counts gives every thread its
+//      place in the ascending output; selected positions are written by
+//      iterating the set bits of per-thread masks, optionally as a bitmask.
 #include "lisa_common.h"
 #include "lisa_kernels.h"
 
 namespace lisa {
 
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_WAVES = SEL_THREADS / WAVE;
+constexpr int NBINS_LOG = 11;
+constexpr int NBINS = 1 << NBINS_LOG;
+constexpr int SEL_CAND_MAX = 1024;  // boundary-set size resolved by exact ranking
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+__device__ __forceinline__ int bitlen(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
+
+template <int NW>
+struct SelShared {
+  uint32_t hist[NBINS];
+  alignas(16) uint32_t wa[NW];
+  alignas(16) uint32_t wb[NW];
+  uint32_t found_bin, found_need, found_cnt, cand_n;
+  uint64_t thr;
+  uint64_t cand[SEL_CAND_MAX];
+};
+
+// Block-wide min of a and max of b (uniform results): one LDS slot per
+// wave, then every wave reduces the NW slots with lane-parallel reads.
+template <int NW>
+__device__ __forceinline__ void block_min_max(SelShared<NW>& sm, uint32_t a, uint32_t b, uint32_t& mn,
+                                              uint32_t& mx) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  a = wave_min_u32(a);
+  b = wave_max_u32(b);
+  if (lane == 0) {
+    sm.wa[wave] = a;
+    sm.wb[wave] = b;
+  }
+  __syncthreads();
+  mn = wave_min_u32(sm.wa[lane % NW]);
+  mx = wave_max_u32(sm.wb[lane % NW]);
+  __syncthreads();
 }
 
-template <int ITEMS>
-__global__ __launch_bounds__(SEL_THREADS) void k_select(SelectArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t found_bin, found_need, found_cnt;
-  __shared__ uint32_t wcnt[ITEMS * SEL_WAVES];
-  __shared__ uint32_t wsum[SEL_WAVES];
+// Block-wide inclusive prefix sum in thread order, and the block total.
+template <int NW>
+__device__ __forceinline__ uint32_t block_incl_scan(SelShared<NW>& sm, uint32_t v, uint32_t& total) {
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const uint32_t inc = wave_incl_scan_u32(v);
+  if (lane == WAVE - 1) sm.wa[wave] = inc;
+  __syncthreads();
+  const uint32_t wi = wave_incl_scan_u32(lane < NW ? sm.wa[lane] : 0u);  // prefix over wave totals
+  const uint32_t all = rl(wi, NW - 1);
+  const uint32_t before = wave == 0 ? 0u : __builtin_amdgcn_readlane((int)wi, wave - 1);
+  __syncthreads();
+  total = all;
+  return before + inc;
+}
+
+// Find the bin holding the need-th largest element (bins counted from the
+// top).  Thread t owns the NBINS / THREADS consecutive bins from t * that.
+template <int THREADS>
+__device__ __forceinline__ void find_bin(SelShared<THREADS / WAVE>& sm, uint32_t need, uint32_t& bin,
+                                         uint32_t& need_in, uint32_t& cnt) {
+  constexpr int BPT = NBINS / THREADS;
+  const int tid = threadIdx.x;
+  uint32_t h[BPT];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    h[i] = sm.hist[tid * BPT + i];
+    tot += h[i];
+  }
+  uint32_t all;
+  const uint32_t inc = block_incl_scan(sm, tot, all);
+  uint32_t above = all - inc;  // elements in bins of higher threads
+#pragma unroll
+  for (int i = BPT - 1; i >= 0; --i) {
+    if (above < need && need <= above + h[i]) {
+      sm.found_bin = tid * BPT + i;
+      sm.found_need = need - above;
+      sm.found_cnt = h[i];
+    }
+    above += h[i];
+  }
+  __syncthreads();
+  bin = sm.found_bin;
+  need_in = sm.found_need;
+  cnt = sm.found_cnt;
+  __syncthreads();
+}
+
+// Keys of the row: in LDS when the row fits (LKEYS), else recomputed from
+// the score row in global memory (L2-resident after the first read).
+template <int THREADS, int ITEMS, bool LKEYS>
+struct KeyStore {
+  uint32_t k[LKEYS ? THREADS * ITEMS : 1];
+};
+
+template <int THREADS, int ITEMS, bool LKEYS>
+__global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
+  static_assert(ITEMS % 4 == 0 && ITEMS <= 64, "items per thread");
+  static_assert(NBINS % THREADS == 0, "bins per thread");
+  constexpr int NW = THREADS / WAVE;
+  __shared__ SelShared<NW> sm;
+  __shared__ KeyStore<THREADS, ITEMS, LKEYS> ks;
 
   const int r = blockIdx.x;
   const int b = r / a.rows_per_seq, t = r % a.rows_per_seq;
   const int len = a.prefill ? t + 1 : a.seq_lens[b];
   const int M = a.M;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   int32_t* orow = a.idx + (size_t)r * a.idx_ld;
   uint32_t* mrow = a.mask ? a.mask + (size_t)r * a.mask_ld : nullptr;
 
   if (len <= M) {  // the whole prefix is selected
-    for (int i = tid; i < M; i += SEL_THREADS) orow[i] = i < len ? i : -1;
+    for (int i = tid; i < M; i += THREADS) orow[i] = i < len ? i : -1;
     if (mrow) {
       const int words = (len + 31) / 32;
-      for (int w = tid; w < words; w += SEL_THREADS) {
+      for (int w = tid; w < words; w += THREADS) {
         const int rem = len - w * 32;
         mrow[w] = rem >= 32 ? 0xffffffffu : ((1u << rem) - 1u);
       }
@@ -49,121 +145,210 @@ __global__ __launch_bounds__(SEL_THREADS) void k_select(SelectArgs a) {
   }
 
   const float* srow = a.scores + ((size_t)b * a.stored_rows + (a.prefill ? t - a.first_row : 0)) * a.ld;
-  uint32_t key[ITEMS];
+  const int p0 = tid * ITEMS;
+  const int nval = max(0, min(ITEMS, len - p0));  // valid items: a prefix of the run
+  const uint64_t vmask = nval >= 64 ? ~0ull : ((1ull << nval) - 1ull);
+  float sv[ITEMS];
+  {
+    const int qmax = (len - 1) & ~3;  // last 4-aligned group that starts inside the row
+    float4 v[ITEMS / 4];
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int j = i * SEL_THREADS + tid;
-    key[i] = j < len ? score_key(srow[j]) : 0u;
+    for (int k = 0; k < ITEMS / 4; ++k) v[k] = *reinterpret_cast<const float4*>(srow + min(p0 + 4 * k, qmax));
+#pragma unroll
+    for (int k = 0; k < ITEMS / 4; ++k) {
+      sv[4 * k + 0] = v[k].x; sv[4 * k + 1] = v[k].y; sv[4 * k + 2] = v[k].z; sv[4 * k + 3] = v[k].w;
+    }
   }
-  // composite = key << PB | position, PB = bits of (len-1)
-  const int PB = 32 - __builtin_clz((unsigned)(len - 1));
-  const int TOT = 32 + PB;
-  uint64_t pref = 0;
-  int depth = 0;  // bits of the composite fixed so far
-  uint32_t need = (uint32_t)M;
+  // Items past the row end take a valid value of the thread (or of the row)
+  // so that they change neither the min nor the max.
+  if (nval < ITEMS) {
+    const float fill = nval > 0 ? sv[0] : srow[0];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+      if (k >= nval) sv[k] = fill;
+  }
+  if constexpr (LKEYS) {
+#pragma unroll
+    for (int k = 0; k < ITEMS / 4; ++k)
+      reinterpret_cast<uint4*>(ks.k + p0)[k] = make_uint4(score_key(sv[4 * k]), score_key(sv[4 * k + 1]),
+                                                          score_key(sv[4 * k + 2]), score_key(sv[4 * k + 3]));
+  }
+  auto key_at = [&](int k) -> uint32_t {  // key of item k of this thread (any k)
+    if constexpr (LKEYS) return ks.k[p0 + k];
+    else return score_key(srow[p0 + k]);
+  };
+  float fmn = sv[0], fmx = sv[0];
+#pragma unroll
+  for (int k = 1; k < ITEMS; ++k) {
+    fmn = fminf(fmn, sv[k]);
+    fmx = fmaxf(fmx, sv[k]);
+  }
+  if (tid == 0) sm.cand_n = 0u;
+  uint32_t lo, hi;  // key range of the boundary set
+  block_min_max(sm, score_key(fmn), score_key(fmx), lo, hi);
 
-  // at most ceil(48 / 8) passes: the composite has at most 32 + 16 bits
+  // Boundary set: elements of value bin bsel (every element without the
+  // value pass), narrowed later to keys in [lo, hi] and, once lo == hi,
+  // positions in [plo, phi].  Everything above it is selected; `need` of its
+  // `cnt` elements are.  `inset` holds this thread's members as bits.
+  uint32_t need = (uint32_t)M, cnt = (uint32_t)len;
+  uint32_t plo = 0, phi = (uint32_t)(len - 1);
+  uint32_t bins[ITEMS];
+  uint32_t bsel = 0;
+  {
+    const float vmin = __uint_as_float((lo & 0x80000000u) ? (lo & 0x7fffffffu) : ~lo);
+    const float vmax = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+    const float inv_w = (float)NBINS / (vmax - vmin);
+    if (lo != hi && inv_w > 0.f && inv_w < 1e30f) {
+#pragma unroll
+      for (int i = 0; i < NBINS / THREADS; ++i) sm.hist[tid + i * THREADS] = 0u;
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) bins[k] = min((uint32_t)((sv[k] - vmin) * inv_w), (uint32_t)(NBINS - 1));
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k)
+        if (k < nval) atomicAdd(&sm.hist[bins[k]], 1u);
+      __syncthreads();
+      find_bin<THREADS>(sm, need, bsel, need, cnt);
+    } else {
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) bins[k] = 0u;
+    }
+  }
+  uint64_t inset = 0;
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) inset |= (uint64_t)(bins[k] == bsel) << k;
+  inset &= vmask;
+
+  bool narrowed = false;  // [lo, hi] / [plo, phi] restrict the boundary set
+  uint64_t thr = 0;       // inside bin bsel: selected iff (key << 32 | pos) >= thr
   for (int pass = 0; pass < 8; ++pass) {
-    const int hi = TOT - depth;
-    const int w = hi < 8 ? hi : 8;
-    const int lo = hi - w;
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int j = i * SEL_THREADS + tid;
-      if (j < len) {
-        const uint64_t c = ((uint64_t)key[i] << PB) | (uint32_t)j;
-        if ((c >> hi) == pref) atomicAdd(&hist[(uint32_t)(c >> lo) & ((1u << w) - 1u)], 1u);
-      }
+    if (cnt == need) {  // the whole boundary set is taken
+      thr = narrowed ? (((uint64_t)lo << 32) | (lo == hi ? plo : 0u)) : 0ull;
+      break;
     }
-    __syncthreads();
-    if (wave == 0) {
-      // lane l owns bins 4l..4l+3; find the bin holding the need-th largest
-      uint32_t h4[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) h4[k] = hist[lane * 4 + k];
-      const uint32_t tot = h4[0] + h4[1] + h4[2] + h4[3];
-      uint32_t suf = tot;  // inclusive suffix sum over lanes >= l
-      for (int off = 1; off < WAVE; off <<= 1) {
-        const uint32_t o = __shfl_down(suf, off, WAVE);
-        if (lane + off < WAVE) suf += o;
+    if (cnt <= (uint32_t)SEL_CAND_MAX) {
+      // gather the boundary set (one LDS atomic per wave), then rank it
+      const uint32_t act = (uint32_t)__builtin_popcountll(inset);
+      const uint32_t winc = wave_incl_scan_u32(act);
+      uint32_t wbase = 0;
+      if (lane == WAVE - 1 && winc) wbase = atomicAdd(&sm.cand_n, winc);
+      uint32_t slot = rl(wbase, WAVE - 1) + winc - act;
+      for (uint64_t m = inset; m; m &= m - 1) {
+        const int k = __builtin_ctzll(m);
+        sm.cand[slot++] = ((uint64_t)key_at(k) << 32) | (uint32_t)(p0 + k);
       }
-      uint32_t above = suf - tot;  // keys in bins owned by higher lanes
+      __syncthreads();
+      for (uint32_t c = tid; c < cnt; c += THREADS) {
+        const uint64_t mine = sm.cand[c];
+        uint32_t above = 0;
+        uint32_t k = 0;
+        for (; k + 8 <= cnt; k += 8) {  // eight LDS reads in flight
+          uint64_t x[8];
 #pragma unroll
-      for (int k = 3; k >= 0; --k) {
-        if (above < need && need <= above + h4[k]) {
-          found_bin = (uint32_t)(lane * 4 + k);
-          found_need = need - above;
-          found_cnt = h4[k];
+          for (int u = 0; u < 8; ++u) x[u] = sm.cand[k + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) above += x[u] > mine ? 1u : 0u;
         }
-        above += h4[k];
+        for (; k < cnt; ++k) above += sm.cand[k] > mine ? 1u : 0u;
+        if (above == need - 1) sm.thr = mine;
       }
+      __syncthreads();
+      thr = sm.thr;
+      break;
+    }
+    // a boundary set too large to rank: one more histogram pass over key
+    // bits, or over positions once it is a single key value
+    if (!narrowed) {  // key range of the boundary bin
+      uint32_t bmin = 0xffffffffu, bmax = 0u;
+      for (uint64_t m = inset; m; m &= m - 1) {
+        const uint32_t kk = key_at(__builtin_ctzll(m));
+        bmin = min(bmin, kk);
+        bmax = max(bmax, kk);
+      }
+      block_min_max(sm, bmin, bmax, lo, hi);
+      narrowed = true;
+    }
+    const bool by_pos = lo == hi;
+#pragma unroll
+    for (int i = 0; i < NBINS / THREADS; ++i) sm.hist[tid + i * THREADS] = 0u;
+    __syncthreads();
+    const int shift = by_pos ? max(0, bitlen(phi - plo) - NBINS_LOG) : max(0, bitlen(hi - lo) - NBINS_LOG);
+    for (uint64_t m = inset; m; m &= m - 1) {
+      const int k = __builtin_ctzll(m);
+      const uint32_t pos = (uint32_t)(p0 + k);
+      atomicAdd(&sm.hist[by_pos ? (pos - plo) >> shift : (key_at(k) - lo) >> shift], 1u);
     }
     __syncthreads();
-    const uint32_t bin = found_bin;
-    need = found_need;
-    pref = (pref << w) | bin;
-    depth += w;
-    if (found_cnt == need) break;
+    uint32_t bin, need_in, c;
+    find_bin<THREADS>(sm, need, bin, need_in, c);
+    if (!by_pos) {
+      const uint32_t nlo = lo + (bin << shift);
+      const uint64_t top = (uint64_t)nlo + ((1ull << shift) - 1ull);
+      hi = (uint32_t)(top < (uint64_t)hi ? top : (uint64_t)hi);
+      lo = nlo;
+    } else {
+      const uint32_t nplo = plo + (bin << shift);
+      phi = min(phi, nplo + ((1u << shift) - 1u));
+      plo = nplo;
+    }
+    need = need_in;
+    cnt = c;
+    // keep the members of the narrowed set
+    uint64_t keep = 0;
+    for (uint64_t m = inset; m; m &= m - 1) {
+      const int k = __builtin_ctzll(m);
+      const uint32_t kk = key_at(k), pos = (uint32_t)(p0 + k);
+      if (kk >= lo && kk <= hi && (lo != hi || (pos >= plo && pos <= phi))) keep |= 1ull << k;
+    }
+    inset = keep;
   }
-  const int shift = TOT - depth;
 
-  // ascending compaction of the selected positions
+  // selection bits: higher value bins whole, the boundary bin by threshold
   uint64_t selbits = 0;
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int j = i * SEL_THREADS + tid;
-    bool sel = false;
-    if (j < len) {
-      const uint64_t c = ((uint64_t)key[i] << PB) | (uint32_t)j;
-      sel = (c >> shift) >= pref;
-    }
-    const uint64_t bal = __ballot(sel);
-    if (sel) selbits |= (1ull << i);
-    if (lane == 0) wcnt[i * SEL_WAVES + wave] = (uint32_t)__builtin_popcountll(bal);
-    if (mrow && (lane & 31) == 0) {
-      const int word = (i * SEL_THREADS + wave * WAVE + lane) >> 5;
-      if (word * 32 < len) mrow[word] = (uint32_t)(bal >> (lane & 32));
-    }
-  }
-  __syncthreads();
-  // exclusive scan of wcnt in (i, wave) order = ascending position order
-  constexpr int E = ITEMS * SEL_WAVES;
-  uint32_t v = tid < E ? wcnt[tid] : 0u;
-  uint32_t inc = v;
-  for (int off = 1; off < WAVE; off <<= 1) {
-    const uint32_t o = __shfl_up(inc, off, WAVE);
-    if (lane >= off) inc += o;
-  }
-  if (lane == WAVE - 1) wsum[wave] = inc;
-  __syncthreads();
-  uint32_t wpre = 0;
-  for (int k = 0; k < wave; ++k) wpre += wsum[k];
-  __syncthreads();
-  if (tid < E) wcnt[tid] = wpre + inc - v;
-  __syncthreads();
+  for (int k = 0; k < ITEMS; ++k) selbits |= (uint64_t)(bins[k] > bsel) << k;
+  {
+    uint64_t bm = 0;
 #pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const bool sel = (selbits >> i) & 1ull;
-    const uint64_t bal = __ballot(sel);
-    if (sel) {
-      const uint32_t o = wcnt[i * SEL_WAVES + wave] + lanes_below(bal);
-      if (o < (uint32_t)M) orow[o] = i * SEL_THREADS + tid;
+    for (int k = 0; k < ITEMS; ++k) bm |= (uint64_t)(bins[k] == bsel) << k;
+    for (bm &= vmask; bm; bm &= bm - 1) {
+      const int k = __builtin_ctzll(bm);
+      if ((((uint64_t)key_at(k)) << 32 | (uint32_t)(p0 + k)) >= thr) selbits |= 1ull << k;
+    }
+  }
+  selbits &= vmask;
+  const uint32_t nsel = (uint32_t)__builtin_popcountll(selbits);
+  uint32_t total;
+  uint32_t o = block_incl_scan(sm, nsel, total) - nsel;
+  for (uint64_t m = selbits; m; m &= m - 1) {
+    if (o < (uint32_t)M) orow[o] = p0 + __builtin_ctzll(m);
+    ++o;
+  }
+  if (mrow) {
+    if constexpr (ITEMS >= 32) {
+#pragma unroll
+      for (int w = 0; w < ITEMS / 32; ++w)
+        if (p0 + 32 * w < len) mrow[(p0 >> 5) + w] = (uint32_t)(selbits >> (32 * w));
+    } else {
+      // 32 / ITEMS threads share a word: OR their shifted bits together
+      constexpr int TPW = 32 / ITEMS;
+      uint32_t word = (uint32_t)selbits << ((tid % TPW) * ITEMS);
+      for (int off = 1; off < TPW; off <<= 1) word |= (uint32_t)__shfl_xor((int)word, off, WAVE);
+      if (tid % TPW == 0 && p0 < len) mrow[p0 >> 5] = word;
     }
   }
   const int m = M < len ? M : len;
-  for (int k = m + tid; k < M; k += SEL_THREADS) orow[k] = -1;
+  for (int k = m + tid; k < M; k += THREADS) orow[k] = -1;
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)a.n_rows), block(SEL_THREADS);
-  if (a.max_len <= 1 * SEL_THREADS) hipLaunchKernelGGL(k_select<1>, grid, block, 0, st, a);
-  else if (a.max_len <= 4 * SEL_THREADS) hipLaunchKernelGGL(k_select<4>, grid, block, 0, st, a);
-  else if (a.max_len <= 16 * SEL_THREADS) hipLaunchKernelGGL(k_select<16>, grid, block, 0, st, a);
-  else if (a.max_len <= 32 * SEL_THREADS) hipLaunchKernelGGL(k_select<32>, grid, block, 0, st, a);
-  else if (a.max_len <= 64 * SEL_THREADS) hipLaunchKernelGGL(k_select<64>, grid, block, 0, st, a);
+  const dim3 grid((unsigned)a.n_rows);
+  if (a.max_len <= 256 * 16) hipLaunchKernelGGL((k_select<256, 16, true>), grid, dim3(256), 0, st, a);
+  else if (a.max_len <= 1024 * 16) hipLaunchKernelGGL((k_select<1024, 16, true>), grid, dim3(1024), 0, st, a);
+  else if (a.max_len <= 1024 * 32) hipLaunchKernelGGL((k_select<1024, 32, true>), grid, dim3(1024), 0, st, a);
+  else if (a.max_len <= 1024 * 64) hipLaunchKernelGGL((k_select<1024, 64, false>), grid, dim3(1024), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

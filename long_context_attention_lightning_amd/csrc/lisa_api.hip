@@ -111,10 +111,10 @@ void decode_split(const Shape& sh, int positions, int& nsplit, int& split_len) {
   nsplit = (positions + sl - 1) / sl;
 }
 
-int decode_gate_chunks(const Shape& sh) { return (sh.hidden + 255) / 256; }
+int decode_gate_chunks(const Shape& sh) { return (sh.hidden + 63) / 64; }
 
 struct DecodeWs {
-  size_t scores, idx, o_lin, lin_den, gate, part, counters, total;
+  size_t scores, idx, o_lin, lin_den, gate, part, total;
   int nsplit, split_len;
 };
 
@@ -128,13 +128,12 @@ DecodeWs decode_ws(const Shape& sh) {
   w.lin_den = L.take((size_t)sh.B * sh.H_L * 4);
   w.gate = L.take((size_t)sh.B * decode_gate_chunks(sh) * sh.H_q * 4);
   w.part = L.take(attention_partial_floats(sh, sh.B, w.nsplit) * 4);
-  w.counters = L.take((size_t)sh.B * sh.H_kv * 4);
   w.total = L.off;
   return w;
 }
 
 struct DenseWs {
-  size_t part, counters, total;
+  size_t part, total;
   int nsplit, split_len;
 };
 
@@ -143,7 +142,6 @@ DenseWs dense_ws(const Shape& sh) {
   Layout L;
   decode_split(sh, sh.max_len, w.nsplit, w.split_len);
   w.part = L.take(attention_partial_floats(sh, sh.B, w.nsplit) * 4);
-  w.counters = L.take((size_t)sh.B * sh.H_kv * 4);
   w.total = L.off;
   return w;
 }
@@ -199,7 +197,7 @@ struct Timing {
 
 const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
-    "prefill_linear", "prefill_attention", "linear_state_update", "zero_counters"};
+    "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine"};
 
 bool timing_on(int kid) { return g_timing.kid == kid && g_timing.count < g_timing.n; }
 
@@ -311,7 +309,6 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   pa.scores = at<float>(ws, w.scores); pa.scores_ld = decode_scores_ld(sh);
   pa.o_lin = at<float>(ws, w.o_lin); pa.lin_den = at<float>(ws, w.lin_den);
   pa.gate_part = at<float>(ws, w.gate); pa.gate_chunks = decode_gate_chunks(sh);
-  pa.counters = at<uint32_t>(ws, w.counters); pa.n_counters = sh.B * sh.H_kv;
   pa.append = 1; pa.do_scores = 1; pa.do_linear = 1; pa.do_gate = 1; pa.linear_output = 1;
   LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
 
@@ -326,9 +323,10 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   aa.sh = sh; aa.n_rows = sh.B; aa.rows_per_seq = 1; aa.prefill = 0; aa.dense = 0; aa.seq_lens = seq_lens;
   aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = idx; aa.idx_ld = sh.M;
   aa.nsplit = w.nsplit; aa.split_len = w.split_len; aa.part = at<float>(ws, w.part);
-  aa.counters = pa.counters; aa.gate_part = pa.gate_part; aa.gate_chunks = pa.gate_chunks;
+  aa.gate_part = pa.gate_part; aa.gate_chunks = pa.gate_chunks;
   aa.o_lin = pa.o_lin; aa.lin_den = (sh.flags & LISA_LINEAR_UNNORMALIZED) ? nullptr : pa.lin_den; aa.out = out;
   LAUNCH(KID_ATTN, st, launch_attention(aa, st));
+  LAUNCH(KID_ATTN_COMBINE, st, launch_attention_combine(aa, st));
   return LISA_OK;
 }
 
@@ -343,15 +341,14 @@ int lisa_dense_decode(const lisa_shape* shape, const int32_t* seq_lens, const vo
   const DenseWs w = dense_ws(sh);
   if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
   hipStream_t st = (hipStream_t)stream;
-  uint32_t* counters = at<uint32_t>(ws, w.counters);
-  LAUNCH(KID_ZERO, st, launch_zero_u32(counters, sh.B * sh.H_kv, st));
   AttnArgs aa{};
   aa.sh = sh; aa.n_rows = sh.B; aa.rows_per_seq = 1; aa.prefill = 0; aa.dense = 1; aa.seq_lens = seq_lens;
   aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = nullptr; aa.idx_ld = 0;
   aa.nsplit = w.nsplit; aa.split_len = w.split_len; aa.part = at<float>(ws, w.part);
-  aa.counters = counters; aa.gate_part = nullptr; aa.gate_chunks = 0; aa.o_lin = nullptr; aa.lin_den = nullptr;
+  aa.gate_part = nullptr; aa.gate_chunks = 0; aa.o_lin = nullptr; aa.lin_den = nullptr;
   aa.out = out;
   LAUNCH(KID_ATTN, st, launch_attention(aa, st));
+  LAUNCH(KID_ATTN_COMBINE, st, launch_attention_combine(aa, st));
   return LISA_OK;
 }
 
@@ -375,8 +372,9 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n, const i
   REQUIRE_PTR(idx_out);
   OPTIONAL_PTR(scores_in);
   OPTIONAL_PTR(scores_out);
-  if ((scores_in || scores_out) && scores_ld < longest)
-    return fail(LISA_ERR_INVALID_ARG, "scores_ld %lld < longest row %d", (long long)scores_ld, longest);
+  if ((scores_in || scores_out) && (scores_ld < longest || scores_ld % 4))
+    return fail(LISA_ERR_INVALID_ARG, "scores_ld %lld must be a multiple of 4 and >= the longest row %d",
+                (long long)scores_ld, longest);
   if (!scores_in) {
     REQUIRE_PTR(q_idx); REQUIRE_PTR(k_idx_cache); REQUIRE_PTR(w_idx);
   }
@@ -481,7 +479,7 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
   AttnArgs aa{};
   aa.sh = sh; aa.n_rows = sh.B * n; aa.rows_per_seq = n; aa.prefill = 1; aa.dense = 0; aa.seq_lens = nullptr;
   aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = idx; aa.idx_ld = sh.M;
-  aa.nsplit = 1; aa.split_len = sh.M; aa.part = nullptr; aa.counters = nullptr;
+  aa.nsplit = 1; aa.split_len = sh.M; aa.part = nullptr;
   aa.gate_part = ga.gate_part; aa.gate_chunks = 1; aa.o_lin = la.o_lin; aa.lin_den = nullptr; aa.out = out;
   LAUNCH(KID_PREFILL_ATTN, st, launch_attention(aa, st));
   return LISA_OK;

@@ -19,7 +19,7 @@ enum KernelId {
   KID_PREFILL_LINEAR = 5,
   KID_PREFILL_ATTN = 6,
   KID_LINEAR_UPDATE = 7,
-  KID_ZERO = 8,
+  KID_ATTN_COMBINE = 8,
   KID_COUNT = 9
 };
 
@@ -40,8 +40,6 @@ struct PhaseAArgs {
   float* lin_den;      // [B, H_L] denominators phi(q) . z_new (normalised mode)
   float* gate_part;    // [B, gate_chunks, H_q]  (pre-sigmoid partial dots)
   int gate_chunks;
-  uint32_t* counters;  // zeroed by this kernel
-  int n_counters;
   int append;          // write the new token into the caches
   int do_scores, do_linear, do_gate;
   int linear_output;   // write o_lin
@@ -85,16 +83,15 @@ struct AttnArgs {
   int64_t idx_ld;
   int nsplit, split_len;    // positions per split
   float* part;              // partials
-  uint32_t* counters;       // [n_rows, H_kv] when nsplit > 1
   const float* gate_part;   // nullable [n_rows, gate_chunks, H_q] pre-sigmoid
   int gate_chunks;
   const float* o_lin;       // [n_rows, H_q, d] (with gate)
   const float* lin_den;     // nullable [n_rows, H_q]: o_lin is divided by it
   void* out;                // [n_rows, H_q, d] T
 };
-hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);          // split kernel
+hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t st);  // merge (nsplit > 1)
 size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit);
 
-hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t st);
 
 }  // namespace lisa

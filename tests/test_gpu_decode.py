@@ -7,7 +7,7 @@ import torch
 import oracle
 from lisa_inputs import CONFIGS, decode_inputs
 from gpu_helpers import (RECALL_MIN, assert_out_close, assert_state_close, check_idx_format,
-                         gpu_decode, gpu_dense_decode, out_errors, recall, host)
+                         gpu_decode, gpu_dense_decode, out_errors, recall, host, saturate_gate)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +29,21 @@ def _parity(cfg, inp, M, label, flags=0):
     return g, ref
 
 
+def _branches(cfg, inp, M, label):
+    """Each branch alone, through an exactly saturated gate."""
+    for sign, key in ((1.0, "o_sparse"), (-1.0, "o_linear")):
+        sat = saturate_gate(inp, sign)
+        g = gpu_decode(cfg, sat, M=M)
+        ref = oracle.decode_step(sat, M)
+        np.testing.assert_array_equal(ref["out"], ref[key])
+        assert_out_close(cfg, g["out"], ref[key], f"{label} {key}")
+
+
 def test_decode_c1_qwen7b_16k():
     cfg = CONFIGS[1]
-    _parity(cfg, decode_inputs(cfg, 1), cfg.M, "C1")
+    inp = decode_inputs(cfg, 1)
+    _parity(cfg, inp, cfg.M, "C1")
+    _branches(cfg, inp, cfg.M, "C1")
 
 
 def test_decode_c2_ragged_batch32():
@@ -39,6 +51,7 @@ def test_decode_c2_ragged_batch32():
     inp = decode_inputs(cfg, 2)
     assert inp["seq_lens"].min() >= 4096 and inp["seq_lens"].max() <= 16384
     _parity(cfg, inp, cfg.M, "C2")
+    _branches(cfg, inp, cfg.M, "C2")
 
 
 @pytest.mark.slow
@@ -72,6 +85,7 @@ def test_decode_small_shapes(label, over, lens, M):
     base = CONFIGS[1].replace(B=len(lens), L=0, cap=max(lens) + 3, **over)
     inp = decode_inputs(base, 11, seq_lens=np.array(lens, np.int32))
     _parity(base, inp, M, label)
+    _branches(base, inp, M, label)
 
 
 def test_decode_signed_head_weights():

@@ -8,7 +8,7 @@ import long_context_attention_lightning_amd as L
 import oracle
 from lisa_inputs import CONFIGS, prefill_inputs, decode_inputs, row_sample
 from gpu_helpers import (RECALL_MIN, assert_out_close, assert_state_close, check_idx_format,
-                         dev, gpu_decode, gpu_prefill, host, recall, shape_of, tdtype)
+                         dev, gpu_decode, gpu_prefill, host, recall, saturate_gate, shape_of, tdtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,6 +24,10 @@ def _full_parity(cfg, inp, M, label):
         assert rc >= RECALL_MIN
     assert_out_close(cfg, g["out"], ref["out"], label)
     assert_state_close(g["S"], g["z"], ref["S"], ref["z"], label)
+    for sign, key in ((1.0, "o_sparse"), (-1.0, "o_linear")):
+        sat = saturate_gate(inp, sign)
+        gs = gpu_prefill(cfg, sat, M=M, want_idx=False)
+        assert_out_close(cfg, gs["out"], ref[key], f"{label} {key}")
     return g, ref
 
 
