@@ -42,8 +42,11 @@ def parse():
     p.add_argument("--nbuf", type=int, default=32, help="rotating buffer sets (>= 512 MB total)")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-dense", action="store_true", help="skip the dense-attention decode baseline")
     p.add_argument("--prefill-iters", type=int, default=5)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run four 256 MiB device copies (a counter-scaling reference)")
     return p.parse_args()
 
 
@@ -73,6 +76,39 @@ def attention_bytes(cfg, L, M, B, dense=False):
     return B * (m * cfg.H_kv * cfg.d * 4 + 2 * 2 * cfg.H_q * cfg.d)
 
 
+def combine_bytes(cfg, B):
+    """The epilogue's own inputs and output: linear numerators and
+    denominators, gate logits, the bf16 output."""
+    return B * (cfg.H_L * cfg.d * 4 + cfg.H_L * 4 + ((cfg.hidden + 63) // 64) * cfg.H_q * 4
+                + cfg.H_q * cfg.d * 2)
+
+
+# Integer work a radix select must do per score: order-preserving key (2),
+# bin index (3), histogram increment (1), threshold compare (1), output
+# compaction (1).
+SELECT_OPS_PER_KEY = 8
+# Chip-wide 32-bit VALU lane operations per second: 256 CUs x 4 SIMDs x 16
+# lanes per cycle x 2.4 GHz (fp32 FMA counted as 2 flops gives 157.3 TFLOP/s).
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+
+def kernel_roofline(name, avg_ms, work, bound):
+    """Roofline entry of one kernel: algorithmic work per launch over its
+    average launch duration against the published (or derived) peak."""
+    if bound == "hbm":
+        achieved = work / (avg_ms * 1e-3) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    elif bound == "mfma":
+        achieved = work / (avg_ms * 1e-3) / 1e12
+        peak, unit = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved = work / (avg_ms * 1e-3) / 1e12
+        peak, unit = ALU_PEAK_TOPS, "TOP/s"
+    return {"kernel": name, "bound": bound, "achieved": round(achieved, 4), "peak": round(peak, 1),
+            "unit": unit, "frac": round(achieved / peak, 5), "traffic": load_traffic(name),
+            "algorithmic_work_per_launch": work, "avg_launch_us": round(avg_ms * 1e3, 3)}
+
+
 # ----------------------------------------------------------------------------
 def main():
     args = parse()
@@ -94,6 +130,13 @@ def main():
     T = torch.bfloat16
     print(f"# bench: {cfg.name} B={B} L={Lctx} M={M} nbuf={args.nbuf}", file=sys.stderr, flush=True)
 
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):  # elementwise kernel: reads 256 MiB, writes 256 MiB
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     inp = decode_inputs(cfg, cid)
 
     def up(a, dt=T):
@@ -194,37 +237,37 @@ def main():
           file=sys.stderr, flush=True)
 
     # dense baseline over the same caches
-    g_dense = capture(dense_step)
-    ms_dense, _ = time_graph(g_dense)
-    kd = kernel_times(dense_step, (2, 8))
-    dense_kernel_us = {Lb.lisa_kernel_name(k): round(v * 1e3, 3) for k, v in kd.items()}
+    if not args.no_dense:
+        g_dense = capture(dense_step)
+        ms_dense, _ = time_graph(g_dense)
+        kd = kernel_times(dense_step, (2, 8))
+        dense_kernel_us = {Lb.lisa_kernel_name(k): round(v * 1e3, 3) for k, v in kd.items()}
+        del g_dense
 
     tok_s = B / (ms_step * 1e-3)
-    dname = Lb.lisa_kernel_name(dom)
-    algo = {0: phase_a_bytes(cfg, Lctx, B), 1: None, 2: attention_bytes(cfg, Lctx, M, B), 8: None}
-    if algo[dom] is not None:
-        achieved = algo[dom] / (dom_ms * 1e-3) / 1e9
-        roof = {"kernel": dname, "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic(dname), "algorithmic_bytes": algo[dom],
-                "avg_launch_us": round(dom_ms * 1e3, 3)}
-    else:
-        roof = {"kernel": dname, "bound": "alu", "achieved": None, "peak": None,
-                "unit": None, "frac": None, "traffic": None, "avg_launch_us": round(dom_ms * 1e3, 3)}
+    work = {0: (phase_a_bytes(cfg, Lctx, B), "hbm"),
+            1: (SELECT_OPS_PER_KEY * Lctx * B, "alu"),
+            2: (attention_bytes(cfg, Lctx, M, B), "hbm"),
+            8: (combine_bytes(cfg, B), "hbm")}
+    roofs = {Lb.lisa_kernel_name(k): kernel_roofline(Lb.lisa_kernel_name(k), kt[k], *work[k]) for k in dec_kids}
+    roof = roofs[Lb.lisa_kernel_name(dom)]
     step_bytes = decode_bytes(cfg, Lctx, M, B)
     extra = {
         "us_per_step": round(ms_step * 1e3, 3),
         "kernel_us": {k: round(v * 1e3, 3) for k, v in per_kernel_ms.items()},
-        "kernel_timing": "HIP events around each kernel, eager steps over the same buffer sets",
+        "kernel_timing": "hipExtLaunchKernel start/stop events on each kernel's dispatch, eager steps "
+                         "over the same buffer sets right after the timed graph replays",
+        "kernel_roofline": roofs,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_roofline_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "dense_decode_us_per_step": round(ms_dense * 1e3, 3),
-        "dense_decode_kernel_us": dense_kernel_us,
-        "dense_decode_tok_s": round(B / (ms_dense * 1e-3), 1),
-        "speedup_vs_dense_decode": round(ms_dense / ms_step, 3),
         "pages_context": "about 50% end-to-end inference speedup at 16K context (other hardware, whole model)",
     }
-    del g_main, g_dense
+    if not args.no_dense:
+        extra.update({"dense_decode_us_per_step": round(ms_dense * 1e3, 3),
+                      "dense_decode_kernel_us": dense_kernel_us,
+                      "dense_decode_tok_s": round(B / (ms_dense * 1e-3), 1),
+                      "speedup_vs_dense_decode": round(ms_dense / ms_step, 3)})
+    del g_main
     sets.clear()
     torch.cuda.empty_cache()
 
@@ -249,25 +292,26 @@ def main():
 
 
 def load_traffic(kernel):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; otherwise None."""
+    """HBM bytes per launch from committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy kernel's reading), if
+    they were taken on the kernel's current source files; otherwise None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        data = json.load(open(path))
-        ent = data.get(kernel)
-        if not ent or ent.get("source_sha256") != source_hash():
+        ent = json.load(open(path)).get(kernel)
+        if not ent or ent.get("source_sha256") != source_hash(ent.get("sources", [])):
             return None
         return ent.get("bytes_per_launch")
     except Exception:
         return None
 
 
-def source_hash():
+def source_hash(files):
+    """sha256 over the named files of the package's csrc directory, in order."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_attention_lightning_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in files:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
@@ -300,7 +344,7 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     kern = {}
     call()
     torch.cuda.synchronize()
-    for kid in (4, 5, 3, 1, 6):
+    for kid in (4, 5, 3, 1, 6):  # one launch each per call
         st = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         sp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for e in st + sp:
@@ -310,7 +354,7 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
         torch.cuda.synchronize()
         cnt = Lb.lisa_timing_count()
         Lb.lisa_timing_enable(0)
-        kern[Lb.lisa_kernel_name(kid)] = round(sum(a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])) * 1e3, 1)
+        kern[Lb.lisa_kernel_name(kid)] = round(st[0].elapsed_time(sp[0]) * 1e3, 1) if cnt else 0.0
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -319,11 +363,22 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.prefill_iters
-    idx_flops = 2.0 * cfg.H_I * cfg.d_I * (n * (n + 1) / 2)
+    # algorithmic work of each prefill kernel (rows t < M take every key and are not scored)
+    r0 = min(M, n)
+    scored_pairs = (n * (n + 1) - r0 * (r0 + 1)) // 2
+    attn_pairs = sum(min(M, t + 1) for t in range(n))
+    lin_bytes = 3 * n * cfg.H_L * cfg.d * 2 + 2 * 4 * cfg.H_L * cfg.d * (cfg.d + 1)
+    pwork = {
+        "prefill_index_scores": (2 * cfg.H_I * cfg.d_I * scored_pairs, "mfma"),
+        "prefill_linear": (lin_bytes, "hbm"),
+        "prefill_attention": (4 * cfg.H_q * cfg.d * attn_pairs, "mfma"),
+        "prefill_gate": (n * cfg.hidden * 2 + cfg.hidden * cfg.H_q * 2 + n * cfg.H_q * 4, "hbm"),
+        "topm_select": (SELECT_OPS_PER_KEY * scored_pairs, "alu"),
+    }
+    proofs = {k: kernel_roofline(k, kern[k] * 1e-3, *pwork[k]) for k in pwork if kern.get(k)}
     res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
            "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
-           "prefill_indexer_mfma_frac": round(idx_flops / (kern["prefill_index_scores"] * 1e-6) / 1e12
-                                              / MFMA_BF16_PEAK_TFLOPS, 4)}
+           "prefill_kernel_roofline": proofs}
     del ws, t, out
     torch.cuda.empty_cache()
     return res

@@ -262,7 +262,7 @@ static hipError_t launch_pa(const PhaseAArgs& a, hipStream_t st) {
   const int n_gate = a.do_gate ? sh.B * a.gate_chunks : 0;
   const int grid = n_idx + n_lin + n_gate;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_decode_phase_a<T, R>), dim3(grid), dim3(PA_THREADS), 0, st, a, n_idx, tiles, tile_rows,
+  klaunch((k_decode_phase_a<T, R>), dim3(grid), dim3(PA_THREADS), 0, st, a, n_idx, tiles, tile_rows,
                      n_lin, slices);
   return hipGetLastError();
 }
@@ -543,11 +543,11 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
 template <typename T, int D>
 static hipError_t launch_attn_td(const AttnArgs& a, dim3 grid, hipStream_t st) {
   const int G = a.sh.H_q / a.sh.H_kv;
-  if (G <= 2) hipLaunchKernelGGL((k_attention<T, D, 2>), grid, dim3(AT_THREADS), 0, st, a);
-  else if (G <= 4) hipLaunchKernelGGL((k_attention<T, D, 4>), grid, dim3(AT_THREADS), 0, st, a);
-  else if (G <= 5) hipLaunchKernelGGL((k_attention<T, D, 5>), grid, dim3(AT_THREADS), 0, st, a);
-  else if (G <= 7) hipLaunchKernelGGL((k_attention<T, D, 7>), grid, dim3(AT_THREADS), 0, st, a);
-  else hipLaunchKernelGGL((k_attention<T, D, 8>), grid, dim3(AT_THREADS), 0, st, a);
+  if (G <= 2) klaunch((k_attention<T, D, 2>), grid, dim3(AT_THREADS), 0, st, a);
+  else if (G <= 4) klaunch((k_attention<T, D, 4>), grid, dim3(AT_THREADS), 0, st, a);
+  else if (G <= 5) klaunch((k_attention<T, D, 5>), grid, dim3(AT_THREADS), 0, st, a);
+  else if (G <= 7) klaunch((k_attention<T, D, 7>), grid, dim3(AT_THREADS), 0, st, a);
+  else klaunch((k_attention<T, D, 8>), grid, dim3(AT_THREADS), 0, st, a);
   return hipGetLastError();
 }
 
@@ -567,7 +567,7 @@ template <typename T>
 static hipError_t launch_combine_t(const AttnArgs& a, hipStream_t st) {
   if (a.nsplit == 1) return hipSuccess;
   const dim3 grid((unsigned)((size_t)a.n_rows * a.sh.H_q));
-  hipLaunchKernelGGL((k_attn_combine<T>), grid, dim3(128), 0, st, a);
+  klaunch((k_attn_combine<T>), grid, dim3(128), 0, st, a);
   return hipGetLastError();
 }
 

@@ -92,9 +92,9 @@ hipError_t launch_index_scores(const IndexScoreArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.n + IS_TILE - 1) / IS_TILE), (unsigned)((rows + IS_TILE - 1) / IS_TILE),
                   (unsigned)a.sh.B);
   if (a.sh.dtype == 0)
-    hipLaunchKernelGGL(k_index_scores_generic<float>, grid, dim3(256), 0, st, a);
+    klaunch(k_index_scores_generic<float>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_index_scores_generic<bf16_t>, grid, dim3(256), 0, st, a);
+    klaunch(k_index_scores_generic<bf16_t>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -152,9 +152,9 @@ hipError_t launch_gate_logits(const GateArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)((a.n_rows + GT_ROWS - 1) / GT_ROWS));
   if (a.sh.dtype == 0)
-    hipLaunchKernelGGL(k_gate_logits<float>, grid, dim3(256), 0, st, a);
+    klaunch(k_gate_logits<float>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_gate_logits<bf16_t>, grid, dim3(256), 0, st, a);
+    klaunch(k_gate_logits<bf16_t>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -258,9 +258,9 @@ hipError_t launch_linear_recurrent(const LinearArgs& a, hipStream_t st) {
   const int slices = a.sh.d / LR_COLS;
   const dim3 grid((unsigned)(a.sh.B * a.sh.H_L * slices));
   if (a.sh.dtype == 0)
-    hipLaunchKernelGGL(k_linear_recurrent<float>, grid, dim3(256), 0, st, a);
+    klaunch(k_linear_recurrent<float>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_linear_recurrent<bf16_t>, grid, dim3(256), 0, st, a);
+    klaunch(k_linear_recurrent<bf16_t>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -271,7 +271,7 @@ __global__ void k_copy_f32(float* dst, const float* src, size_t n) {
 
 hipError_t launch_copy_f32(float* dst, const float* src, size_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
+  klaunch(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
   return hipGetLastError();
 }
 

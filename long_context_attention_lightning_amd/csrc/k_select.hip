@@ -345,10 +345,10 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)a.n_rows);
-  if (a.max_len <= 256 * 16) hipLaunchKernelGGL((k_select<256, 16, true>), grid, dim3(256), 0, st, a);
-  else if (a.max_len <= 1024 * 16) hipLaunchKernelGGL((k_select<1024, 16, true>), grid, dim3(1024), 0, st, a);
-  else if (a.max_len <= 1024 * 32) hipLaunchKernelGGL((k_select<1024, 32, true>), grid, dim3(1024), 0, st, a);
-  else if (a.max_len <= 1024 * 64) hipLaunchKernelGGL((k_select<1024, 64, false>), grid, dim3(1024), 0, st, a);
+  if (a.max_len <= 256 * 16) klaunch((k_select<256, 16, true>), grid, dim3(256), 0, st, a);
+  else if (a.max_len <= 1024 * 16) klaunch((k_select<1024, 16, true>), grid, dim3(1024), 0, st, a);
+  else if (a.max_len <= 1024 * 32) klaunch((k_select<1024, 32, true>), grid, dim3(1024), 0, st, a);
+  else if (a.max_len <= 1024 * 64) klaunch((k_select<1024, 64, false>), grid, dim3(1024), 0, st, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

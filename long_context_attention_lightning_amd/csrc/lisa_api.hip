@@ -199,21 +199,30 @@ const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
     "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine"};
 
+thread_local LaunchEvents g_next_launch;
+
 bool timing_on(int kid) { return g_timing.kid == kid && g_timing.count < g_timing.n; }
 
+// A timed launch hands its event pair to the kernel's own dispatch
+// (hipExtLaunchKernel); the pair counts once the launcher has consumed it.
 #define LAUNCH(kid, st, call)                                                       \
   do {                                                                              \
     const bool timed_ = timing_on(kid);                                             \
-    if (timed_) (void)hipEventRecord(g_timing.starts[g_timing.count], (st));        \
+    if (timed_) {                                                                   \
+      next_launch_events().start = g_timing.starts[g_timing.count];                 \
+      next_launch_events().stop = g_timing.stops[g_timing.count];                   \
+    }                                                                               \
     const hipError_t e_ = (call);                                                   \
     if (timed_) {                                                                   \
-      (void)hipEventRecord(g_timing.stops[g_timing.count], (st));                   \
-      ++g_timing.count;                                                             \
+      if (!next_launch_events().start) ++g_timing.count;                            \
+      next_launch_events() = LaunchEvents();                                        \
     }                                                                               \
     if (e_ != hipSuccess) return fail_hip(e_, kKernelNames[kid]);                   \
   } while (0)
 
 }  // namespace
+
+LaunchEvents& lisa::next_launch_events() { return g_next_launch; }
 
 // ===========================================================================
 // exported entry points

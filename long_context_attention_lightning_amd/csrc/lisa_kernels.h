@@ -1,5 +1,6 @@
 // Launch interface between the C-ABI host layer and the HIP kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -9,6 +10,25 @@ struct Shape {
   int B, H_q, H_kv, d, H_I, H_Ik, d_I, H_L, hidden, M, cap, max_len, chunk, dtype;
   unsigned flags;
 };
+
+// Start/stop events for the next kernel launch of this host thread. When set,
+// the launch goes through hipExtLaunchKernel, which timestamps the kernel's
+// own dispatch (the same interval a kernel trace reports).
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& next_launch_events();
+
+template <typename F, typename... Args>
+inline void klaunch(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t st, Args... args) {
+  LaunchEvents& ev = next_launch_events();
+  if (ev.start) {
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, ev.start, ev.stop, 0, args...);
+    ev = LaunchEvents();
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, st, args...);
+  }
+}
 
 enum KernelId {
   KID_DECODE_PHASE_A = 0,
