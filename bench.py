@@ -344,7 +344,7 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     kern = {}
     call()
     torch.cuda.synchronize()
-    for kid in (4, 5, 3, 1, 6):  # one launch each per call
+    for kid in (4, 9, 10, 5, 3, 1, 6):  # one launch each per call
         st = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         sp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for e in st + sp:
@@ -376,6 +376,11 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
         "topm_select": (SELECT_OPS_PER_KEY * scored_pairs, "alu"),
     }
     proofs = {k: kernel_roofline(k, kern[k] * 1e-3, *pwork[k]) for k in pwork if kern.get(k)}
+    # the linear branch as a whole (segment sums + prefix + chunked outputs)
+    lin_us = sum(kern.get(k, 0.0) for k in ("prefill_linear_sums", "prefill_linear_prefix", "prefill_linear"))
+    lin_flops = 2 * cfg.H_L * (n * cfg.d * 64 + 2 * n * cfg.d * cfg.d)  # causal half of A, A V, phi(Q) S, phi(K)^T V
+    proofs["prefill_linear_branch"] = kernel_roofline("prefill_linear_branch", lin_us * 1e-3, lin_bytes, "hbm")
+    proofs["prefill_linear_branch_mfma"] = kernel_roofline("prefill_linear_branch", lin_us * 1e-3, lin_flops, "mfma")
     res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
            "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
            "prefill_kernel_roofline": proofs}

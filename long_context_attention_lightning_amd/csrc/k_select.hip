@@ -129,11 +129,12 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
   const int len = a.prefill ? t + 1 : a.seq_lens[b];
   const int M = a.M;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
-  int32_t* orow = a.idx + (size_t)r * a.idx_ld;
+  int32_t* orow = a.idx ? a.idx + (size_t)r * a.idx_ld : nullptr;  // null: bitmask only
   uint32_t* mrow = a.mask ? a.mask + (size_t)r * a.mask_ld : nullptr;
 
   if (len <= M) {  // the whole prefix is selected
-    for (int i = tid; i < M; i += THREADS) orow[i] = i < len ? i : -1;
+    if (orow)
+      for (int i = tid; i < M; i += THREADS) orow[i] = i < len ? i : -1;
     if (mrow) {
       const int words = (len + 31) / 32;
       for (int w = tid; w < words; w += THREADS) {
@@ -321,10 +322,11 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
   const uint32_t nsel = (uint32_t)__builtin_popcountll(selbits);
   uint32_t total;
   uint32_t o = block_incl_scan(sm, nsel, total) - nsel;
-  for (uint64_t m = selbits; m; m &= m - 1) {
-    if (o < (uint32_t)M) orow[o] = p0 + __builtin_ctzll(m);
-    ++o;
-  }
+  if (orow)
+    for (uint64_t m = selbits; m; m &= m - 1) {
+      if (o < (uint32_t)M) orow[o] = p0 + __builtin_ctzll(m);
+      ++o;
+    }
   if (mrow) {
     if constexpr (ITEMS >= 32) {
 #pragma unroll
@@ -339,7 +341,8 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
     }
   }
   const int m = M < len ? M : len;
-  for (int k = m + tid; k < M; k += THREADS) orow[k] = -1;
+  if (orow)
+    for (int k = m + tid; k < M; k += THREADS) orow[k] = -1;
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {

@@ -2,6 +2,7 @@
 // layout, launch sequencing, error state and the kernel timing hook.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -149,18 +150,22 @@ DenseWs dense_ws(const Shape& sh) {
 int64_t prefill_scores_ld(int n) { return (int64_t)align_up((size_t)n, 64); }
 
 struct PrefillWs {
-  size_t scores, idx, o_lin, gate, z_tmp, total;
+  size_t scores, idx, mask, o_lin, gate, w_t, z_tmp, seg, total;
 };
 
 PrefillWs prefill_ws(const Shape& sh, int n) {
   PrefillWs w;
   Layout L;
   const int srows = n > sh.M ? n - sh.M : 0;
+  const bool mfma_attn = attn_mfma_supported(sh);
   w.scores = L.take((size_t)sh.B * srows * prefill_scores_ld(n) * 4);
-  w.idx = L.take((size_t)sh.B * n * sh.M * 4);
+  w.idx = L.take(mfma_attn ? 0 : (size_t)sh.B * n * sh.M * 4);  // the MFMA path reads the bitmask
+  w.mask = L.take(mfma_attn ? (size_t)sh.B * n * attn_mask_ld(n) * 4 : 0);
   w.o_lin = L.take((size_t)sh.B * n * sh.H_L * sh.d * 4);
   w.gate = L.take((size_t)sh.B * n * sh.H_q * 4);
+  w.w_t = L.take(gate_mfma_supported(sh) ? gate_transpose_elems(sh) * 2 : 0);
   w.z_tmp = L.take((size_t)sh.B * sh.H_L * sh.d * 4);
+  w.seg = L.take(linear_mfma_supported(sh) ? linear_seg_floats(sh, n) * 4 : 0);
   w.total = L.off;
   return w;
 }
@@ -197,7 +202,8 @@ struct Timing {
 
 const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
-    "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine"};
+    "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine",
+    "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose"};
 
 thread_local LaunchEvents g_next_launch;
 
@@ -424,7 +430,8 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n, const i
         ia.row0 = n > sh.M ? sh.M : n; ia.stored_rows = n > sh.M ? n - sh.M : 0;
         ia.scores = at<float>(ws, w.scores); ia.ld = prefill_scores_ld(n);
       }
-      LAUNCH(KID_PREFILL_INDEX, st, launch_index_scores(ia, st));
+      LAUNCH(KID_PREFILL_INDEX, st, index_mfma_supported(sh) ? launch_index_scores_mfma(ia, st)
+                                                             : launch_index_scores(ia, st));
       sa.scores = ia.scores; sa.ld = ia.ld; sa.first_row = ia.row0; sa.stored_rows = ia.stored_rows;
     }
   }
@@ -440,6 +447,13 @@ int lisa_linear_state_update(const lisa_shape* shape, int32_t n_tokens, const vo
   if (n_tokens < 1) return fail(LISA_ERR_INVALID_ARG, "n_tokens %d", n_tokens);
   REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(S); REQUIRE_PTR(z);
   hipStream_t st = (hipStream_t)stream;
+  if (linear_mfma_supported(sh)) {
+    LinearChunkArgs lc{};
+    lc.sh = sh; lc.n = n_tokens; lc.k_lin = k_lin; lc.v_lin = v_lin; lc.S = S; lc.z = z;
+    lc.nseg = 1; lc.seg_len = (n_tokens + 63) / 64 * 64; lc.in_place = 1;
+    LAUNCH(KID_LINEAR_UPDATE, st, launch_linear_seg_sums(lc, st));
+    return LISA_OK;
+  }
   LinearArgs la{};
   la.sh = sh; la.n = n_tokens; la.q_lin = nullptr; la.k_lin = k_lin; la.v_lin = v_lin;
   la.S = S; la.z_in = z; la.z_out = z; la.o_lin = nullptr;  // without outputs only slice 0 touches z
@@ -464,32 +478,60 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
 
   GateArgs ga{};
   ga.sh = sh; ga.n_rows = sh.B * n; ga.x = x; ga.w_gate = w_gate; ga.gate_part = at<float>(ws, w.gate);
-  LAUNCH(KID_PREFILL_GATE, st, launch_gate_logits(ga, st));
+  if (gate_mfma_supported(sh)) {
+    ga.w_t = at<bf16_t>(ws, w.w_t);
+    LAUNCH(KID_PREFILL_GATE_PREP, st, launch_gate_transpose(ga, st));
+    LAUNCH(KID_PREFILL_GATE, st, launch_gate_mfma(ga, st));
+  } else {
+    LAUNCH(KID_PREFILL_GATE, st, launch_gate_logits(ga, st));
+  }
 
-  LinearArgs la{};
-  la.sh = sh; la.n = n; la.q_lin = q_lin; la.k_lin = k_lin; la.v_lin = v_lin; la.S = S;
-  la.z_in = z; la.z_out = at<float>(ws, w.z_tmp); la.o_lin = at<float>(ws, w.o_lin);
-  LAUNCH(KID_PREFILL_LINEAR, st, launch_linear_recurrent(la, st));
-  LAUNCH(KID_PREFILL_LINEAR, st, launch_copy_f32(z, la.z_out, (size_t)sh.B * sh.H_L * sh.d, st));
+  float* o_lin = at<float>(ws, w.o_lin);
+  if (linear_mfma_supported(sh)) {
+    LinearChunkArgs lc{};
+    lc.sh = sh; lc.n = n; lc.q_lin = q_lin; lc.k_lin = k_lin; lc.v_lin = v_lin; lc.S = S; lc.z = z;
+    lc.seg_state = at<float>(ws, w.seg); lc.in_place = 0; lc.o_lin = o_lin;
+    linear_segments(sh, n, lc.nseg, lc.seg_len);
+    LAUNCH(KID_PREFILL_LIN_SUMS, st, launch_linear_seg_sums(lc, st));
+    LAUNCH(KID_PREFILL_LIN_PREFIX, st, launch_linear_seg_prefix(lc, st));
+    LAUNCH(KID_PREFILL_LINEAR, st, launch_linear_chunks(lc, st));
+  } else {
+    LinearArgs la{};
+    la.sh = sh; la.n = n; la.q_lin = q_lin; la.k_lin = k_lin; la.v_lin = v_lin; la.S = S;
+    la.z_in = z; la.z_out = at<float>(ws, w.z_tmp); la.o_lin = o_lin;
+    LAUNCH(KID_PREFILL_LINEAR, st, launch_linear_recurrent(la, st));
+    LAUNCH(KID_PREFILL_LINEAR, st, launch_copy_f32(z, la.z_out, (size_t)sh.B * sh.H_L * sh.d, st));
+  }
 
   IndexScoreArgs ia{};
   ia.sh = sh; ia.n = n; ia.q_idx = q_idx; ia.k_idx = k_idx_cache; ia.w_idx = w_idx;
   ia.row0 = n > sh.M ? sh.M : n; ia.stored_rows = n > sh.M ? n - sh.M : 0;
   ia.scores = at<float>(ws, w.scores); ia.ld = prefill_scores_ld(n);
-  LAUNCH(KID_PREFILL_INDEX, st, launch_index_scores(ia, st));
+  LAUNCH(KID_PREFILL_INDEX, st, index_mfma_supported(sh) ? launch_index_scores_mfma(ia, st)
+                                                         : launch_index_scores(ia, st));
 
-  int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, w.idx);
+  const bool mfma_attn = attn_mfma_supported(sh);
+  int32_t* idx = idx_out ? idx_out : (mfma_attn ? nullptr : at<int32_t>(ws, w.idx));
   SelectArgs sa{};
   sa.n_rows = sh.B * n; sa.rows_per_seq = n; sa.prefill = 1; sa.seq_lens = nullptr;
   sa.scores = ia.scores; sa.ld = ia.ld; sa.first_row = ia.row0; sa.stored_rows = ia.stored_rows;
-  sa.M = sh.M; sa.max_len = n; sa.idx = idx; sa.idx_ld = sh.M; sa.mask = nullptr;
+  sa.M = sh.M; sa.max_len = n; sa.idx = idx; sa.idx_ld = sh.M;
+  sa.mask = mfma_attn ? at<uint32_t>(ws, w.mask) : nullptr; sa.mask_ld = attn_mask_ld(n);
   LAUNCH(KID_SELECT, st, launch_select(sa, st));
 
+  if (mfma_attn) {
+    AttnMaskArgs am{};
+    am.sh = sh; am.n = n; am.q = q; am.k_cache = k_cache; am.v_cache = v_cache; am.mask = sa.mask;
+    am.mask_ld = sa.mask_ld; am.scale_log2e = 1.4426950408889634f / sqrtf((float)sh.d);
+    am.gate_part = ga.gate_part; am.o_lin = o_lin; am.out = out;
+    LAUNCH(KID_PREFILL_ATTN, st, launch_attn_prefill_mfma(am, st));
+    return LISA_OK;
+  }
   AttnArgs aa{};
   aa.sh = sh; aa.n_rows = sh.B * n; aa.rows_per_seq = n; aa.prefill = 1; aa.dense = 0; aa.seq_lens = nullptr;
   aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = idx; aa.idx_ld = sh.M;
   aa.nsplit = 1; aa.split_len = sh.M; aa.part = nullptr;
-  aa.gate_part = ga.gate_part; aa.gate_chunks = 1; aa.o_lin = la.o_lin; aa.lin_den = nullptr; aa.out = out;
+  aa.gate_part = ga.gate_part; aa.gate_chunks = 1; aa.o_lin = o_lin; aa.lin_den = nullptr; aa.out = out;
   LAUNCH(KID_PREFILL_ATTN, st, launch_attention(aa, st));
   return LISA_OK;
 }

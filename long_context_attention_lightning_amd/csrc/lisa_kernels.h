@@ -40,7 +40,10 @@ enum KernelId {
   KID_PREFILL_ATTN = 6,
   KID_LINEAR_UPDATE = 7,
   KID_ATTN_COMBINE = 8,
-  KID_COUNT = 9
+  KID_PREFILL_LIN_SUMS = 9,
+  KID_PREFILL_LIN_PREFIX = 10,
+  KID_PREFILL_GATE_PREP = 11,
+  KID_COUNT = 12
 };
 
 // ---------------------------------------------------------------------------
@@ -80,7 +83,7 @@ struct SelectArgs {
   int stored_rows;          // stored score rows per sequence (prefill)
   int M;
   int max_len;              // longest row
-  int32_t* idx;             // [n_rows, idx_ld]
+  int32_t* idx;             // nullable [n_rows, idx_ld]
   int64_t idx_ld;
   uint32_t* mask;           // nullable [n_rows, mask_ld] selection bitmask
   int64_t mask_ld;

@@ -62,6 +62,24 @@ def test_prefill_small_bf16(n, M, B):
     _full_parity(cfg, prefill_inputs(cfg, 3, n=n, salt=n), M, f"bf16 n={n} M={M}")
 
 
+PREFILL_SHAPES = [
+    # (label, overrides, n, M): head dim 64 and a shared index key; GQA groups of 3 and 8
+    ("bf16 G3 d64 shared key", dict(H_q=6, H_kv=2, H_L=6, d=64, H_I=2, H_Ik=1, d_I=32, hidden=96), 300, 40),
+    ("bf16 G8 d128", dict(H_q=16, H_kv=2, H_L=16, H_I=2, H_Ik=2, d_I=64, hidden=160), 257, 100),
+]
+
+
+@pytest.mark.parametrize("label,over,n,M", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
+def test_prefill_bf16_shapes(label, over, n, M):
+    cfg = CONFIGS[3].replace(n=n, cap=n + 1, **over)
+    inp = prefill_inputs(cfg, 3, n=n, salt=31)
+    # start from a state carried over from an earlier part of the sequence
+    r = np.random.default_rng(17)
+    inp["S0"] = (r.standard_normal(inp["S0"].shape) * 30).astype(np.float32)
+    inp["z0"] = (np.abs(r.standard_normal(inp["z0"].shape)) * 100 + 1).astype(np.float32)
+    _full_parity(cfg, inp, M, label)
+
+
 def test_prefill_fp32_shared_key_small_heads():
     cfg = CONFIGS[0].replace(H_q=6, H_kv=2, H_L=6, H_I=2, H_Ik=1, n=300, cap=300, d=64, d_I=16)
     _full_parity(cfg, prefill_inputs(cfg, 0, n=300, salt=5), 40, "fp32 shared key")
