@@ -228,9 +228,10 @@ def main():
     ms_step, done = time_graph(g_main)
     print(f"# timed {done} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
     # ---------------- per-kernel durations (HIP events on the launch stream)
-    dec_kids = (0, 1, 2, 8)
+    dec_kids = (0, 1, 12, 2, 8)
     kt = kernel_times(step, dec_kids)
-    per_kernel_ms = {Lb.lisa_kernel_name(k): v for k, v in kt.items()}
+    dec_kids = tuple(k for k in dec_kids if kt[k] > 0)  # kernels this shape launches
+    per_kernel_ms = {Lb.lisa_kernel_name(k): kt[k] for k in dec_kids}
     dom = max(dec_kids, key=lambda k: kt[k])
     dom_ms = kt[dom]
     print(f"# kernels (us): " + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in per_kernel_ms.items()),
@@ -247,6 +248,7 @@ def main():
     tok_s = B / (ms_step * 1e-3)
     work = {0: (phase_a_bytes(cfg, Lctx, B), "hbm"),
             1: (SELECT_OPS_PER_KEY * Lctx * B, "alu"),
+            12: (attention_bytes(cfg, Lctx, M, B) + 4 * Lctx * B, "hbm"),
             2: (attention_bytes(cfg, Lctx, M, B), "hbm"),
             8: (combine_bytes(cfg, B), "hbm")}
     roofs = {Lb.lisa_kernel_name(k): kernel_roofline(Lb.lisa_kernel_name(k), kt[k], *work[k]) for k in dec_kids}

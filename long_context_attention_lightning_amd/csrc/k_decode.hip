@@ -14,8 +14,11 @@
 //   over the selected set, with an in-kernel combine by the last split block
 //   and the gate epilogue out = g*O_s + (1-g)*O_L (Section 3.2 Eq. 1, with
 //   the gate on the sparse branch).
+#include <type_traits>
+
 #include "lisa_common.h"
 #include "lisa_kernels.h"
+#include "lisa_attend.h"
 
 namespace lisa {
 
@@ -279,41 +282,18 @@ hipError_t launch_decode_phase_a(const PhaseAArgs& a, hipStream_t st) {
   return launch_pa<bf16_t, 4>(a, st);
 }
 
-// ---------------------------------------------------------------------------
-// gathered GQA attention
-// ---------------------------------------------------------------------------
-// Block = (row, KV head, split).  A "slot" of D/VEC lanes owns one gathered
-// row of K (then V) at a time; each slot keeps its own online-softmax state
-// (max, sum, accumulator) for the GT query heads of the group and loads the
-// K and V rows of AT_RP positions at once, so one round costs two dependent
-// memory trips (the index, then the rows).  Slots are merged with xor
-// shuffles inside the wave and through LDS across the four waves.
-constexpr int AT_THREADS = 256;
-constexpr int AT_RP = 4;        // positions per slot per round
-constexpr int AT_MAX_SPLITS = 32;
-
 size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit) {
   const int G = sh.H_q / sh.H_kv;
   return (size_t)n_rows * sh.H_kv * nsplit * (size_t)(G * sh.d + 2 * G);
 }
 
-__device__ __forceinline__ float scale_from(float m_old, float m_new) {
-  return m_old == -INFINITY ? 0.f : exp2f(m_old - m_new);
-}
 
 template <typename T, int D, int GT>
 __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
-  using V = Vec<T>;
-  constexpr int VEC = V::N;
-  constexpr int LG = D / VEC;            // lanes per row of one head
-  constexpr int NG = AT_THREADS / LG;    // slots
-  constexpr int NW = AT_THREADS / WAVE;
-  constexpr int ROUND = NG * AT_RP;      // positions per round
-  __shared__ float wm[NW][GT], wl[NW][GT];
-  __shared__ float wacc[NW][GT * D];
-
+  constexpr bool MF = sizeof(T) == 2;  // bf16: MFMA split attention
+  using SharedT = typename std::conditional<MF, AttnMfmaShared<D, GT>, AttnMergeShared<AT_THREADS / WAVE, GT, D>>::type;
+  __shared__ SharedT ms;
   const Shape& sh = a.sh;
-  const int G = sh.H_q / sh.H_kv;
   int blk = blockIdx.x;
   const int s = blk % a.nsplit;
   blk /= a.nsplit;
@@ -325,162 +305,10 @@ __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
   const int i0 = s * a.split_len;
   if (i0 >= m) return;  // empty split: the combine skips it
   const int i1 = min(m, i0 + a.split_len);
-
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-  const int ps = tid / LG, li = tid % LG;
-  const float scale = 1.4426950408889634f * rsqrtf((float)D);
-
-  float q[GT][VEC];
-  const T* qrow = (const T*)a.q + ((size_t)r * sh.H_q + (size_t)g * G) * D + li * VEC;
-#pragma unroll
-  for (int hh = 0; hh < GT; ++hh) {
-    V::unpack(ld16(qrow + (size_t)min(hh, G - 1) * D), q[hh]);
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) q[hh][v] *= scale;
-  }
-  float mrun[GT], lrun[GT], acc[GT][VEC];
-#pragma unroll
-  for (int hh = 0; hh < GT; ++hh) {
-    mrun[hh] = -INFINITY;
-    lrun[hh] = 0.f;
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[hh][v] = 0.f;
-  }
-  const size_t row_stride = (size_t)sh.H_kv * D;
-  const T* kb = (const T*)a.k_cache + ((size_t)b * sh.cap * sh.H_kv + g) * D + li * VEC;
-  const T* vb = (const T*)a.v_cache + ((size_t)b * sh.cap * sh.H_kv + g) * D + li * VEC;
-  const int32_t* irow = a.idx ? a.idx + (size_t)r * a.idx_ld : nullptr;
-
-  for (int c0 = i0; c0 < i1; c0 += ROUND) {
-    int pos[AT_RP];
-    bool valid[AT_RP];
-#pragma unroll
-    for (int k = 0; k < AT_RP; ++k) {
-      const int i = c0 + ps + NG * k;
-      valid[k] = i < i1;
-      const int ii = min(i, i1 - 1);
-      const int pp = a.dense ? ii : irow[ii];
-      pos[k] = min(max(pp, 0), len - 1);  // defensive: never read outside the row
-    }
-    uint4 kr[AT_RP], vr[AT_RP];
-#pragma unroll
-    for (int k = 0; k < AT_RP; ++k) {
-      kr[k] = ld16(kb + (size_t)pos[k] * row_stride);
-      vr[k] = ld16(vb + (size_t)pos[k] * row_stride);
-    }
-    float lg[AT_RP][GT];
-#pragma unroll
-    for (int k = 0; k < AT_RP; ++k) {
-      float kf[VEC];
-      V::unpack(kr[k], kf);
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh) {
-        float dot = 0.f;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) dot = fmaf(q[hh][v], kf[v], dot);
-        lg[k][hh] = group_sum(dot, LG);
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      float mx = mrun[hh];
-#pragma unroll
-      for (int k = 0; k < AT_RP; ++k)
-        if (valid[k]) mx = fmaxf(mx, lg[k][hh]);
-      const float f = scale_from(mrun[hh], mx);
-      float psum = 0.f;
-#pragma unroll
-      for (int k = 0; k < AT_RP; ++k) {
-        const float p = valid[k] ? exp2f(lg[k][hh] - mx) : 0.f;
-        lg[k][hh] = p;
-        psum += p;
-      }
-      lrun[hh] = lrun[hh] * f + psum;
-      mrun[hh] = mx;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[hh][v] *= f;
-    }
-#pragma unroll
-    for (int k = 0; k < AT_RP; ++k) {
-      float vf[VEC];
-      V::unpack(vr[k], vf);
-#pragma unroll
-      for (int hh = 0; hh < GT; ++hh)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[hh][v] = fmaf(lg[k][hh], vf[v], acc[hh][v]);
-    }
-  }
-
-  // merge the slots of the wave (xor partners hold the same dimensions)
-#pragma unroll
-  for (int off = LG; off < WAVE; off <<= 1) {
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      const float mo = __shfl_xor(mrun[hh], off, WAVE);
-      const float lo = __shfl_xor(lrun[hh], off, WAVE);
-      const float mn = fmaxf(mrun[hh], mo);
-      const float f1 = scale_from(mrun[hh], mn), f2 = scale_from(mo, mn);
-      lrun[hh] = lrun[hh] * f1 + lo * f2;
-      mrun[hh] = mn;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const float ao = __shfl_xor(acc[hh][v], off, WAVE);
-        acc[hh][v] = acc[hh][v] * f1 + ao * f2;
-      }
-    }
-  }
-  if (lane < LG) {
-#pragma unroll
-    for (int hh = 0; hh < GT; ++hh) {
-      if (lane == 0) {
-        wm[wave][hh] = mrun[hh];
-        wl[wave][hh] = lrun[hh];
-      }
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) wacc[wave][hh * D + li * VEC + v] = acc[hh][v];
-    }
-  }
-  __syncthreads();
-
-  const int GD = G * D;
-  const int PS = GD + 2 * G;
-  float* mypart = a.nsplit > 1 ? a.part + (((size_t)r * sh.H_kv + g) * a.nsplit + s) * PS : nullptr;
-  for (int e = tid; e < GD; e += AT_THREADS) {
-    const int hh = e / D, dim = e % D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, wm[w][hh]);
-    float l = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = scale_from(wm[w][hh], mx);
-      l = fmaf(wl[w][hh], f, l);
-      o = fmaf(wacc[w][e], f, o);
-    }
-    if (mypart) {
-      // split partial: unnormalised accumulator, max and sum; the combine
-      // kernel merges the splits (the kernel boundary orders the writes
-      // before its reads, with no device-scope fence here)
-      mypart[e] = o;
-      if (dim == 0) {
-        mypart[GD + hh] = mx;
-        mypart[GD + G + hh] = l;
-      }
-      continue;
-    }
-    o = o / l;
-    const int h = g * G + hh;
-    const size_t oi = ((size_t)r * sh.H_q + h) * D + dim;
-    if (a.gate_part) {
-      float gl = 0.f;
-      for (int c = 0; c < a.gate_chunks; ++c) gl += a.gate_part[((size_t)r * a.gate_chunks + c) * sh.H_q + h];
-      const float gv = sigmoidf(gl);
-      float ol = a.o_lin[oi];
-      if (a.lin_den) ol = ol / a.lin_den[(size_t)r * sh.H_q + h];
-      o = gv * o + (1.f - gv) * ol;
-    }
-    st1<T>((T*)a.out + oi, o);
-  }
+  const int32_t* irow = a.dense ? nullptr : a.idx + (size_t)r * a.idx_ld;
+  auto pos_of = [irow](int i) { return irow ? irow[i] : i; };
+  if constexpr (MF) attend_split_mfma<D, GT, AT_THREADS>(a, r, g, s, len, i0, i1, pos_of, ms);
+  else attend_split<T, D, GT, AT_THREADS, AT_RP>(a, r, g, s, len, i0, i1, pos_of, ms);
 }
 
 // Merge the split partials of one (row, query head) and apply the epilogue.

@@ -203,7 +203,7 @@ struct Timing {
 const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
     "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine",
-    "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose"};
+    "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose", "select_attention"};
 
 thread_local LaunchEvents g_next_launch;
 
@@ -327,12 +327,12 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   pa.append = 1; pa.do_scores = 1; pa.do_linear = 1; pa.do_gate = 1; pa.linear_output = 1;
   LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
 
-  int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, w.idx);
+  const bool fused = select_attend_supported(sh, w.nsplit, w.split_len);
+  int32_t* idx = idx_out ? idx_out : (fused ? nullptr : at<int32_t>(ws, w.idx));
   SelectArgs sa{};
   sa.n_rows = sh.B; sa.rows_per_seq = 1; sa.prefill = 0; sa.seq_lens = seq_lens;
   sa.scores = pa.scores; sa.ld = pa.scores_ld; sa.first_row = 0; sa.stored_rows = 1;
   sa.M = sh.M; sa.max_len = sh.max_len; sa.idx = idx; sa.idx_ld = sh.M; sa.mask = nullptr;
-  LAUNCH(KID_SELECT, st, launch_select(sa, st));
 
   AttnArgs aa{};
   aa.sh = sh; aa.n_rows = sh.B; aa.rows_per_seq = 1; aa.prefill = 0; aa.dense = 0; aa.seq_lens = seq_lens;
@@ -340,7 +340,12 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   aa.nsplit = w.nsplit; aa.split_len = w.split_len; aa.part = at<float>(ws, w.part);
   aa.gate_part = pa.gate_part; aa.gate_chunks = pa.gate_chunks;
   aa.o_lin = pa.o_lin; aa.lin_den = (sh.flags & LISA_LINEAR_UNNORMALIZED) ? nullptr : pa.lin_den; aa.out = out;
-  LAUNCH(KID_ATTN, st, launch_attention(aa, st));
+  if (fused) {
+    LAUNCH(KID_SELECT_ATTN, st, launch_select_attend(aa, sa, st));
+  } else {
+    LAUNCH(KID_SELECT, st, launch_select(sa, st));
+    LAUNCH(KID_ATTN, st, launch_attention(aa, st));
+  }
   LAUNCH(KID_ATTN_COMBINE, st, launch_attention_combine(aa, st));
   return LISA_OK;
 }

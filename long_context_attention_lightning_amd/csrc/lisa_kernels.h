@@ -43,7 +43,8 @@ enum KernelId {
   KID_PREFILL_LIN_SUMS = 9,
   KID_PREFILL_LIN_PREFIX = 10,
   KID_PREFILL_GATE_PREP = 11,
-  KID_COUNT = 12
+  KID_SELECT_ATTN = 12,
+  KID_COUNT = 13
 };
 
 // ---------------------------------------------------------------------------
@@ -115,6 +116,11 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);          // split kernel
 hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t st);  // merge (nsplit > 1)
 size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit);
+
+// Decode with few sequences: selection and split attention in one launch
+// (every split block selects the whole row; split partials as above).
+bool select_attend_supported(const Shape& sh, int nsplit, int split_len);
+hipError_t launch_select_attend(const AttnArgs& a, const SelectArgs& sa, hipStream_t st);
 
 
 }  // namespace lisa
