@@ -23,7 +23,7 @@
 namespace lisa {
 
 constexpr int PA_THREADS = 256;
-constexpr int IDX_ROWS_IN_FLIGHT = 8;  // index-key rows each lane loads at once
+constexpr int IDX_ROWS_IN_FLIGHT = 4;  // index-key rows each lane loads at once
 constexpr int LIN_COLS = 32;     // columns of S per linear block
 constexpr int GATE_ROWS = 64;    // hidden rows per gate block
 

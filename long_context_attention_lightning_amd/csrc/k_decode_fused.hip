@@ -46,6 +46,9 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, Select
   blk /= a.nsplit;
   const int g = blk % sh.H_kv;
   const int b = blk / sh.H_kv;  // decode: one row per sequence
+  // the score row is read up to max_len while the sequence length loads
+  RunLoad<ITEMS> ld;
+  run_load<FS_THREADS, ITEMS>(sa.scores + (size_t)b * sa.ld, sa.max_len, ld);
   const int len = a.seq_lens[b];
   const int M = sh.M;
   const int m = min(M, len);
@@ -54,10 +57,13 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, Select
   if (i0 >= m && !want_idx) return;  // empty split: the combine skips it
   const int i1 = min(m, i0 + a.split_len);
 
+  // thread-contiguous runs: their compaction is one scan, which is what a
+  // latency-bound single row wants
   uint64_t selbits;
   uint32_t o;
   int p0;
-  select_row<FS_THREADS, ITEMS, true>(sa.scores + (size_t)b * sa.ld, len, M, u.sel.sm, u.sel.ks, selbits, o, p0);
+  select_row_runs<FS_THREADS, ITEMS, true>(sa.scores + (size_t)b * sa.ld, len, M, u.sel.sm, u.sel.ks, ld, selbits, o,
+                                           p0);
 
   if (want_idx) {  // the index list, written once per sequence
     int32_t* orow = sa.idx + (size_t)b * sa.idx_ld;

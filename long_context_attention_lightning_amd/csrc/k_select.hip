@@ -33,33 +33,37 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
   __shared__ KeyStore<THREADS, ITEMS, LKEYS> ks;
   const int r = blockIdx.x;
   const int b = r / a.rows_per_seq, t = r % a.rows_per_seq;
-  const int len = a.prefill ? t + 1 : a.seq_lens[b];
   const int M = a.M;
   const int tid = threadIdx.x;
   int32_t* orow = a.idx ? a.idx + (size_t)r * a.idx_ld : nullptr;  // null: bitmask only
   uint32_t* mrow = a.mask ? a.mask + (size_t)r * a.mask_ld : nullptr;
-  // rows of at most M positions have no stored scores (and are not read)
+  // Decode rows always exist and are read up to max_len while the length is
+  // still on its way; prefill rows of at most M positions are not stored
+  // (and not read).
+  SelLoad<THREADS, ITEMS> ld;
+  int len;
+  if (a.prefill) {
+    len = t + 1;
+    if (len > M) select_load<THREADS, ITEMS>(a.scores + ((size_t)b * a.stored_rows + (t - a.first_row)) * a.ld, len, ld);
+  } else {
+    select_load<THREADS, ITEMS>(a.scores + (size_t)b * a.ld, a.max_len, ld);
+    len = a.seq_lens[b];
+  }
   const float* srow = a.scores + ((size_t)b * a.stored_rows + (a.prefill ? max(t - a.first_row, 0) : 0)) * a.ld;
-  uint64_t selbits;
-  uint32_t o;
-  int p0;
-  select_row<THREADS, ITEMS, LKEYS>(srow, len, M, sm, ks, selbits, o, p0);
-  if (orow)
-    for (uint64_t m = selbits; m; m &= m - 1) {
-      if (o < (uint32_t)M) orow[o] = p0 + __builtin_ctzll(m);
-      ++o;
-    }
+  SelResult<ITEMS> res;
+  select_row<THREADS, ITEMS, LKEYS>(srow, len, M, sm, ks, ld, res);
+  if (orow) for_each_selected<THREADS, ITEMS>(res, [&](uint32_t rank, int pos) { if (rank < (uint32_t)M) orow[rank] = pos; });
   if (mrow) {
-    if constexpr (ITEMS >= 32) {
+    // eight consecutive lanes hold the 32 positions of one mask word
+    const int lane = tid & (WAVE - 1);
 #pragma unroll
-      for (int w = 0; w < ITEMS / 32; ++w)
-        if (p0 + 32 * w < len) mrow[(p0 >> 5) + w] = (uint32_t)(selbits >> (32 * w));
-    } else {
-      // 32 / ITEMS threads share a word: OR their shifted bits together
-      constexpr int TPW = 32 / ITEMS;
-      uint32_t word = (uint32_t)selbits << ((tid % TPW) * ITEMS);
-      for (int off = 1; off < TPW; off <<= 1) word |= (uint32_t)__shfl_xor((int)word, off, WAVE);
-      if (tid % TPW == 0 && p0 < len) mrow[p0 >> 5] = word;
+    for (int k = 0; k < ITEMS / 4; ++k) {
+      const int f = sel_group<THREADS>(k);
+      uint32_t word = (uint32_t)((res.bits >> (4 * k)) & 0xfull) << (4 * (lane & 7));
+      word |= (uint32_t)__shfl_xor((int)word, 1, WAVE);
+      word |= (uint32_t)__shfl_xor((int)word, 2, WAVE);
+      word |= (uint32_t)__shfl_xor((int)word, 4, WAVE);
+      if ((lane & 7) == 0 && 4 * f < len) mrow[f >> 3] = word;
     }
   }
   const int m = M < len ? M : len;
