@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-dense", action="store_true", help="skip the dense-attention decode baseline")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
     p.add_argument("--prefill-iters", type=int, default=5)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -137,6 +139,9 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if args.prefill_only:
+        print(json.dumps(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs)), flush=True)
+        return
     inp = decode_inputs(cfg, cid)
 
     def up(a, dt=T):

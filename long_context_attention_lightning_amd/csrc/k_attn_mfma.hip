@@ -26,14 +26,23 @@
 namespace lisa {
 
 constexpr int AK = 64;    // keys per tile
-constexpr int AP = 4;     // query tiles of 16 per wave
+constexpr int AP = 2;     // query tiles of 16 per wave
 constexpr int AQ = 16 * AP;
 
 template <int D>
 struct AttnShared {
-  bf16_t k[AK][D + 8];
-  bf16_t vt[D][AK + 8];
+  bf16_t k[AK][D + 16];
+  bf16_t vt[D + 16][AK + 8];  // rows D .. D + 15 hold ones: P V also yields the row sums
 };
+
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even, one instruction on gfx950).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 
 template <int D>
 struct AttnRegs {
@@ -44,13 +53,14 @@ struct AttnRegs {
 };
 
 template <int D>
-__device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& sm) {
+__device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& sm, bool with_v) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
 #pragma unroll
   for (int m = 0; m < AttnRegs<D>::NK; ++m) {
     const int e = tid + 256 * m;
     *reinterpret_cast<uint4*>(&sm.k[e / (D / 8)][8 * (e % (D / 8))]) = r.k[m];
   }
+  if (!with_v) return;
 #pragma unroll
   for (int m = 0; m < AttnRegs<D>::NV; ++m) {
     const int tau = lane & 31, c8 = 2 * (wave + 4 * m) + (lane >> 5);
@@ -65,7 +75,7 @@ __device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& 
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_prefill_mfma(AttnMaskArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) {  // two blocks per CU
   __shared__ AttnShared<D> sm;
   const Shape& sh = a.sh;
   const int G = sh.H_q / sh.H_kv;
@@ -81,7 +91,7 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(AttnMaskArgs a) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int r16 = lane & 15, g = lane >> 4;
   const int hl = 4 * hg + wave;             // head inside the KV group
-  const bool active = hl < G;               // idle waves still stage tiles
+  const bool active = hl < G;  // idle waves compute a duplicate head on their own SIMD and store nothing
   const int h = kvh * G + min(hl, G - 1);
   const int T0 = pb * AQ;
   const int n = a.n;
@@ -93,25 +103,6 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(AttnMaskArgs a) {
   const bf16_t* qb = (const bf16_t*)a.q + (size_t)b * n * q_stride + (size_t)h * D;
   const uint32_t* mrow0 = a.mask + (size_t)b * n * a.mask_ld;
 
-  // Q^T operands: lane holds Q[t = T0 + 16 i + r16][32 s + 8 g .. + 7]
-  bf16x8 qf[AP][D / 32];
-#pragma unroll
-  for (int i = 0; i < AP; ++i) {
-    const int t = min(T0 + 16 * i + r16, n - 1);
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[i][s] = as_bf16x8(ld16(qb + (size_t)t * q_stride + 32 * s + 8 * g));
-  }
-  f32x4 o[AP][D / 16];
-#pragma unroll
-  for (int i = 0; i < AP; ++i)
-#pragma unroll
-    for (int q = 0; q < D / 16; ++q) o[i][q] = zero4();
-  float mrun[AP], lrun[AP];
-#pragma unroll
-  for (int i = 0; i < AP; ++i) {
-    mrun[i] = -INFINITY;
-    lrun[i] = 0.f;
-  }
   const float scale = a.scale_log2e;
   const int tmax = min(T0 + AQ, n) - 1;
   const int nkt = tmax / AK + 1;
@@ -121,133 +112,215 @@ __global__ __launch_bounds__(256) void k_attn_prefill_mfma(AttnMaskArgs a) {
   // rows past n read row n-1 (its results are never stored)
   const int mrow_clamp = n - 1 - T0;
 
-  // next tile's K, V and mask words, held in registers while this one runs
+  // next tile's K (and V in the second pass) and mask words, held in
+  // registers while the current tile runs
   AttnRegs<D> rg;
-  auto prefetch = [&](int J0) {
-    const int tid_ = threadIdx.x, lane_ = tid_ & (WAVE - 1), wave_ = tid_ / WAVE;
+  auto prefetch = [&](int J0, bool with_v) {
 #pragma unroll
     for (int m = 0; m < AttnRegs<D>::NK; ++m) {
-      const int e = tid_ + 256 * m;
+      const int e = tid + 256 * m;
       const int tok = e / (D / 8), c8 = e % (D / 8);
       rg.k[m] = ld16(kb + (size_t)min(J0 + tok, n - 1) * kv_stride + 8 * c8);
     }
+    if (with_v) {
 #pragma unroll
-    for (int m = 0; m < AttnRegs<D>::NV; ++m) {
-      const int tau = lane_ & 31, c8 = 2 * (wave_ + 4 * m) + (lane_ >> 5);
+      for (int m = 0; m < AttnRegs<D>::NV; ++m) {
+        const int tau = lane & 31, c8 = 2 * (wave + 4 * m) + (lane >> 5);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        rg.v[2 * m + u] = ld16(vb + (size_t)min(J0 + 2 * tau + u, n - 1) * kv_stride + 8 * c8);
+        for (int u = 0; u < 2; ++u)
+          rg.v[2 * m + u] = ld16(vb + (size_t)min(J0 + 2 * tau + u, n - 1) * kv_stride + 8 * c8);
+      }
     }
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
-      const int rr = min(16 * i + (lane_ & 15), mrow_clamp);
+      const int rr = min(16 * i + r16, mrow_clamp);
       rg.mw[i] = *reinterpret_cast<const uint2*>(mq + (size_t)rr * a.mask_ld + J0 / 32);
     }
   };
+  // S^T of query tile i against the staged keys: sv[c][r] = q . k for the
+  // query T0 + 16 i + r16 and the key J0 + 16 c + 4 g + r, or -inf where the
+  // key is not selected (or, on tiles that reach past the block's first
+  // query, not causal)
+  // Q^T operands, held for the whole block: lane holds Q[T0 + 16 i + r16][32 s + 8 g .. + 7]
+  bf16x8 qreg[AP][D / 32];
+#pragma unroll
+  for (int i = 0; i < AP; ++i) {
+    const int t = min(T0 + 16 * i + r16, n - 1);
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qreg[i][s] = as_bf16x8(ld16(qb + (size_t)t * q_stride + 32 * s + 8 * g));
+  }
+  // S^T of query tile i against the staged keys: st[c][r] = q . k for the
+  // query T0 + 16 i + r16 and the key J0 + 16 c + 4 g + r; sel[c] holds the
+  // selection bits of those keys (bit r), cut to the causal ones on tiles
+  // that reach past the block's first query
+  auto scores = [&](int i, int J0, uint2 mw, f32x4 (&st)[4], uint32_t (&sel)[4]) {
+    const bf16x8 (&qf)[D / 32] = qreg[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      st[c] = zero4();
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)  // K operand: key 16 c + r16, dims 32 s + 8 g .. + 7
+        st[c] = mfma16(as_bf16x8(lds_read16(&sm.k[16 * c + r16][32 * s + 8 * g])), qf[s], st[c]);
+    }
+    uint32_t wx = mw.x, wy = mw.y;
+    if (J0 + AK - 1 > T0) {
+      const int lim = T0 + 16 * i + r16 - J0;  // last key of the row inside the tile
+      wx &= lim >= 31 ? ~0u : (lim < 0 ? 0u : ((2u << lim) - 1u));
+      wy &= lim >= 63 ? ~0u : (lim < 32 ? 0u : ((2u << (lim - 32)) - 1u));
+    }
+    sel[0] = wx >> (4 * g);
+    sel[1] = wx >> (16 + 4 * g);
+    sel[2] = wy >> (4 * g);
+    sel[3] = wy >> (16 + 4 * g);
+  };
+  // all-ones where bit r of w is set, else zero
+  auto bitmask = [](uint32_t w, int r) -> uint32_t { return (uint32_t)__builtin_amdgcn_sbfe((int)w, r, 1); };
 
-  prefetch(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int J0 = kt * AK;
-    uint2 mw[AP];
-#pragma unroll
-    for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
-    __syncthreads();  // readers of the previous tile are done
-    attn_stage<D>(rg, sm);
-    __syncthreads();
-    if (kt + 1 < nkt) prefetch(J0 + AK);
-    if (!active) continue;
+  // the ones rows of the V tile (written once; staging never touches them)
+  for (int e = tid; e < 16 * (AK + 8); e += 256) sm.vt[D + e / (AK + 8)][e % (AK + 8)] = (bf16_t)0x3f80;
+  constexpr int NQ = D / 16 + 1;  // output column blocks, the last one accumulates the row sums
 
-    // K operands of the tile: key 16 c + r16, dims 32 s + 8 g .. + 7
-    bf16x8 kf[4][D / 32];
+  // Every row accumulates O = sum_k p_k v_k and l = sum_k p_k with
+  // p_k = exp2(s_k scale - moff) for one fixed offset per row, so the
+  // accumulators are never rescaled.  First attempt: the offset is the
+  // row's max over the whole first key tile (unmasked; any finite offset
+  // gives the same softmax in exact arithmetic).  The attempt is kept when l
+  // lies in [2^-60, inf) and O is finite for every row of the block, which
+  // bounds both underflow of the leading terms and overflow; otherwise the
+  // block recomputes with the exact max over the selected keys (a pass over
+  // the key tiles without V), for which every p <= 1.
+  f32x4 o[AP][NQ];
+  float moff[AP];
+  // O += P V over all key tiles with the offsets in moff; with set_offset the
+  // offsets are first taken from the first tile
+  auto accumulate = [&](bool set_offset) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < AP; ++i)
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) kf[c][s] = as_bf16x8(lds_read16(&sm.k[16 * c + r16][32 * s + 8 * g]));
-
-    uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
+      for (int q = 0; q < NQ; ++q) o[i][q] = zero4();
+    prefetch(0, true);
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int J0 = kt * AK;
+      uint2 mw[AP];
 #pragma unroll
-    for (int i = 0; i < AP; ++i) {
-      const int t = T0 + 16 * i + r16;
-      f32x4 st[4];
+      for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
+      __syncthreads();
+      attn_stage<D>(rg, sm, true);
+      __syncthreads();
+      if (kt + 1 < nkt) prefetch(J0 + AK, true);
+      uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        st[c] = zero4();
+      for (int i = 0; i < AP; ++i) {
+        f32x4 st[4];
+        uint32_t sel[4];
+        scores(i, J0, mw[i], st, sel);
+        if (set_offset && kt == 0) {  // the row's offset: max over the first tile
+          float m = -INFINITY;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) st[c] = mfma16(kf[c][s], qf[i][s], st[c]);
-      }
-      // lane holds s[t][J0 + 16 c + 4 g + r]
-      float mt = -INFINITY;
-      float sv[4][4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t word = (c < 2) ? mw[i].x : mw[i].y;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kk = 16 * c + 4 * g + r;
-          const bool on = ((word >> ((kk & 31))) & 1u) && (J0 + kk <= t);
-          sv[c][r] = on ? st[c][r] * scale : -INFINITY;
-          mt = fmaxf(mt, sv[c][r]);
+          for (int c = 0; c < 4; ++c) m = fmaxf(m, fmaxf(fmaxf(st[c][0], st[c][1]), fmaxf(st[c][2], st[c][3])));
+          m = fmaxf(m, __shfl_xor(m, 16, WAVE));
+          m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+          moff[i] = m * scale;
         }
+        // every score is exponentiated; unselected ones (which may be far
+        // above the offset and even overflow) are cleared in the packed bf16
+        uint32_t pk[4][2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            const uint32_t keep = (bitmask(sel[c], r) & 0x0000ffffu) | (bitmask(sel[c], r + 1) & 0xffff0000u);
+            pk[c][r / 2] = keep & cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(st[c][r], scale, -moff[i])),
+                                              __builtin_amdgcn_exp2f(fmaf(st[c][r + 1], scale, -moff[i])));
+          }
+        // contraction step s covers key blocks 2 s and 2 s + 1
+#pragma unroll
+        for (int s = 0; s < 2; ++s) pf[i][s] = make_uint4(pk[2 * s][0], pk[2 * s][1], pk[2 * s + 1][0], pk[2 * s + 1][1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, WAVE));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, WAVE));
-      const float mnew = fmaxf(mrun[i], mt);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(mrun[i] - muse);
-      mrun[i] = mnew;
-      float lsum = 0.f;
-      uint32_t pb16[4][4];
+      // O += P V over the output blocks and the ones block: V operand of block
+      // q, step s: keys {32 s + 4 g .. +3, 32 s + 16 + 4 g .. +3}
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int q = 0; q < NQ; ++q)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pb16[c][r] = f2bf(exp2f(sv[c][r] - muse));
-          lsum += bf2f(pb16[c][r]);
+        for (int s = 0; s < 2; ++s) {
+          const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.vt[16 * q + r16][32 * s + 4 * g]);
+          const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.vt[16 * q + r16][32 * s + 16 + 4 * g]);
+          const bf16x8 vf = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
+#pragma unroll
+          for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf, o[i][q]);
         }
-      lrun[i] = lrun[i] * alpha + lsum;
-      // contraction step s covers key blocks 2 s and 2 s + 1
+    }
+  };
+
+  accumulate(true);
+  // keep the result unless some row of the block is out of range
+  bool bad = false;
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        pf[i][s] = make_uint4(pb16[2 * s][0] | (pb16[2 * s][1] << 16), pb16[2 * s][2] | (pb16[2 * s][3] << 16),
-                              pb16[2 * s + 1][0] | (pb16[2 * s + 1][1] << 16),
-                              pb16[2 * s + 1][2] | (pb16[2 * s + 1][3] << 16));
-      // rescale O rows 4 g + r by the alpha of their query (held by lane 4 g + r)
+  for (int i = 0; i < AP; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * g + r, WAVE);
+    for (int r = 0; r < 4; ++r) {
+      const float l = o[i][NQ - 1][r];
+      bad |= !(l >= 0x1p-60f && l < INFINITY);
 #pragma unroll
-        for (int q = 0; q < D / 16; ++q) o[i][q][r] *= ar;
+      for (int q = 0; q < NQ - 1; ++q) bad |= !(fabsf(o[i][q][r]) < INFINITY);
+    }
+  if (__syncthreads_or(bad)) {
+    // exact maxima over the selected keys (a pass without V), then again
+    float mx[AP];
+#pragma unroll
+    for (int i = 0; i < AP; ++i) mx[i] = -INFINITY;
+    prefetch(0, false);
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int J0 = kt * AK;
+      uint2 mw[AP];
+#pragma unroll
+      for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
+      __syncthreads();  // readers of the previous tile are done
+      attn_stage<D>(rg, sm, false);
+      __syncthreads();
+      if (kt + 1 < nkt) prefetch(J0 + AK, false);
+#pragma unroll
+      for (int i = 0; i < AP; ++i) {
+        f32x4 st[4];
+        uint32_t sel[4];
+        scores(i, J0, mw[i], st, sel);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {  // the score where selected, -inf elsewhere
+            const uint32_t m = bitmask(sel[c], r);
+            v[r] = __uint_as_float((__float_as_uint(st[c][r]) & m) | (0xff800000u & ~m));
+          }
+          mx[i] = fmaxf(mx[i], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // O += P V: V operand of dv block q, step s: keys {32 s + 4 g .. +3, 32 s + 16 + 4 g .. +3}
 #pragma unroll
-    for (int q = 0; q < D / 16; ++q)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.vt[16 * q + r16][32 * s + 4 * g]);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.vt[16 * q + r16][32 * s + 16 + 4 * g]);
-        const bf16x8 vf = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
-#pragma unroll
-        for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf, o[i][q]);
-      }
+    for (int i = 0; i < AP; ++i) {
+      float m = fmaxf(mx[i], __shfl_xor(mx[i], 16, WAVE));
+      m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+      moff[i] = m == -INFINITY ? 0.f : m * scale;
+    }
+    __syncthreads();
+    accumulate(false);
   }
   if (!active) return;
 
-  // epilogue: out = g O_s + (1 - g) O_L for rows t = T0 + 16 i + 4 g + r
+  // epilogue: out = g O_s + (1 - g) O_L for rows t = T0 + 16 i + 4 g + r;
+  // the row sum of a row is in its ones block
   const float* gate = a.gate_part;
   const float* olin = a.o_lin;
   bf16_t* out = (bf16_t*)a.out;
 #pragma unroll
   for (int i = 0; i < AP; ++i) {
-    float lt = lrun[i];
-    lt += __shfl_xor(lt, 16, WAVE);
-    lt += __shfl_xor(lt, 32, WAVE);
-    const float inv = 1.f / lt;  // every causal row selects at least itself
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float ir = __shfl(inv, 4 * g + r, WAVE);
       const int t = T0 + 16 * i + 4 * g + r;
       if (t >= n) continue;
+      const float ir = 1.f / o[i][NQ - 1][r];  // every causal row selects at least itself
       const size_t row = (size_t)b * n + t;
       const float gv = sigmoidf(gate[row * sh.H_q + h]);
       const float* ol = olin + (row * sh.H_q + h) * D;

@@ -80,6 +80,29 @@ def test_prefill_bf16_shapes(label, over, n, M):
     _full_parity(cfg, inp, M, label)
 
 
+def test_prefill_bf16_offset_fallback():
+    """Rows whose selected keys all score far below the first key tile: a
+    softmax offset taken from the first tile leaves every selected
+    probability below 2^-126, so the attention must recompute with the exact
+    maximum over the selected keys, and still match."""
+    cfg = CONFIGS[3].replace(n=300, cap=300)
+    n, M = 300, 64
+    inp = prefill_inputs(cfg, 3, n=n, salt=41)
+    from lisa_inputs import round_bf16
+    u = np.ones(cfg.d) / np.sqrt(cfg.d)
+    q = inp["q"].astype(np.float64) + 10.0 * u          # every query shares a direction
+    k = inp["k"].astype(np.float64)
+    k[:, :64] = 150.0 * u                                # the first tile scores about 1500: from an offset
+    kidx = inp["k_idx"].copy()
+    # there, every selected probability underflows to zero (l = 0), so only
+    # the exact-maximum recomputation gives finite outputs
+    kidx[:, :64] = 0.0                                   # the first tile is never selected past row M
+    inp["q"], inp["k"], inp["k_idx"] = round_bf16(q.astype(np.float32)), round_bf16(k.astype(np.float32)), kidx
+    ref = oracle.prefill(inp, M)
+    assert all(np.all(np.asarray(ref["idx"][0][t]) >= 64) for t in range(128, n))  # construction holds
+    _full_parity(cfg, inp, M, "offset fallback")
+
+
 def test_prefill_fp32_shared_key_small_heads():
     cfg = CONFIGS[0].replace(H_q=6, H_kv=2, H_L=6, H_I=2, H_Ik=1, n=300, cap=300, d=64, d_I=16)
     _full_parity(cfg, prefill_inputs(cfg, 0, n=300, salt=5), 40, "fp32 shared key")
