@@ -6,7 +6,7 @@
 //    MFMA contraction over d_I; ReLU and w_h are applied to the fp32 result.
 //    Tiles are computed transposed (keys along the accumulator rows) so that
 //    each lane holds four consecutive keys of one query row and stores them
-//    as one float4.
+//    as one float4.  Query and key rows are staged in LDS per head.
 //  * gate logits (Section 3.3 Eq. 5): x[row] . W_g[:, h] as one GEMM over
 //    the hidden dimension; the sigmoid is applied where the gate is used.
 #include "lisa_common.h"
@@ -17,67 +17,99 @@
 namespace lisa {
 
 // ---------------------------------------------------------------------------
-// index scores: block = 64 query rows x 128 keys, wave = 32 rows x 64 keys
-// (2 x 4 tiles of 16 x 16), operands read straight from global memory.
+// index scores: block = 128 query rows x 128 keys, wave = 64 x 64 (4 x 4
+// tiles of 16 x 16).  Per indexer head the block stages the head's query and
+// key rows in LDS (the next head's rows are loaded into registers meanwhile),
+// and every wave reads its MFMA operands from there.
 // ---------------------------------------------------------------------------
-constexpr int IX_ROWS = 64, IX_COLS = 128;
+constexpr int IX_T = 128;          // query rows and keys per block
+constexpr int IX_PAD = 8;
 
+template <int DI>
+struct IndexShared {
+  bf16_t q[IX_T][DI + IX_PAD];
+  bf16_t k[IX_T][DI + IX_PAD];
+};
+
+template <int DI>
 __global__ __launch_bounds__(256) void k_index_scores_mfma(IndexScoreArgs a) {
+  __shared__ IndexShared<DI> sm;
   const Shape& sh = a.sh;
   const int b = blockIdx.z;
-  const int T0 = IX_ROWS * blockIdx.y, J0 = IX_COLS * blockIdx.x;
-  if (J0 > T0 + IX_ROWS - 1 || T0 + IX_ROWS <= a.row0) return;  // above the diagonal / not stored
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int T0 = IX_T * blockIdx.y, J0 = IX_T * blockIdx.x;
+  if (J0 > T0 + IX_T - 1 || T0 + IX_T <= a.row0) return;  // above the diagonal / not stored
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int r16 = lane & 15, g = lane >> 4;
-  const int tw = T0 + 32 * (wave >> 1), jw = J0 + 64 * (wave & 1);
-  if (jw > tw + 31) return;  // the wave's tiles are all above the diagonal
-  const int dI = sh.d_I, R = sh.H_I / sh.H_Ik;
-  const bf16_t* qb = (const bf16_t*)a.q_idx + (size_t)b * a.n * sh.H_I * dI;
-  const bf16_t* kb = (const bf16_t*)a.k_idx + (size_t)b * sh.cap * sh.H_Ik * dI;
+  const int tw = T0 + 64 * (wave >> 1), jw = J0 + 64 * (wave & 1);
+  const bool live = jw <= tw + 63;  // some key of the wave's tiles is causal for some row
+  const int R = sh.H_I / sh.H_Ik;
+  const bf16_t* qb = (const bf16_t*)a.q_idx + (size_t)b * a.n * sh.H_I * DI;
+  const bf16_t* kb = (const bf16_t*)a.k_idx + (size_t)b * sh.cap * sh.H_Ik * DI;
 
-  // operand rows of this lane (clamped inside the sequence; results for
-  // rows or keys past n are never stored)
-  int tq[2], jk[4];
+  // staging: the block's 128 rows of one head, DI / 8 vectors of 16 B each
+  constexpr int NV = IX_T * DI / 8 / 256;
+  uint4 rq[NV], rk[NV];
+  auto fetch = [&](int h) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) tq[i] = min(tw + 16 * i + r16, a.n - 1);
+    for (int m = 0; m < NV; ++m) {
+      const int e = tid + 256 * m;
+      const int row = e / (DI / 8), c8 = e % (DI / 8);
+      rq[m] = ld16(qb + ((size_t)min(T0 + row, a.n - 1) * sh.H_I + h) * DI + 8 * c8);
+      rk[m] = ld16(kb + ((size_t)min(J0 + row, a.n - 1) * sh.H_Ik + h / R) * DI + 8 * c8);
+    }
+  };
+  auto stage = [&]() {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) jk[c] = min(jw + 16 * c + r16, a.n - 1);
+    for (int m = 0; m < NV; ++m) {
+      const int e = tid + 256 * m;
+      const int row = e / (DI / 8), c8 = e % (DI / 8);
+      *reinterpret_cast<uint4*>(&sm.q[row][8 * c8]) = rq[m];
+      *reinterpret_cast<uint4*>(&sm.k[row][8 * c8]) = rk[m];
+    }
+  };
 
-  f32x4 sc[2][4];
+  f32x4 sc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int c = 0; c < 4; ++c) sc[i][c] = zero4();
-
+  const int qr0 = 64 * (wave >> 1), kr0 = 64 * (wave & 1);  // the wave's rows in the staged tiles
+  fetch(0);
   for (int h = 0; h < sh.H_I; ++h) {
-    const int kh = h / R;
+    __syncthreads();  // readers of the previous head are done
+    stage();
+    __syncthreads();
+    if (h + 1 < sh.H_I) fetch(h + 1);
+    if (!live) continue;
     const float w = a.w_idx[h];
-    f32x4 acc[2][4];
+    f32x4 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[i][c] = zero4();
-    for (int k0 = 0; k0 < dI; k0 += 32) {
-      bf16x8 qf[2], kf[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) qf[i] = as_bf16x8(ld16(qb + ((size_t)tq[i] * sh.H_I + h) * dI + k0 + 8 * g));
+    for (int k0 = 0; k0 < DI; k0 += 32) {
+      bf16x8 qf[4], kf[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(ld16(kb + ((size_t)jk[c] * sh.H_Ik + kh) * dI + k0 + 8 * g));
+      for (int i = 0; i < 4; ++i) qf[i] = as_bf16x8(lds_read16(&sm.q[qr0 + 16 * i + r16][k0 + 8 * g]));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int c = 0; c < 4; ++c) kf[c] = as_bf16x8(lds_read16(&sm.k[kr0 + 16 * c + r16][k0 + 8 * g]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[i][c] = mfma16(kf[c], qf[i], acc[i][c]);  // [key][query]
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[i][c][r] = fmaf(w, fmaxf(acc[i][c][r], 0.f), sc[i][c][r]);
   }
+  if (!live) return;
   // lane holds s[t = tw + 16 i + r16][j = jw + 16 c + 4 g + r]; keys past t are written as 0
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int t = tw + 16 * i + r16;
     if (t < a.row0 || t >= a.n) continue;
     float* orow = a.scores + ((size_t)b * a.stored_rows + (t - a.row0)) * a.ld;
@@ -95,13 +127,16 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IndexScoreArgs a) {
   }
 }
 
-bool index_mfma_supported(const Shape& sh) { return sh.dtype == 1 && sh.d_I % 32 == 0; }
+bool index_mfma_supported(const Shape& sh) { return sh.dtype == 1 && (sh.d_I == 32 || sh.d_I == 64 || sh.d_I == 128); }
 
 hipError_t launch_index_scores_mfma(const IndexScoreArgs& a, hipStream_t st) {
   if (a.n - a.row0 <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n + IX_COLS - 1) / IX_COLS), (unsigned)((a.n + IX_ROWS - 1) / IX_ROWS),
-                  (unsigned)a.sh.B);
-  klaunch(k_index_scores_mfma, grid, dim3(256), 0, st, a);
+  const dim3 grid((unsigned)((a.n + IX_T - 1) / IX_T), (unsigned)((a.n + IX_T - 1) / IX_T), (unsigned)a.sh.B);
+  switch (a.sh.d_I) {
+    case 32: klaunch(k_index_scores_mfma<32>, grid, dim3(256), 0, st, a); break;
+    case 64: klaunch(k_index_scores_mfma<64>, grid, dim3(256), 0, st, a); break;
+    default: klaunch(k_index_scores_mfma<128>, grid, dim3(256), 0, st, a); break;
+  }
   return hipGetLastError();
 }
 
