@@ -36,13 +36,6 @@ struct AttnShared {
 };
 
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two floats to packed bf16 (round to nearest even, one instruction on gfx950).
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
-}
 
 template <int D>
 struct AttnRegs {

@@ -28,8 +28,15 @@
 namespace lisa {
 
 constexpr int LC = 64;          // chunk length
-constexpr int LT = 256;         // threads per block (4 waves)
 constexpr int LPAD = 8;         // LDS row padding (elements)
+
+// One wave per 16 value columns of the state: D / 16 waves.
+template <int D>
+struct LinCfg {
+  static constexpr int W = D / 16;        // waves per block
+  static constexpr int T = 64 * W;        // threads per block
+  static constexpr int WPI = W / 4;       // waves per 16-row query block of a chunk
+};
 
 template <int D>
 struct LinShared {
@@ -40,7 +47,7 @@ struct LinShared {
   bf16_t vt[D][LC + LPAD];      // V transposed
   bf16_t a[LC][LC + LPAD];      // masked intra-chunk scores
   float z[2][D];                // normaliser before / after the chunk
-  float den[LC];
+  float rs[LinCfg<D>::WPI + 1][LC];  // partial row sums of A; last: phi(q) . z
 };
 
 template <int D>
@@ -52,19 +59,20 @@ struct LinSumShared {
 
 // Global -> register prefetch of one chunk.  A thread holds, per matrix,
 // NP pairs of 16-byte vectors: tokens 2 tau and 2 tau + 1 (tau = lane % 32)
-// at columns 8 c8, c8 = 2 (wave + 4 m) + lane / 32.  Holding two adjacent
+// at columns 8 c8, c8 = 2 (wave + W m) + lane / 32.  Holding two adjacent
 // tokens lets the transposed LDS copies be written as packed token pairs:
 // 32 consecutive dwords of one row per half wave, free of bank conflicts.
 template <int D, bool WITH_Q>
 struct ChunkRegs {
-  static constexpr int NP = LC * D / 16 / LT;
+  static constexpr int NP = LC * D / 16 / LinCfg<D>::T;
   uint4 q[WITH_Q ? 2 * NP : 1], k[2 * NP], v[2 * NP];
 };
 
+template <int D>
 __device__ __forceinline__ void pair_coords(int m, int& tau, int& c8) {
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   tau = lane & 31;
-  c8 = 2 * (wave + 4 * m) + (lane >> 5);
+  c8 = 2 * (wave + LinCfg<D>::W * m) + (lane >> 5);
 }
 
 template <int D, bool WITH_Q>
@@ -73,7 +81,7 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<D, WITH_Q>& r, const bf16_t
 #pragma unroll
   for (int m = 0; m < ChunkRegs<D, WITH_Q>::NP; ++m) {
     int tau, c8;
-    pair_coords(m, tau, c8);
+    pair_coords<D>(m, tau, c8);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       // clamped: every load is issued unconditionally
@@ -85,15 +93,6 @@ __device__ __forceinline__ void chunk_load(ChunkRegs<D, WITH_Q>& r, const bf16_t
   }
 }
 
-__device__ __forceinline__ void split_hi_lo(float f, uint32_t& hi, uint32_t& lo) {
-  hi = f2bf(f);
-  lo = f2bf(f - bf2f(hi));
-}
-
-__device__ __forceinline__ uint4 pack8(const uint32_t (&h)[8]) {
-  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-}
-
 // Registers -> LDS: phi applied, hi/lo split, transposed copies.  Tokens at
 // or past n are written as zeros (phi(0) = 1 would otherwise count them).
 template <int D, bool WITH_Q, typename SM>
@@ -101,64 +100,71 @@ __device__ __forceinline__ void chunk_store(const ChunkRegs<D, WITH_Q>& r, SM& s
 #pragma unroll
   for (int m = 0; m < ChunkRegs<D, WITH_Q>::NP; ++m) {
     int tau, c8;
-    pair_coords(m, tau, c8);
-    uint32_t kh[2][8], kl[2][8], vv[2][8];
+    pair_coords<D>(m, tau, c8);
+    const bool v0 = t0 + 2 * tau < n, v1 = t0 + 2 * tau + 1 < n;
+    float k0[8], k1[8];
+    Vec<bf16_t>::unpack(r.k[2 * m], k0);
+    Vec<bf16_t>::unpack(r.k[2 * m + 1], k1);
+    // element e of both tokens as one packed pair: the transposed row's dword
+    uint32_t kh[8], kl[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tok = 2 * tau + u;
-      const bool valid = t0 + tok < n;
-      float kf[8];
-      Vec<bf16_t>::unpack(r.k[2 * m + u], kf);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) split_hi_lo(valid ? phi(kf[e]) : 0.f, kh[u][e], kl[u][e]);
-      const uint4 v = valid ? r.v[2 * m + u] : make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vv[u][2 * e] = vw[e] & 0xffffu;
-        vv[u][2 * e + 1] = vw[e] >> 16;
-      }
-      if constexpr (WITH_Q) {
-        *reinterpret_cast<uint4*>(&sm.k[tok][8 * c8]) = pack8(kh[u]);
-        float qf[8];
-        Vec<bf16_t>::unpack(r.q[2 * m + u], qf);
-        uint32_t qh[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qh[e] = f2bf(valid ? phi(qf[e]) : 0.f);
-        *reinterpret_cast<uint4*>(&sm.q[tok][8 * c8]) = pack8(qh);
-      }
-    }
+    for (int e = 0; e < 8; ++e) split_pk(v0 ? phi(k0[e]) : 0.f, v1 ? phi(k1[e]) : 0.f, kh[e], kl[e]);
+    const uint4 va = v0 ? r.v[2 * m] : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 vb = v1 ? r.v[2 * m + 1] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t a4[4] = {va.x, va.y, va.z, va.w}, b4[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int row = 8 * c8 + e;
-      *reinterpret_cast<uint32_t*>(&sm.kt_hi[row][2 * tau]) = kh[0][e] | (kh[1][e] << 16);
-      *reinterpret_cast<uint32_t*>(&sm.kt_lo[row][2 * tau]) = kl[0][e] | (kl[1][e] << 16);
-      *reinterpret_cast<uint32_t*>(&sm.vt[row][2 * tau]) = vv[0][e] | (vv[1][e] << 16);
+      *reinterpret_cast<uint32_t*>(&sm.kt_hi[row][2 * tau]) = kh[e];
+      *reinterpret_cast<uint32_t*>(&sm.kt_lo[row][2 * tau]) = kl[e];
+      const uint32_t x = a4[e / 2], y = b4[e / 2];
+      *reinterpret_cast<uint32_t*>(&sm.vt[row][2 * tau]) =
+          (e & 1) ? __builtin_amdgcn_perm(y, x, 0x07060302u) : __builtin_amdgcn_perm(y, x, 0x05040100u);
+    }
+    if constexpr (WITH_Q) {
+      // row-major phi(K) (hi) of each token: regroup the pairs by token
+      uint4 r0, r1;
+      uint32_t* p0 = &r0.x;
+      uint32_t* p1 = &r1.x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p0[j] = __builtin_amdgcn_perm(kh[2 * j + 1], kh[2 * j], 0x05040100u);
+        p1[j] = __builtin_amdgcn_perm(kh[2 * j + 1], kh[2 * j], 0x07060302u);
+      }
+      *reinterpret_cast<uint4*>(&sm.k[2 * tau][8 * c8]) = r0;
+      *reinterpret_cast<uint4*>(&sm.k[2 * tau + 1][8 * c8]) = r1;
+      float q0[8], q1[8];
+      Vec<bf16_t>::unpack(r.q[2 * m], q0);
+      Vec<bf16_t>::unpack(r.q[2 * m + 1], q1);
+      uint4 s0, s1;
+      uint32_t* w0 = &s0.x;
+      uint32_t* w1 = &s1.x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w0[j] = cvt_pk_bf16(v0 ? phi(q0[2 * j]) : 0.f, v0 ? phi(q0[2 * j + 1]) : 0.f);
+        w1[j] = cvt_pk_bf16(v1 ? phi(q1[2 * j]) : 0.f, v1 ? phi(q1[2 * j + 1]) : 0.f);
+      }
+      *reinterpret_cast<uint4*>(&sm.q[2 * tau][8 * c8]) = s0;
+      *reinterpret_cast<uint4*>(&sm.q[2 * tau + 1][8 * c8]) = s1;
     }
   }
 }
 
 // S[dk][dv] += sum_tok phi(K)[tok][dk] V[tok][dv] over the staged chunk, for
-// the wave's dv blocks: tiles (p, q) with p over dk blocks of 16.
+// the wave's 16 dv columns: tiles p over dk blocks of 16.
 template <int D, typename SM>
-__device__ __forceinline__ void state_update(f32x4 (&S)[D / 16][D / 64], const SM& sm, int wave) {
+__device__ __forceinline__ void state_update(f32x4 (&S)[D / 16], const SM& sm, int wave) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int s = 0; s < LC / 32; ++s) {
-    bf16x8 bv[D / 64];
-#pragma unroll
-    for (int q = 0; q < D / 64; ++q)
-      bv[q] = as_bf16x8(lds_read16(&sm.vt[16 * (wave * (D / 64) + q) + r16][32 * s + 8 * g]));
+    const bf16x8 bv = as_bf16x8(lds_read16(&sm.vt[16 * wave + r16][32 * s + 8 * g]));
 #pragma unroll
     for (int p = 0; p < D / 16; ++p) {
       const bf16x8 ah = as_bf16x8(lds_read16(&sm.kt_hi[16 * p + r16][32 * s + 8 * g]));
       const bf16x8 al = as_bf16x8(lds_read16(&sm.kt_lo[16 * p + r16][32 * s + 8 * g]));
-#pragma unroll
-      for (int q = 0; q < D / 64; ++q) {
-        S[p][q] = mfma16(ah, bv[q], S[p][q]);
-        S[p][q] = mfma16(al, bv[q], S[p][q]);
-      }
+      S[p] = mfma16(ah, bv, S[p]);
+      S[p] = mfma16(al, bv, S[p]);
     }
   }
 }
@@ -186,11 +192,11 @@ __device__ __forceinline__ size_t tile_off(int D, int p, int qg, int lane, int r
 
 // ---------------------------------------------------------------------------
 // state increments: block (b, h, segment); wave w owns dv columns
-// [D/4 w, D/4 (w+1)).  Segment mode writes the increment to `seg`; in-place
+// [16 w, 16 w + 16).  Segment mode writes the increment to `seg`; in-place
 // mode (one segment) adds it to S and z.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(LT) void k_lin_seg_sums(LinearChunkArgs a) {
+__global__ __launch_bounds__(LinCfg<D>::T) void k_lin_seg_sums(LinearChunkArgs a) {
   __shared__ LinSumShared<D> sm;
   const Shape& sh = a.sh;
   const int seg = blockIdx.x % a.nseg;
@@ -203,15 +209,12 @@ __global__ __launch_bounds__(LT) void k_lin_seg_sums(LinearChunkArgs a) {
   const int t_begin = seg * a.seg_len;
   const int t_end = min(a.n, t_begin + a.seg_len);
 
-  f32x4 S[D / 16][D / 64];
+  f32x4 S[D / 16];
   float* Sg = a.S + (size_t)bh * D * D;
 #pragma unroll
   for (int p = 0; p < D / 16; ++p)
 #pragma unroll
-    for (int q = 0; q < D / 64; ++q)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[p][q][r] = a.in_place ? Sg[tile_off(D, p, wave * (D / 64) + q, lane, r)] : 0.f;
+    for (int r = 0; r < 4; ++r) S[p][r] = a.in_place ? Sg[tile_off(D, p, wave, lane, r)] : 0.f;
   float zacc = (a.in_place && tid < D) ? a.z[(size_t)bh * D + tid] : 0.f;
 
   ChunkRegs<D, false> cr;
@@ -228,9 +231,7 @@ __global__ __launch_bounds__(LT) void k_lin_seg_sums(LinearChunkArgs a) {
 #pragma unroll
   for (int p = 0; p < D / 16; ++p)
 #pragma unroll
-    for (int q = 0; q < D / 64; ++q)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[tile_off(D, p, wave * (D / 64) + q, lane, r)] = S[p][q][r];
+    for (int r = 0; r < 4; ++r) dst[tile_off(D, p, wave, lane, r)] = S[p][r];
   if (tid < D) {
     if (a.in_place) a.z[(size_t)bh * D + tid] = zacc;
     else dst[D * D + tid] = zacc;
@@ -262,11 +263,13 @@ __global__ __launch_bounds__(256) void k_lin_seg_prefix(LinearChunkArgs a) {
 
 // ---------------------------------------------------------------------------
 // chunked outputs: block (b, h, segment), starting from the segment's state.
+// Wave w owns dv columns [16 w, 16 w + 16) of S and of the outputs; the
+// intra-chunk score tiles are shared out WPI waves per query block.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(LT) void k_lin_chunks(LinearChunkArgs a) {
+__global__ __launch_bounds__(LinCfg<D>::T) void k_lin_chunks(LinearChunkArgs a) {
   __shared__ LinShared<D> sm;
-  constexpr int NQ = D / 64;  // dv blocks of 16 per wave
+  constexpr int WPI = LinCfg<D>::WPI;
   const Shape& sh = a.sh;
   const bool normalized = !(sh.flags & 1u);
   const int seg = blockIdx.x % a.nseg;
@@ -284,13 +287,11 @@ __global__ __launch_bounds__(LT) void k_lin_chunks(LinearChunkArgs a) {
   if (t_begin >= t_end) return;
 
   const float* st = a.seg_state + ((size_t)bh * a.nseg + seg) * (D * D + D);
-  f32x4 S[D / 16][NQ];
+  f32x4 S[D / 16];
 #pragma unroll
   for (int p = 0; p < D / 16; ++p)
 #pragma unroll
-    for (int q = 0; q < NQ; ++q)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[p][q][r] = st[tile_off(D, p, wave * NQ + q, lane, r)];
+    for (int r = 0; r < 4; ++r) S[p][r] = st[tile_off(D, p, wave, lane, r)];
   if (tid < D) sm.z[0][tid] = st[D * D + tid];
   int zc = 0;
 
@@ -302,32 +303,38 @@ __global__ __launch_bounds__(LT) void k_lin_chunks(LinearChunkArgs a) {
     __syncthreads();
     if (t0 + LC < t_end) chunk_load<D, true>(cr, qb, kb, vb, tok_stride, t0 + LC, a.n);
 
-    // intra-chunk scores of query block ib = wave, key blocks kb <= ib
-    // (plus a zero block where the next MFMA reads past the diagonal)
-    const int ib = wave;
+    // intra-chunk scores of query block ib, key blocks kbk = sub, sub + WPI,
+    // ... up to ib (plus the zero block above the diagonal that the A V
+    // product reads when ib is even)
+    const int ib = wave / WPI, sub = wave % WPI;
     float rsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kbk = 0; kbk < 4; ++kbk) {
+    for (int kk = 0; kk < 4 / WPI; ++kk) {
+      const int kbk = sub + WPI * kk;
       if (kbk > (ib | 1)) break;
       f32x4 acc = zero4();
       if (kbk <= ib) {
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) {
           const bf16x8 qa = as_bf16x8(lds_read16(&sm.q[16 * ib + r16][32 * s + 8 * g]));
-          const bf16x8 kk = as_bf16x8(lds_read16(&sm.k[16 * kbk + r16][32 * s + 8 * g]));
-          acc = mfma16(qa, kk, acc);
+          const bf16x8 kk8 = as_bf16x8(lds_read16(&sm.k[16 * kbk + r16][32 * s + 8 * g]));
+          acc = mfma16(qa, kk8, acc);
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ib + 4 * g + r, j = 16 * kbk + r16;
-        const uint32_t ab = j <= i ? f2bf(acc[r]) : 0u;
+        const uint32_t ab = j <= i ? (cvt_pk_bf16(acc[r], 0.f) & 0xffffu) : 0u;
         sm.a[i][j] = (bf16_t)ab;
         rsum[r] += bf2f(ab);
       }
     }
-    // den for the 16 rows of block ib: rowsum(A) + phi(q) . z
-    {
+    // partial row sums: rows 16 ib + 4 g + r, summed over the 16 key lanes
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rsum[r] = group_sum(rsum[r], 16);
+    if (r16 < 4)
+      sm.rs[sub][16 * ib + 4 * g + r16] = r16 == 0 ? rsum[0] : r16 == 1 ? rsum[1] : r16 == 2 ? rsum[2] : rsum[3];
+    if (sub == WPI - 1) {  // phi(q) . z for the 16 rows of block ib
       float qz = 0.f;
       const int i = 16 * ib + r16;
 #pragma unroll
@@ -339,72 +346,61 @@ __global__ __launch_bounds__(LT) void k_lin_chunks(LinearChunkArgs a) {
       }
       qz += __shfl_xor(qz, 16, WAVE);
       qz += __shfl_xor(qz, 32, WAVE);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) rsum[r] = group_sum(rsum[r], 16);
-      // row r16 of the block: rsum[r16 % 4] of lane group r16 / 4
-      float mine = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = __shfl(rsum[r], 16 * (r16 >> 2), WAVE);
-        if ((r16 & 3) == r) mine = x;
-      }
-      if (g == 0) sm.den[i] = mine + qz;
+      if (g == 0) sm.rs[WPI][i] = qz;
     }
-    __syncthreads();  // A and den complete
+    __syncthreads();  // A and the row sums complete
 
-    // num = A V + phi(Q) S for every query block and the wave's dv blocks
-    uint4 shi[D / 32][NQ], slo[D / 32][NQ];
+    // num = A V + phi(Q) S for every query block, the wave's dv block.  S
+    // enters as the B operand straight from the accumulator: lane (r16, g)
+    // holds dk rows 32 pp + 4 g + r and 32 pp + 16 + 4 g + r of column
+    // r16, so phi(Q) is read in that same contraction order.
+    uint4 shi[D / 32], slo[D / 32];
 #pragma unroll
-    for (int pp = 0; pp < D / 32; ++pp)
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        uint32_t h8[8], l8[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          split_hi_lo(S[2 * pp][q][r], h8[r], l8[r]);
-          split_hi_lo(S[2 * pp + 1][q][r], h8[4 + r], l8[4 + r]);
-        }
-        shi[pp][q] = make_uint4(h8[0] | (h8[1] << 16), h8[2] | (h8[3] << 16), h8[4] | (h8[5] << 16),
-                                h8[6] | (h8[7] << 16));
-        slo[pp][q] = make_uint4(l8[0] | (l8[1] << 16), l8[2] | (l8[3] << 16), l8[4] | (l8[5] << 16),
-                                l8[6] | (l8[7] << 16));
-      }
+    for (int pp = 0; pp < D / 32; ++pp) {
+      uint32_t h4[4], l4[4];
+      split_pk(S[2 * pp][0], S[2 * pp][1], h4[0], l4[0]);
+      split_pk(S[2 * pp][2], S[2 * pp][3], h4[1], l4[1]);
+      split_pk(S[2 * pp + 1][0], S[2 * pp + 1][1], h4[2], l4[2]);
+      split_pk(S[2 * pp + 1][2], S[2 * pp + 1][3], h4[3], l4[3]);
+      shi[pp] = make_uint4(h4[0], h4[1], h4[2], h4[3]);
+      slo[pp] = make_uint4(l4[0], l4[1], l4[2], l4[3]);
+    }
 #pragma unroll
     for (int ibq = 0; ibq < 4; ++ibq) {
-      f32x4 num[NQ];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) num[q] = zero4();
+      f32x4 num = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (s == 1 && ibq < 2) break;
         const bf16x8 aa = as_bf16x8(lds_read16(&sm.a[16 * ibq + r16][32 * s + 8 * g]));
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const bf16x8 vv = as_bf16x8(lds_read16(&sm.vt[16 * (wave * NQ + q) + r16][32 * s + 8 * g]));
-          num[q] = mfma16(aa, vv, num[q]);
-        }
+        const bf16x8 vv = as_bf16x8(lds_read16(&sm.vt[16 * wave + r16][32 * s + 8 * g]));
+        num = mfma16(aa, vv, num);
       }
 #pragma unroll
       for (int pp = 0; pp < D / 32; ++pp) {
         const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.q[16 * ibq + r16][32 * pp + 4 * g]);
         const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.q[16 * ibq + r16][32 * pp + 16 + 4 * g]);
         const bf16x8 qa = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          num[q] = mfma16(qa, as_bf16x8(shi[pp][q]), num[q]);
-          num[q] = mfma16(qa, as_bf16x8(slo[pp][q]), num[q]);
-        }
+        num = mfma16(qa, as_bf16x8(shi[pp]), num);
+        num = mfma16(qa, as_bf16x8(slo[pp]), num);
       }
       // outputs of rows 16 ibq + 4 g + r
+      const int i0 = 16 * ibq + 4 * g;
+      float4 den = *reinterpret_cast<const float4*>(&sm.rs[WPI][i0]);
+#pragma unroll
+      for (int u = 0; u < WPI; ++u) {
+        const float4 x = *reinterpret_cast<const float4*>(&sm.rs[u][i0]);
+        den.x += x.x;
+        den.y += x.y;
+        den.z += x.z;
+        den.w += x.w;
+      }
+      const float dd[4] = {den.x, den.y, den.z, den.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ibq + 4 * g + r;
-        const int t = t0 + i;
-        const float inv = normalized ? 1.f / sm.den[i] : 1.f;
+        const int t = t0 + i0 + r;
         if (t < t_end) {
-          float* o = a.o_lin + ((size_t)b * a.n + t) * tok_stride + (size_t)h * D;
-#pragma unroll
-          for (int q = 0; q < NQ; ++q) o[16 * (wave * NQ + q) + r16] = num[q][r] * inv;
+          const float inv = normalized ? __builtin_amdgcn_rcpf(dd[r]) : 1.f;
+          a.o_lin[((size_t)b * a.n + t) * tok_stride + (size_t)h * D + 16 * wave + r16] = num[r] * inv;
         }
       }
     }
@@ -420,10 +416,25 @@ __global__ __launch_bounds__(LT) void k_lin_chunks(LinearChunkArgs a) {
 // ---------------------------------------------------------------------------
 bool linear_mfma_supported(const Shape& sh) { return sh.dtype == 1 && (sh.d == 64 || sh.d == 128); }
 
+// Compute units of the current device (256 where it cannot be queried).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cached[dev] = c;
+  }
+  return cached[dev];
+}
+
+// Segments per (sequence, head): the chunk kernel holds one block per CU (its
+// LDS), so the blocks are sized to come out at no more than one per CU.
 void linear_segments(const Shape& sh, int n, int& nseg, int& seg_len) {
   const int chunks = (n + LC - 1) / LC;
   const int bh = sh.B * sh.H_L;
-  int want = (512 + bh - 1) / bh;
+  int want = max(1, device_cu_count() / bh);
   want = max(1, min(want, chunks));
   const int cps = (chunks + want - 1) / want;
   seg_len = cps * LC;
@@ -438,8 +449,8 @@ size_t linear_seg_floats(const Shape& sh, int n) {
 
 hipError_t launch_linear_seg_sums(const LinearChunkArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.sh.B * a.sh.H_L * a.nseg));
-  if (a.sh.d == 128) klaunch(k_lin_seg_sums<128>, grid, dim3(LT), 0, st, a);
-  else klaunch(k_lin_seg_sums<64>, grid, dim3(LT), 0, st, a);
+  if (a.sh.d == 128) klaunch(k_lin_seg_sums<128>, grid, dim3(LinCfg<128>::T), 0, st, a);
+  else klaunch(k_lin_seg_sums<64>, grid, dim3(LinCfg<64>::T), 0, st, a);
   return hipGetLastError();
 }
 
@@ -452,8 +463,8 @@ hipError_t launch_linear_seg_prefix(const LinearChunkArgs& a, hipStream_t st) {
 
 hipError_t launch_linear_chunks(const LinearChunkArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(a.sh.B * a.sh.H_L * a.nseg));
-  if (a.sh.d == 128) klaunch(k_lin_chunks<128>, grid, dim3(LT), 0, st, a);
-  else klaunch(k_lin_chunks<64>, grid, dim3(LT), 0, st, a);
+  if (a.sh.d == 128) klaunch(k_lin_chunks<128>, grid, dim3(LinCfg<128>::T), 0, st, a);
+  else klaunch(k_lin_chunks<64>, grid, dim3(LinCfg<64>::T), 0, st, a);
   return hipGetLastError();
 }
 
