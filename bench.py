@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-dense", action="store_true", help="skip the dense-attention decode baseline")
+    p.add_argument("--no-batched", action="store_true", help="skip the batch-32 ragged decode leg")
+    p.add_argument("--batched-steps", type=int, default=64)
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
     p.add_argument("--prefill-iters", type=int, default=5)
@@ -55,27 +57,39 @@ def parse():
 # ----------------------------------------------------------------------------
 # algorithmic traffic (bytes the method must move), per launch
 # ----------------------------------------------------------------------------
+def _lens(L, B):
+    """Context lengths of the B sequences (L: one length, or one per sequence)."""
+    return np.broadcast_to(np.asarray(L, dtype=np.int64), (B,))
+
+
 def decode_bytes(cfg, L, M, B):
     """Per-step bytes of the whole decode step (all sequences)."""
-    m = min(M, L)
-    per_tok = (L * cfg.H_Ik * cfg.d_I * 2                       # index keys
-               + m * cfg.H_kv * cfg.d * 4                        # gathered K and V
-               + 8 * cfg.H_L * cfg.d * (cfg.d + 1)               # S and z, read + write
-               + 2 * (2 * cfg.H_q * cfg.d + 3 * cfg.H_L * cfg.d + cfg.H_I * cfg.d_I
-                      + 2 * cfg.H_kv * cfg.d + cfg.H_Ik * cfg.d_I + cfg.hidden))
-    return B * per_tok + 2 * cfg.hidden * cfg.H_q
+    tot = 0
+    for l in _lens(L, B):
+        m = min(M, int(l))
+        tot += (int(l) * cfg.H_Ik * cfg.d_I * 2                   # index keys
+                + m * cfg.H_kv * cfg.d * 4                        # gathered K and V
+                + 8 * cfg.H_L * cfg.d * (cfg.d + 1)               # S and z, read + write
+                + 2 * (2 * cfg.H_q * cfg.d + 3 * cfg.H_L * cfg.d + cfg.H_I * cfg.d_I
+                       + 2 * cfg.H_kv * cfg.d + cfg.H_Ik * cfg.d_I + cfg.hidden))
+    return tot + 2 * cfg.hidden * cfg.H_q
 
 
 def phase_a_bytes(cfg, L, B):
-    per = (L * cfg.H_Ik * cfg.d_I * 2 + 8 * cfg.H_L * cfg.d * (cfg.d + 1)
-           + 2 * (3 * cfg.H_L * cfg.d + cfg.H_I * cfg.d_I + cfg.hidden)
-           + 2 * 2 * (2 * cfg.H_kv * cfg.d + cfg.H_Ik * cfg.d_I))   # new rows read + appended
-    return B * per + 2 * cfg.hidden * cfg.H_q
+    tot = 0
+    for l in _lens(L, B):
+        tot += (int(l) * cfg.H_Ik * cfg.d_I * 2 + 8 * cfg.H_L * cfg.d * (cfg.d + 1)
+                + 2 * (3 * cfg.H_L * cfg.d + cfg.H_I * cfg.d_I + cfg.hidden)
+                + 2 * 2 * (2 * cfg.H_kv * cfg.d + cfg.H_Ik * cfg.d_I))   # new rows read + appended
+    return tot + 2 * cfg.hidden * cfg.H_q
 
 
 def attention_bytes(cfg, L, M, B, dense=False):
-    m = L if dense else min(M, L)
-    return B * (m * cfg.H_kv * cfg.d * 4 + 2 * 2 * cfg.H_q * cfg.d)
+    tot = 0
+    for l in _lens(L, B):
+        m = int(l) if dense else min(M, int(l))
+        tot += m * cfg.H_kv * cfg.d * 4 + 2 * 2 * cfg.H_q * cfg.d
+    return tot
 
 
 def combine_bytes(cfg, B):
@@ -111,37 +125,13 @@ def kernel_roofline(name, avg_ms, work, bound):
             "algorithmic_work_per_launch": work, "avg_launch_us": round(avg_ms * 1e3, 3)}
 
 
-# ----------------------------------------------------------------------------
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer runs on a single "
-              "MI355X and this build has no multi-GPU path.", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import long_context_attention_lightning_amd as Lb
-    from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    Lb.library()
-    cid = 1
-    cfg = CONFIGS[cid]
-    B, Lctx, M = cfg.B, cfg.L, cfg.M
+def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense):
+    """Graph-replayed decode steps of one workload over nbuf buffer sets:
+    step time, per-kernel durations and rooflines, the dense baseline."""
+    from lisa_inputs import decode_inputs
+    B, Lctx, M = cfg.B, (cfg.L or cfg.L_hi), cfg.M
     T = torch.bfloat16
-    print(f"# bench: {cfg.name} B={B} L={Lctx} M={M} nbuf={args.nbuf}", file=sys.stderr, flush=True)
-
-    if args.copy_calibration:
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(4):  # elementwise kernel: reads 256 MiB, writes 256 MiB
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-    if args.prefill_only:
-        print(json.dumps(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs)), flush=True)
-        return
+    print(f"# decode: {cfg.name} B={B} L={Lctx} M={M} nbuf={nbuf}", file=sys.stderr, flush=True)
     inp = decode_inputs(cfg, cid)
 
     def up(a, dt=T):
@@ -158,7 +148,7 @@ def main():
     sets = []
     per_set = ("q", "k_new", "v_new", "q_idx", "k_idx_new", "q_lin", "k_lin", "v_lin", "x",
                "k_cache", "v_cache", "k_idx_cache", "S", "z")
-    for i in range(args.nbuf):
+    for i in range(nbuf):
         s = {k: base[k].clone() for k in per_set}
         s["out"] = torch.empty((B, cfg.H_q, cfg.d), dtype=T, device="cuda")
         s["out_dense"] = torch.empty((B, cfg.H_q, cfg.d), dtype=T, device="cuda")
@@ -167,7 +157,7 @@ def main():
         s["ws_dense"] = Lb.workspace(sh, Lb.LISA_OP_DENSE_DECODE)
         sets.append(s)
     set_bytes = sum(t.numel() * t.element_size() for t in sets[0].values())
-    print(f"# {args.nbuf} buffer sets of {set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
+    print(f"# {nbuf} buffer sets of {set_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
 
     def step(s):
         Lb.lisa_decode_step(sh, seq, s["q"], s["k_new"], s["v_new"], s["q_idx"], s["k_idx_new"],
@@ -199,12 +189,12 @@ def main():
         return reps * len(sets)
 
     def time_graph(g):
-        run(g, args.warmup)
+        run(g, warmup)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
-        n = run(g, args.steps)
+        n = run(g, steps)
         t1.record()
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / n, n
@@ -243,22 +233,22 @@ def main():
           file=sys.stderr, flush=True)
 
     # dense baseline over the same caches
-    if not args.no_dense:
+    if with_dense:
         g_dense = capture(dense_step)
         ms_dense, _ = time_graph(g_dense)
         kd = kernel_times(dense_step, (2, 8))
         dense_kernel_us = {Lb.lisa_kernel_name(k): round(v * 1e3, 3) for k, v in kd.items()}
         del g_dense
 
-    tok_s = B / (ms_step * 1e-3)
-    work = {0: (phase_a_bytes(cfg, Lctx, B), "hbm"),
-            1: (SELECT_OPS_PER_KEY * Lctx * B, "alu"),
-            12: (attention_bytes(cfg, Lctx, M, B) + 4 * Lctx * B, "hbm"),
-            2: (attention_bytes(cfg, Lctx, M, B), "hbm"),
+    lens = inp["seq_lens"].astype(np.int64)
+    work = {0: (phase_a_bytes(cfg, lens, B), "hbm"),
+            1: (SELECT_OPS_PER_KEY * int(lens.sum()), "alu"),
+            12: (attention_bytes(cfg, lens, M, B) + 4 * int(lens.sum()), "hbm"),
+            2: (attention_bytes(cfg, lens, M, B), "hbm"),
             8: (combine_bytes(cfg, B), "hbm")}
     roofs = {Lb.lisa_kernel_name(k): kernel_roofline(Lb.lisa_kernel_name(k), kt[k], *work[k]) for k in dec_kids}
     roof = roofs[Lb.lisa_kernel_name(dom)]
-    step_bytes = decode_bytes(cfg, Lctx, M, B)
+    step_bytes = decode_bytes(cfg, lens, M, B)
     extra = {
         "us_per_step": round(ms_step * 1e3, 3),
         "kernel_us": {k: round(v * 1e3, 3) for k, v in per_kernel_ms.items()},
@@ -267,9 +257,8 @@ def main():
         "kernel_roofline": roofs,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_roofline_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "pages_context": "about 50% end-to-end inference speedup at 16K context (other hardware, whole model)",
     }
-    if not args.no_dense:
+    if with_dense:
         extra.update({"dense_decode_us_per_step": round(ms_dense * 1e3, 3),
                       "dense_decode_kernel_us": dense_kernel_us,
                       "dense_decode_tok_s": round(B / (ms_dense * 1e-3), 1),
@@ -277,6 +266,57 @@ def main():
     del g_main
     sets.clear()
     torch.cuda.empty_cache()
+    extra.update(inp=inp, ms_step=ms_step, steps=done, roofline=roof)
+    return extra
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer runs on a single "
+              "MI355X and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_attention_lightning_amd as Lb
+    from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    Lb.library()
+    cid = 1
+    cfg = CONFIGS[cid]
+    B, Lctx, M = cfg.B, cfg.L, cfg.M
+    T = torch.bfloat16
+    print(f"# bench: {cfg.name} B={B} L={Lctx} M={M} nbuf={args.nbuf}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):  # elementwise kernel: reads 256 MiB, writes 256 MiB
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.prefill_only:
+        print(json.dumps(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs)), flush=True)
+        return
+    d = bench_decode(args, torch, Lb, cfg, cid, args.nbuf, args.steps, args.warmup, not args.no_dense)
+    inp = d.pop("inp")
+    ms_step, done, roof = d.pop("ms_step"), d.pop("steps"), d.pop("roofline")
+    tok_s = B / (ms_step * 1e-3)
+    extra = d
+    extra["pages_context"] = "about 50% end-to-end inference speedup at 16K context (other hardware, whole model)"
+    if not args.no_batched:
+        cb = CONFIGS[2]
+        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense)
+        db.pop("inp")
+        bms = db.pop("ms_step")
+        db.pop("steps")
+        extra["batched_decode"] = dict(workload=cb.name, batch=cb.B, context=f"{cb.L_lo}..{cb.L_hi} (seeded uniform)",
+                                       tok_s=round(cb.B / (bms * 1e-3), 1), **db)
+        del db
+        torch.cuda.empty_cache()
 
     if not args.no_prefill:
         extra.update(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs))
