@@ -11,9 +11,9 @@
 // flash-attention forward pass, and sends unselected pairs to -inf before
 // the online softmax.
 //
-// Block = 4 waves, one query head each, 64 query positions (4 tiles of 16)
-// of one KV head; the K tile (row-major) and V tile (transposed) of 64 keys
-// are staged in LDS for all four heads.  Per tile a wave computes
+// Block = 4 waves of one KV head, each wave one (query head, 32 query
+// positions) unit; the K tile (row-major) and V tile (transposed) of 64
+// keys are staged in LDS for all four waves.  Per tile a wave computes
 // S^T = K Q^T (keys along the accumulator rows, so a lane holds four
 // consecutive keys of one query), masks and exponentiates it, and feeds the
 // probabilities straight from registers into O += P V, with the key order
@@ -71,23 +71,27 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) {  // two blocks per CU
   __shared__ AttnShared<D> sm;
   const Shape& sh = a.sh;
+  const int n = a.n;
   const int G = sh.H_q / sh.H_kv;
-  const int nhg = (G + 3) / 4;
-  const int npb = (a.n + AQ - 1) / AQ;
-  // longest causal rows first
-  const int per_pb = sh.B * sh.H_kv * nhg;
-  const int pb = npb - 1 - (int)(blockIdx.x / per_pb);
-  int rest = blockIdx.x % per_pb;
-  const int hg = rest % nhg;
-  rest /= nhg;
-  const int kvh = rest % sh.H_kv, b = rest / sh.H_kv;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int r16 = lane & 15, g = lane >> 4;
-  const int hl = 4 * hg + wave;             // head inside the KV group
-  const bool active = hl < G;  // idle waves compute a duplicate head on their own SIMD and store nothing
-  const int h = kvh * G + min(hl, G - 1);
-  const int T0 = pb * AQ;
-  const int n = a.n;
+  // Work units are (query tile of AQ rows, head of the KV group) pairs,
+  // numbered head-fastest from the last query tile down; block k takes
+  // units 4k .. 4k + 3, one per wave (at most two adjacent query tiles, so
+  // the staged K/V tiles serve every wave), longest causal rows first.
+  const int nqt = (n + AQ - 1) / AQ;
+  const int units = nqt * G;
+  const int per = sh.B * sh.H_kv;
+  const int kblk = (int)(blockIdx.x / per);
+  const int rest = (int)(blockIdx.x % per);
+  const int kvh = rest % sh.H_kv, b = rest / sh.H_kv;
+  const int unit = 4 * kblk + wave;
+  const bool active = unit < units;  // idle waves repeat the last unit and store nothing
+  const int uu = min(unit, units - 1);
+  const int h = kvh * G + uu % G;
+  const int T0 = (nqt - 1 - uu / G) * AQ;
+  // keys up to the last row of the block's highest query tile
+  const int tmax = min((nqt - (4 * kblk) / G) * AQ, n) - 1;
 
   const size_t kv_stride = (size_t)sh.H_kv * D;
   const bf16_t* kb = (const bf16_t*)a.k_cache + (size_t)b * sh.cap * kv_stride + (size_t)kvh * D;
@@ -97,7 +101,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   const uint32_t* mrow0 = a.mask + (size_t)b * n * a.mask_ld;
 
   const float scale = a.scale_log2e;
-  const int tmax = min(T0 + AQ, n) - 1;
   const int nkt = tmax / AK + 1;
 
   // mask rows: row of query tile i for this lane, clamped to the sequence
@@ -335,8 +338,8 @@ int64_t attn_mask_ld(int n) { return (int64_t)((((n + 31) / 32) + 1) / 2 * 2); }
 
 hipError_t launch_attn_prefill_mfma(const AttnMaskArgs& a, hipStream_t st) {
   const int G = a.sh.H_q / a.sh.H_kv;
-  const int npb = (a.n + AQ - 1) / AQ;
-  const dim3 grid((unsigned)(npb * a.sh.B * a.sh.H_kv * ((G + 3) / 4)));
+  const int units = (a.n + AQ - 1) / AQ * G;
+  const dim3 grid((unsigned)((units + 3) / 4 * a.sh.B * a.sh.H_kv));
   if (a.sh.d == 128) klaunch(k_attn_prefill_mfma<128>, grid, dim3(256), 0, st, a);
   else klaunch(k_attn_prefill_mfma<64>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
