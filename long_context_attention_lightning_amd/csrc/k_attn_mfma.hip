@@ -29,11 +29,20 @@ constexpr int AK = 64;    // keys per tile
 constexpr int AP = 2;     // query tiles of 16 per wave
 constexpr int AQ = 16 * AP;
 
+// Row strides of 4 dwords modulo the 32 LDS banks keep every 16-byte
+// operand read free of bank conflicts.  The key columns of the V tile are
+// stored permuted within each 32-key half (vt_col), so that the eight keys
+// one lane contributes to a P V step are adjacent.
 template <int D>
 struct AttnShared {
-  bf16_t k[AK][D + 16];
+  bf16_t k[AK][D + 8];
   bf16_t vt[D + 16][AK + 8];  // rows D .. D + 15 hold ones: P V also yields the row sums
 };
+
+// Column of key j in the V tile: key 32 s + 16 h + 4 g + r sits at
+// 32 s + 8 g + 4 h + r, matching the P operand, whose lane group g holds keys
+// 32 s + 4 g + r and 32 s + 16 + 4 g + r of contraction step s.
+__device__ __forceinline__ int vt_col(int j) { return (j & 32) | ((j & 12) << 1) | ((j & 16) >> 2) | (j & 3); }
 
 
 
@@ -59,10 +68,11 @@ __device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& 
     const int tau = lane & 31, c8 = 2 * (wave + 4 * m) + (lane >> 5);
     const uint32_t a[4] = {r.v[2 * m].x, r.v[2 * m].y, r.v[2 * m].z, r.v[2 * m].w};
     const uint32_t b[4] = {r.v[2 * m + 1].x, r.v[2 * m + 1].y, r.v[2 * m + 1].z, r.v[2 * m + 1].w};
+    const int col = vt_col(2 * tau);  // keys 2 tau and 2 tau + 1 stay adjacent
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<uint32_t*>(&sm.vt[8 * c8 + 2 * e][2 * tau]) = (a[e] & 0xffffu) | (b[e] << 16);
-      *reinterpret_cast<uint32_t*>(&sm.vt[8 * c8 + 2 * e + 1][2 * tau]) = (a[e] >> 16) | (b[e] & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&sm.vt[8 * c8 + 2 * e][col]) = __builtin_amdgcn_perm(b[e], a[e], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&sm.vt[8 * c8 + 2 * e + 1][col]) = __builtin_amdgcn_perm(b[e], a[e], 0x07060302u);
     }
   }
 }
@@ -94,49 +104,55 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   const int tmax = min((nqt - (4 * kblk) / G) * AQ, n) - 1;
 
   const size_t kv_stride = (size_t)sh.H_kv * D;
-  const bf16_t* kb = (const bf16_t*)a.k_cache + (size_t)b * sh.cap * kv_stride + (size_t)kvh * D;
-  const bf16_t* vb = (const bf16_t*)a.v_cache + (size_t)b * sh.cap * kv_stride + (size_t)kvh * D;
   const size_t q_stride = (size_t)sh.H_q * D;
   const bf16_t* qb = (const bf16_t*)a.q + (size_t)b * n * q_stride + (size_t)h * D;
-  const uint32_t* mrow0 = a.mask + (size_t)b * n * a.mask_ld;
 
   const float scale = a.scale_log2e;
   const int nkt = tmax / AK + 1;
 
-  // mask rows: row of query tile i for this lane, clamped to the sequence
-  const uint32_t* mq = mrow0 + (size_t)min(T0, n - 1) * a.mask_ld;
-  // rows past n read row n-1 (its results are never stored)
-  const int mrow_clamp = n - 1 - T0;
-
-  // next tile's K (and V in the second pass) and mask words, held in
-  // registers while the current tile runs
-  AttnRegs<D> rg;
-  auto prefetch = [&](int J0, bool with_v) {
+  // K, V and mask rows of the sequence through buffer resources limited to
+  // its n rows: loads past them return zeros.  Per-thread byte offsets start
+  // at key tile 0 and advance by one tile per prefetch.
+  const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16_t*)a.k_cache + (size_t)b * sh.cap * kv_stride), (short)0, (int)(n * kv_stride * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((const bf16_t*)a.v_cache + (size_t)b * sh.cap * kv_stride), (short)0, (int)(n * kv_stride * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t mres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.mask + (size_t)b * n * a.mask_ld), (short)0, (int)(n * a.mask_ld * 4), 0x00020000);
+  const uint32_t tile_kv_bytes = (uint32_t)(AK * kv_stride * 2);
+  uint32_t koff[AttnRegs<D>::NK], voff[2 * AttnRegs<D>::NV], moff_b[AP];
 #pragma unroll
-    for (int m = 0; m < AttnRegs<D>::NK; ++m) {
-      const int e = tid + 256 * m;
-      const int tok = e / (D / 8), c8 = e % (D / 8);
-      rg.k[m] = ld16(kb + (size_t)min(J0 + tok, n - 1) * kv_stride + 8 * c8);
-    }
+  for (int m = 0; m < AttnRegs<D>::NK; ++m) {
+    const int e = tid + 256 * m;
+    koff[m] = (uint32_t)(((e / (D / 8)) * kv_stride + (size_t)kvh * D + 8 * (e % (D / 8))) * 2);
+  }
+#pragma unroll
+  for (int m = 0; m < AttnRegs<D>::NV; ++m) {
+    const int tau = lane & 31, c8 = 2 * (wave + 4 * m) + (lane >> 5);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) voff[2 * m + u] = (uint32_t)(((2 * tau + u) * kv_stride + (size_t)kvh * D + 8 * c8) * 2);
+  }
+  // mask rows of the wave's queries (rows past n read row n - 1; never stored)
+#pragma unroll
+  for (int i = 0; i < AP; ++i) moff_b[i] = (uint32_t)((size_t)min(T0 + 16 * i + r16, n - 1) * a.mask_ld * 4);
+
+  // next tile's K (and V) and mask words, held in registers while the
+  // current tile runs
+  AttnRegs<D> rg;
+  auto prefetch = [&](int kt, bool with_v) {
+    const uint32_t tk = (uint32_t)kt * tile_kv_bytes;
+#pragma unroll
+    for (int m = 0; m < AttnRegs<D>::NK; ++m)
+      rg.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kres, koff[m] + tk, 0, 0));
     if (with_v) {
 #pragma unroll
-      for (int m = 0; m < AttnRegs<D>::NV; ++m) {
-        const int tau = lane & 31, c8 = 2 * (wave + 4 * m) + (lane >> 5);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          rg.v[2 * m + u] = ld16(vb + (size_t)min(J0 + 2 * tau + u, n - 1) * kv_stride + 8 * c8);
-      }
+      for (int m = 0; m < 2 * AttnRegs<D>::NV; ++m)
+        rg.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff[m] + tk, 0, 0));
     }
 #pragma unroll
-    for (int i = 0; i < AP; ++i) {
-      const int rr = min(16 * i + r16, mrow_clamp);
-      rg.mw[i] = *reinterpret_cast<const uint2*>(mq + (size_t)rr * a.mask_ld + J0 / 32);
-    }
+    for (int i = 0; i < AP; ++i)
+      rg.mw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(mres, moff_b[i] + (uint32_t)kt * 8u, 0, 0));
   };
-  // S^T of query tile i against the staged keys: sv[c][r] = q . k for the
-  // query T0 + 16 i + r16 and the key J0 + 16 c + 4 g + r, or -inf where the
-  // key is not selected (or, on tiles that reach past the block's first
-  // query, not causal)
   // Q^T operands, held for the whole block: lane holds Q[T0 + 16 i + r16][32 s + 8 g .. + 7]
   bf16x8 qreg[AP][D / 32];
 #pragma unroll
@@ -203,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       __syncthreads();
       attn_stage<D>(rg, sm, true);
       __syncthreads();
-      if (kt + 1 < nkt) prefetch(J0 + AK, true);
+      if (kt + 1 < nkt) prefetch(kt + 1, true);
       uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
@@ -218,17 +234,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
           m = fmaxf(m, __shfl_xor(m, 32, WAVE));
           moff[i] = m * scale;
         }
-        // every score is exponentiated; unselected ones (which may be far
-        // above the offset and even overflow) are cleared in the packed bf16
+        // exponent s scale - offset, replaced by -inf (exp2 -> 0) where the
+        // key is not selected
         uint32_t pk[4][2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c) {
+          float x[4];
 #pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            const uint32_t keep = (bitmask(sel[c], r) & 0x0000ffffu) | (bitmask(sel[c], r + 1) & 0xffff0000u);
-            pk[c][r / 2] = keep & cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(st[c][r], scale, -moff[i])),
-                                              __builtin_amdgcn_exp2f(fmaf(st[c][r + 1], scale, -moff[i])));
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t m = bitmask(sel[c], r);
+            x[r] = __uint_as_float((__float_as_uint(fmaf(st[c][r], scale, -moff[i])) & m) | (0xff800000u & ~m));
           }
+#pragma unroll
+          for (int r = 0; r < 4; r += 2)
+            pk[c][r / 2] = cvt_pk_bf16(__builtin_amdgcn_exp2f(x[r]), __builtin_amdgcn_exp2f(x[r + 1]));
+        }
         // contraction step s covers key blocks 2 s and 2 s + 1
 #pragma unroll
         for (int s = 0; s < 2; ++s) pf[i][s] = make_uint4(pk[2 * s][0], pk[2 * s][1], pk[2 * s + 1][0], pk[2 * s + 1][1]);
@@ -240,9 +260,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.vt[16 * q + r16][32 * s + 4 * g]);
-          const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.vt[16 * q + r16][32 * s + 16 + 4 * g]);
-          const bf16x8 vf = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
+          const bf16x8 vf = as_bf16x8(lds_read16(&sm.vt[16 * q + r16][32 * s + 8 * g]));
 #pragma unroll
           for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf, o[i][q]);
         }
@@ -275,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       __syncthreads();  // readers of the previous tile are done
       attn_stage<D>(rg, sm, false);
       __syncthreads();
-      if (kt + 1 < nkt) prefetch(J0 + AK, false);
+      if (kt + 1 < nkt) prefetch(kt + 1, false);
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
         f32x4 st[4];
@@ -337,6 +355,9 @@ bool attn_mfma_supported(const Shape& sh) {
 int64_t attn_mask_ld(int n) { return (int64_t)((((n + 31) / 32) + 1) / 2 * 2); }
 
 hipError_t launch_attn_prefill_mfma(const AttnMaskArgs& a, hipStream_t st) {
+  // buffer resources address a sequence's K, V and mask rows with 31-bit offsets
+  if ((size_t)a.n * a.sh.H_kv * a.sh.d * 2 > 0x7fffffffu || (size_t)a.n * a.mask_ld * 4 > 0x7fffffffu)
+    return hipErrorInvalidValue;
   const int G = a.sh.H_q / a.sh.H_kv;
   const int units = (a.n + AQ - 1) / AQ * G;
   const dim3 grid((unsigned)((units + 3) / 4 * a.sh.B * a.sh.H_kv));
