@@ -161,29 +161,36 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
 #pragma unroll
     for (int s = 0; s < D / 32; ++s) qreg[i][s] = as_bf16x8(ld16(qb + (size_t)t * q_stride + 32 * s + 8 * g));
   }
-  // S^T of query tile i against the staged keys: st[c][r] = q . k for the
-  // query T0 + 16 i + r16 and the key J0 + 16 c + 4 g + r; sel[c] holds the
-  // selection bits of those keys (bit r), cut to the causal ones on tiles
-  // that reach past the block's first query
-  auto scores = [&](int i, int J0, uint2 mw, f32x4 (&st)[4], uint32_t (&sel)[4]) {
-    const bf16x8 (&qf)[D / 32] = qreg[i];
+  // S^T of every query tile i against the staged keys: st[i][c][r] = q . k
+  // for the query T0 + 16 i + r16 and the key J0 + 16 c + 4 g + r; sel[i][c]
+  // holds the selection bits of those keys (bit r), cut to the causal ones
+  // on tiles that reach past the wave's first query
+  // (every K operand read from LDS serves all AP query tiles)
+  auto scores = [&](int J0, const uint2 (&mw)[AP], f32x4 (&st)[AP][4], uint32_t (&sel)[AP][4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      st[c] = zero4();
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s)  // K operand: key 16 c + r16, dims 32 s + 8 g .. + 7
-        st[c] = mfma16(as_bf16x8(lds_read16(&sm.k[16 * c + r16][32 * s + 8 * g])), qf[s], st[c]);
+      for (int i = 0; i < AP; ++i) st[i][c] = zero4();
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) {  // K operand: key 16 c + r16, dims 32 s + 8 g .. + 7
+        const bf16x8 kf = as_bf16x8(lds_read16(&sm.k[16 * c + r16][32 * s + 8 * g]));
+#pragma unroll
+        for (int i = 0; i < AP; ++i) st[i][c] = mfma16(kf, qreg[i][s], st[i][c]);
+      }
     }
-    uint32_t wx = mw.x, wy = mw.y;
-    if (J0 + AK - 1 > T0) {
-      const int lim = T0 + 16 * i + r16 - J0;  // last key of the row inside the tile
-      wx &= lim >= 31 ? ~0u : (lim < 0 ? 0u : ((2u << lim) - 1u));
-      wy &= lim >= 63 ? ~0u : (lim < 32 ? 0u : ((2u << (lim - 32)) - 1u));
+#pragma unroll
+    for (int i = 0; i < AP; ++i) {
+      uint32_t wx = mw[i].x, wy = mw[i].y;
+      if (J0 + AK - 1 > T0) {
+        const int lim = T0 + 16 * i + r16 - J0;  // last key of the row inside the tile
+        wx &= lim >= 31 ? ~0u : (lim < 0 ? 0u : ((2u << lim) - 1u));
+        wy &= lim >= 63 ? ~0u : (lim < 32 ? 0u : ((2u << (lim - 32)) - 1u));
+      }
+      sel[i][0] = wx >> (4 * g);
+      sel[i][1] = wx >> (16 + 4 * g);
+      sel[i][2] = wy >> (4 * g);
+      sel[i][3] = wy >> (16 + 4 * g);
     }
-    sel[0] = wx >> (4 * g);
-    sel[1] = wx >> (16 + 4 * g);
-    sel[2] = wy >> (4 * g);
-    sel[3] = wy >> (16 + 4 * g);
   };
   // all-ones where bit r of w is set, else zero
   auto bitmask = [](uint32_t w, int r) -> uint32_t { return (uint32_t)__builtin_amdgcn_sbfe((int)w, r, 1); };
@@ -221,15 +228,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       __syncthreads();
       if (kt + 1 < nkt) prefetch(kt + 1, true);
       uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
+      f32x4 st[AP][4];
+      uint32_t sel[AP][4];
+      scores(J0, mw, st, sel);
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
-        f32x4 st[4];
-        uint32_t sel[4];
-        scores(i, J0, mw[i], st, sel);
         if (set_offset && kt == 0) {  // the row's offset: max over the first tile
           float m = -INFINITY;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) m = fmaxf(m, fmaxf(fmaxf(st[c][0], st[c][1]), fmaxf(st[c][2], st[c][3])));
+          for (int c = 0; c < 4; ++c) m = fmaxf(m, fmaxf(fmaxf(st[i][c][0], st[i][c][1]), fmaxf(st[i][c][2], st[i][c][3])));
           m = fmaxf(m, __shfl_xor(m, 16, WAVE));
           m = fmaxf(m, __shfl_xor(m, 32, WAVE));
           moff[i] = m * scale;
@@ -242,8 +249,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
           float x[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t m = bitmask(sel[c], r);
-            x[r] = __uint_as_float((__float_as_uint(fmaf(st[c][r], scale, -moff[i])) & m) | (0xff800000u & ~m));
+            const uint32_t m = bitmask(sel[i][c], r);
+            x[r] = __uint_as_float((__float_as_uint(fmaf(st[i][c][r], scale, -moff[i])) & m) | (0xff800000u & ~m));
           }
 #pragma unroll
           for (int r = 0; r < 4; r += 2)
@@ -294,18 +301,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       attn_stage<D>(rg, sm, false);
       __syncthreads();
       if (kt + 1 < nkt) prefetch(kt + 1, false);
+      f32x4 st[AP][4];
+      uint32_t sel[AP][4];
+      scores(J0, mw, st, sel);
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
-        f32x4 st[4];
-        uint32_t sel[4];
-        scores(i, J0, mw[i], st, sel);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {  // the score where selected, -inf elsewhere
-            const uint32_t m = bitmask(sel[c], r);
-            v[r] = __uint_as_float((__float_as_uint(st[c][r]) & m) | (0xff800000u & ~m));
+            const uint32_t m = bitmask(sel[i][c], r);
+            v[r] = __uint_as_float((__float_as_uint(st[i][c][r]) & m) | (0xff800000u & ~m));
           }
           mx[i] = fmaxf(mx[i], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
         }
