@@ -33,18 +33,18 @@ constexpr int AQ = 16 * AP;
 // operand read free of bank conflicts.  The key columns of the V tile are
 // stored permuted within each 32-key half (vt_col), so that the eight keys
 // one lane contributes to a P V step are adjacent.
+// Two buffers: tile kt is read from buffer kt & 1 while tile kt + 1 is
+// staged into the other one.
 template <int D>
 struct AttnShared {
-  bf16_t k[AK][D + 8];
-  bf16_t vt[D + 16][AK + 8];  // rows D .. D + 15 hold ones: P V also yields the row sums
+  bf16_t k[2][AK][D + 8];
+  bf16_t vt[2][D + 16][AK + 8];  // rows D .. D + 15 hold ones: P V also yields the row sums
 };
 
 // Column of key j in the V tile: key 32 s + 16 h + 4 g + r sits at
 // 32 s + 8 g + 4 h + r, matching the P operand, whose lane group g holds keys
 // 32 s + 4 g + r and 32 s + 16 + 4 g + r of contraction step s.
 __device__ __forceinline__ int vt_col(int j) { return (j & 32) | ((j & 12) << 1) | ((j & 16) >> 2) | (j & 3); }
-
-
 
 template <int D>
 struct AttnRegs {
@@ -55,12 +55,12 @@ struct AttnRegs {
 };
 
 template <int D>
-__device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& sm, bool with_v) {
+__device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& sm, int buf, bool with_v) {
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
 #pragma unroll
   for (int m = 0; m < AttnRegs<D>::NK; ++m) {
     const int e = tid + 256 * m;
-    *reinterpret_cast<uint4*>(&sm.k[e / (D / 8)][8 * (e % (D / 8))]) = r.k[m];
+    *reinterpret_cast<uint4*>(&sm.k[buf][e / (D / 8)][8 * (e % (D / 8))]) = r.k[m];
   }
   if (!with_v) return;
 #pragma unroll
@@ -71,8 +71,8 @@ __device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& 
     const int col = vt_col(2 * tau);  // keys 2 tau and 2 tau + 1 stay adjacent
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<uint32_t*>(&sm.vt[8 * c8 + 2 * e][col]) = __builtin_amdgcn_perm(b[e], a[e], 0x05040100u);
-      *reinterpret_cast<uint32_t*>(&sm.vt[8 * c8 + 2 * e + 1][col]) = __builtin_amdgcn_perm(b[e], a[e], 0x07060302u);
+      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * c8 + 2 * e][col]) = __builtin_amdgcn_perm(b[e], a[e], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * c8 + 2 * e + 1][col]) = __builtin_amdgcn_perm(b[e], a[e], 0x07060302u);
     }
   }
 }
@@ -166,14 +166,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   // holds the selection bits of those keys (bit r), cut to the causal ones
   // on tiles that reach past the wave's first query
   // (every K operand read from LDS serves all AP query tiles)
-  auto scores = [&](int J0, const uint2 (&mw)[AP], f32x4 (&st)[AP][4], uint32_t (&sel)[AP][4]) {
+  auto scores = [&](int buf, int J0, const uint2 (&mw)[AP], f32x4 (&st)[AP][4], uint32_t (&sel)[AP][4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
       for (int i = 0; i < AP; ++i) st[i][c] = zero4();
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {  // K operand: key 16 c + r16, dims 32 s + 8 g .. + 7
-        const bf16x8 kf = as_bf16x8(lds_read16(&sm.k[16 * c + r16][32 * s + 8 * g]));
+        const bf16x8 kf = as_bf16x8(lds_read16(&sm.k[buf][16 * c + r16][32 * s + 8 * g]));
 #pragma unroll
         for (int i = 0; i < AP; ++i) st[i][c] = mfma16(kf, qreg[i][s], st[i][c]);
       }
@@ -195,8 +195,33 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   // all-ones where bit r of w is set, else zero
   auto bitmask = [](uint32_t w, int r) -> uint32_t { return (uint32_t)__builtin_amdgcn_sbfe((int)w, r, 1); };
 
-  // the ones rows of the V tile (written once; staging never touches them)
-  for (int e = tid; e < 16 * (AK + 8); e += 256) sm.vt[D + e / (AK + 8)][e % (AK + 8)] = (bf16_t)0x3f80;
+  // the ones rows of both V buffers (written once; staging never touches them)
+  for (int e = tid; e < 2 * 16 * (AK + 8); e += 256)
+    sm.vt[e / (16 * (AK + 8))][D + (e / (AK + 8)) % 16][e % (AK + 8)] = (bf16_t)0x3f80;
+
+  // Walks the key tiles: body(kt, buf, mw) computes tile kt from LDS buffer
+  // buf with the mask words mw of the wave's rows, while tile kt + 1 (loaded
+  // into registers one tile earlier) is staged into the other buffer; one
+  // barrier per tile.
+  auto walk = [&](bool with_v, auto&& body) {
+    uint2 mw[AP];
+    prefetch(0, with_v);
+    attn_stage<D>(rg, sm, 0, with_v);
+#pragma unroll
+    for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
+    __syncthreads();
+    if (nkt > 1) prefetch(1, with_v);
+    for (int kt = 0; kt < nkt; ++kt) {
+      body(kt, kt & 1, mw);
+      if (kt + 1 < nkt) {
+        attn_stage<D>(rg, sm, (kt + 1) & 1, with_v);
+#pragma unroll
+        for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
+      }
+      __syncthreads();
+      if (kt + 2 < nkt) prefetch(kt + 2, with_v);
+    }
+  };
   constexpr int NQ = D / 16 + 1;  // output column blocks, the last one accumulates the row sums
 
   // Every row accumulates O = sum_k p_k v_k and l = sum_k p_k with
@@ -217,20 +242,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
     for (int i = 0; i < AP; ++i)
 #pragma unroll
       for (int q = 0; q < NQ; ++q) o[i][q] = zero4();
-    prefetch(0, true);
-    for (int kt = 0; kt < nkt; ++kt) {
+    walk(true, [&](int kt, int buf, const uint2 (&mw)[AP]) {
       const int J0 = kt * AK;
-      uint2 mw[AP];
-#pragma unroll
-      for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
-      __syncthreads();
-      attn_stage<D>(rg, sm, true);
-      __syncthreads();
-      if (kt + 1 < nkt) prefetch(kt + 1, true);
       uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
       f32x4 st[AP][4];
       uint32_t sel[AP][4];
-      scores(J0, mw, st, sel);
+      scores(buf, J0, mw, st, sel);
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
         if (set_offset && kt == 0) {  // the row's offset: max over the first tile
@@ -267,11 +284,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 vf = as_bf16x8(lds_read16(&sm.vt[16 * q + r16][32 * s + 8 * g]));
+          const bf16x8 vf = as_bf16x8(lds_read16(&sm.vt[buf][16 * q + r16][32 * s + 8 * g]));
 #pragma unroll
           for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf, o[i][q]);
         }
-    }
+    });
   };
 
   accumulate(true);
@@ -291,19 +308,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
     float mx[AP];
 #pragma unroll
     for (int i = 0; i < AP; ++i) mx[i] = -INFINITY;
-    prefetch(0, false);
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int J0 = kt * AK;
-      uint2 mw[AP];
-#pragma unroll
-      for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
-      __syncthreads();  // readers of the previous tile are done
-      attn_stage<D>(rg, sm, false);
-      __syncthreads();
-      if (kt + 1 < nkt) prefetch(kt + 1, false);
+    walk(false, [&](int kt, int buf, const uint2 (&mw)[AP]) {
       f32x4 st[AP][4];
       uint32_t sel[AP][4];
-      scores(J0, mw, st, sel);
+      scores(buf, kt * AK, mw, st, sel);
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
 #pragma unroll
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
+    });
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
       float m = fmaxf(mx[i], __shfl_xor(mx[i], 16, WAVE));
