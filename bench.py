@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-dense", action="store_true", help="skip the dense-attention decode baseline")
     p.add_argument("--no-batched", action="store_true", help="skip the batch-32 ragged decode leg")
+    p.add_argument("--batched-only", action="store_true", help="only the batch-32 ragged decode leg (profiling)")
     p.add_argument("--batched-steps", type=int, default=64)
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
@@ -108,7 +109,7 @@ SELECT_OPS_PER_KEY = 8
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 
-def kernel_roofline(name, avg_ms, work, bound):
+def kernel_roofline(name, avg_ms, work, bound, traffic_key=None):
     """Roofline entry of one kernel: algorithmic work per launch over its
     average launch duration against the published (or derived) peak."""
     if bound == "hbm":
@@ -121,11 +122,11 @@ def kernel_roofline(name, avg_ms, work, bound):
         achieved = work / (avg_ms * 1e-3) / 1e12
         peak, unit = ALU_PEAK_TOPS, "TOP/s"
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 4), "peak": round(peak, 1),
-            "unit": unit, "frac": round(achieved / peak, 5), "traffic": load_traffic(name),
+            "unit": unit, "frac": round(achieved / peak, 5), "traffic": load_traffic(traffic_key or name),
             "algorithmic_work_per_launch": work, "avg_launch_us": round(avg_ms * 1e3, 3)}
 
 
-def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense):
+def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, traffic_prefix=""):
     """Graph-replayed decode steps of one workload over nbuf buffer sets:
     step time, per-kernel durations and rooflines, the dense baseline."""
     from lisa_inputs import decode_inputs
@@ -246,7 +247,9 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense):
             12: (attention_bytes(cfg, lens, M, B) + 4 * int(lens.sum()), "hbm"),
             2: (attention_bytes(cfg, lens, M, B), "hbm"),
             8: (combine_bytes(cfg, B), "hbm")}
-    roofs = {Lb.lisa_kernel_name(k): kernel_roofline(Lb.lisa_kernel_name(k), kt[k], *work[k]) for k in dec_kids}
+    roofs = {Lb.lisa_kernel_name(k): kernel_roofline(Lb.lisa_kernel_name(k), kt[k], *work[k],
+                                                     traffic_key=traffic_prefix + Lb.lisa_kernel_name(k))
+             for k in dec_kids}
     roof = roofs[Lb.lisa_kernel_name(dom)]
     step_bytes = decode_bytes(cfg, lens, M, B)
     extra = {
@@ -301,6 +304,12 @@ def main():
     if args.prefill_only:
         print(json.dumps(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs)), flush=True)
         return
+    if args.batched_only:
+        cb = CONFIGS[2]
+        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense, "batched:")
+        db.pop("inp")
+        print(json.dumps({k: v for k, v in db.items()}), flush=True)
+        return
     d = bench_decode(args, torch, Lb, cfg, cid, args.nbuf, args.steps, args.warmup, not args.no_dense)
     inp = d.pop("inp")
     ms_step, done, roof = d.pop("ms_step"), d.pop("steps"), d.pop("roofline")
@@ -309,7 +318,7 @@ def main():
     extra["pages_context"] = "about 50% end-to-end inference speedup at 16K context (other hardware, whole model)"
     if not args.no_batched:
         cb = CONFIGS[2]
-        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense)
+        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense, "batched:")
         db.pop("inp")
         bms = db.pop("ms_step")
         db.pop("steps")
@@ -414,7 +423,8 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     r0 = min(M, n)
     scored_pairs = (n * (n + 1) - r0 * (r0 + 1)) // 2
     attn_pairs = sum(min(M, t + 1) for t in range(n))
-    lin_bytes = 3 * n * cfg.H_L * cfg.d * 2 + 2 * 4 * cfg.H_L * cfg.d * (cfg.d + 1)
+    # q, k, v read once, fp32 outputs written once, the state read and written
+    lin_bytes = 3 * n * cfg.H_L * cfg.d * 2 + n * cfg.H_L * cfg.d * 4 + 2 * 4 * cfg.H_L * cfg.d * (cfg.d + 1)
     pwork = {
         "prefill_index_scores": (2 * cfg.H_I * cfg.d_I * scored_pairs, "mfma"),
         "prefill_linear": (lin_bytes, "hbm"),

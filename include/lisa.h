@@ -216,9 +216,12 @@ const char* lisa_last_error(void);
  * stops, n) makes the next n launches of kernel k, on the calling host
  * thread, go through hipExtLaunchKernel with the given hipEvent_t pairs, so
  * each pair brackets that kernel's own dispatch (the interval a kernel trace
- * reports, without launch gaps); lisa_timing_count() returns how many pairs
- * were used so far; lisa_timing_enable(k, NULL, NULL, 0) disables it.  Not
- * for use under stream capture.  Kernel ids are listed by lisa_kernel_name().
+ * reports, without launch gaps).  Before each such launch the library waits
+ * on the host for the stream's earlier work, so that the pair does not also
+ * cover the tail of the kernel before it.  lisa_timing_count() returns how
+ * many pairs were used so far; lisa_timing_enable(k, NULL, NULL, 0) disables
+ * it.  Not for use under stream capture.  Kernel ids are listed by
+ * lisa_kernel_name().
  */
 int lisa_timing_enable(int kernel_id, void** start_events, void** stop_events, int n);
 int lisa_timing_count(void);

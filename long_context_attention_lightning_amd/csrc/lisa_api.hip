@@ -215,6 +215,7 @@ bool timing_on(int kid) { return g_timing.kid == kid && g_timing.count < g_timin
   do {                                                                              \
     const bool timed_ = timing_on(kid);                                             \
     if (timed_) {                                                                   \
+      (void)hipStreamSynchronize(st); /* the pair times this kernel alone */        \
       next_launch_events().start = g_timing.starts[g_timing.count];                 \
       next_launch_events().stop = g_timing.stops[g_timing.count];                   \
     }                                                                               \
