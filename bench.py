@@ -432,7 +432,7 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
         "prefill_gate": (n * cfg.hidden * 2 + cfg.hidden * cfg.H_q * 2 + n * cfg.H_q * 4, "hbm"),
         "topm_select": (SELECT_OPS_PER_KEY * scored_pairs, "alu"),
     }
-    proofs = {k: kernel_roofline(k, kern[k] * 1e-3, *pwork[k]) for k in pwork if kern.get(k)}
+    proofs = {k: kernel_roofline(k, kern[k] * 1e-3, *pwork[k], traffic_key="prefill:" + k) for k in pwork if kern.get(k)}
     # the linear branch as a whole (segment sums + prefix + chunked outputs)
     lin_us = sum(kern.get(k, 0.0) for k in ("prefill_linear_sums", "prefill_linear_prefix", "prefill_linear"))
     lin_flops = 2 * cfg.H_L * (n * cfg.d * 64 + 2 * n * cfg.d * cfg.d)  # causal half of A, A V, phi(Q) S, phi(K)^T V
