@@ -247,7 +247,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
       f32x4 st[AP][4];
       uint32_t sel[AP][4];
+      // MFMA phases at raised wave priority, so that the other wave on the
+      // SIMD fills the matrix-core time with its softmax arithmetic
+      __builtin_amdgcn_s_setprio(1);
       scores(buf, J0, mw, st, sel);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
         if (set_offset && kt == 0) {  // the row's offset: max over the first tile
@@ -278,6 +282,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
         for (int s = 0; s < 2; ++s) pf[i][s] = make_uint4(pk[2 * s][0], pk[2 * s][1], pk[2 * s + 1][0], pk[2 * s + 1][1]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(1);
       // O += P V over the output blocks and the ones block: V operand of block
       // q, step s: keys {32 s + 4 g .. +3, 32 s + 16 + 4 g .. +3}
 #pragma unroll
@@ -288,6 +293,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
 #pragma unroll
           for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf, o[i][q]);
         }
+      __builtin_amdgcn_s_setprio(0);
     });
   };
 
