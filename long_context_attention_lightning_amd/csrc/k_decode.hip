@@ -291,7 +291,8 @@ size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit) {
 template <typename T, int D, int GT>
 __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
   constexpr bool MF = sizeof(T) == 2;  // bf16: MFMA split attention
-  using SharedT = typename std::conditional<MF, AttnMfmaShared<D, GT>, AttnMergeShared<AT_THREADS / WAVE, GT, D>>::type;
+  using SharedT = typename std::conditional<MF, AttnMfmaShared<D, GT, AT_THREADS / WAVE>,
+                                            AttnMergeShared<AT_THREADS / WAVE, GT, D>>::type;
   __shared__ SharedT ms;
   const Shape& sh = a.sh;
   int blk = blockIdx.x;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
   const int i1 = min(m, i0 + a.split_len);
   const int32_t* irow = a.dense ? nullptr : a.idx + (size_t)r * a.idx_ld;
   auto pos_of = [irow](int i) { return irow ? irow[i] : i; };
-  if constexpr (MF) attend_split_mfma<D, GT, AT_THREADS>(a, r, g, s, len, i0, i1, pos_of, ms);
+  if constexpr (MF) attend_split_mfma<D, GT, AT_THREADS, AT_THREADS / WAVE>(a, r, g, s, len, i0, i1, pos_of, ms);
   else attend_split<T, D, GT, AT_THREADS, AT_RP>(a, r, g, s, len, i0, i1, pos_of, ms);
 }
 

@@ -32,7 +32,8 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, Select
     KeyStore<FS_THREADS, ITEMS, true> ks;
   };
   constexpr bool MF = sizeof(T) == 2;  // bf16: MFMA split attention
-  using AttT = typename std::conditional<MF, AttnMfmaShared<D, GT>, AttnMergeShared<NW, GT, D>>::type;
+  // splits of at most FS_MAX_SPLIT entries: two attending waves of 32
+  using AttT = typename std::conditional<MF, AttnMfmaShared<D, GT, FS_MAX_SPLIT / 32>, AttnMergeShared<NW, GT, D>>::type;
   union Shared {
     SelPart sel;
     AttT att;  // used only after the selection is complete
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, Select
   }
   __syncthreads();
   auto pos_of = [&](int i) { return plist[i - i0]; };
-  if constexpr (MF) attend_split_mfma<D, GT, FS_THREADS>(a, b, g, s, len, i0, i1, pos_of, u.att);
+  if constexpr (MF) attend_split_mfma<D, GT, FS_THREADS, FS_MAX_SPLIT / 32>(a, b, g, s, len, i0, i1, pos_of, u.att);
   else attend_split<T, D, GT, FS_THREADS, 2>(a, b, g, s, len, i0, i1, pos_of, u.att);
 }
 

@@ -107,6 +107,9 @@ int64_t decode_scores_ld(const Shape& sh) { return (int64_t)align_up((size_t)sh.
 void decode_split(const Shape& sh, int positions, int& nsplit, int& split_len) {
   int sl = 64;
   while ((positions + sl - 1) / sl > 32) sl *= 2;
+  // with many blocks, 128 positions per split keep all four waves of a
+  // gather block busy (32 entries each per round)
+  if ((size_t)sh.B * sh.H_kv * ((positions + sl - 1) / sl) > 1024 && sl < 128) sl = 128;
   while ((size_t)sh.B * sh.H_kv * ((positions + sl - 1) / sl) > 4096 && sl < positions) sl *= 2;
   split_len = sl;
   nsplit = (positions + sl - 1) / sl;

@@ -224,17 +224,19 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int r, int g, in
 // V) and V transposed through LDS as packed position pairs.  The other waves
 // only join the block's barriers.
 // ---------------------------------------------------------------------------
-constexpr int AM_WAVES = 2;
-
-template <int D, int GT>
+// NWA waves of the block gather and attend, 32 selected entries each per
+// round, with their own online-softmax state; the epilogue merges them.
+template <int D, int GT, int NWA>
 struct AttnMfmaShared {
-  bf16_t vt[AM_WAVES][D][32 + 8];
-  AttnMergeShared<AM_WAVES, GT, D> ms;
+  union {  // the merge state is written once no wave reads its V tile any more
+    bf16_t vt[NWA][D][32 + 8];
+    AttnMergeShared<NWA, GT, D> ms;
+  };
 };
 
-template <int D, int GT, int THREADS, typename PosFn>
+template <int D, int GT, int THREADS, int NWA, typename PosFn>
 __device__ __forceinline__ void attend_split_mfma(const AttnArgs& a, int r, int g, int s, int len, int i0, int i1,
-                                                  PosFn pos_of, AttnMfmaShared<D, GT>& sm) {
+                                                  PosFn pos_of, AttnMfmaShared<D, GT, NWA>& sm) {
   static_assert(GT <= 8, "query heads per KV head");
   const Shape& sh = a.sh;
   const int G = sh.H_q / sh.H_kv;
@@ -242,7 +244,11 @@ __device__ __forceinline__ void attend_split_mfma(const AttnArgs& a, int r, int 
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int r16 = lane & 15, g4 = lane >> 4;
   const float scale = 1.4426950408889634f * rsqrtf((float)D);
-  if (wave < AM_WAVES) {
+  float mrun = -INFINITY, lrun = 0.f;  // of query head r16
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int q = 0; q < D / 16; ++q) o[q] = zero4();
+  if (wave < NWA) {
     const size_t row_stride = (size_t)sh.H_kv * D;
     const bf16_t* kb = (const bf16_t*)a.k_cache + (size_t)b * sh.cap * row_stride + (size_t)g * D;
     const bf16_t* vb = (const bf16_t*)a.v_cache + (size_t)b * sh.cap * row_stride + (size_t)g * D;
@@ -256,12 +262,8 @@ __device__ __forceinline__ void attend_split_mfma(const AttnArgs& a, int r, int 
         qf[k] = as_bf16x8(r16 < G ? v : make_uint4(0u, 0u, 0u, 0u));
       }
     }
-    float mrun = -INFINITY, lrun = 0.f;  // of query head r16
-    f32x4 o[D / 16];
-#pragma unroll
-    for (int q = 0; q < D / 16; ++q) o[q] = zero4();
     bf16_t(*vt)[32 + 8] = sm.vt[wave];
-    for (int c0 = i0 + 32 * wave; c0 < i1; c0 += 64) {
+    for (int c0 = i0 + 32 * wave; c0 < i1; c0 += 32 * NWA) {
       // gathered rows: K of entries c0 + 16 c + r16; V of entry pairs c0 + 2 r16 + u
       int pk[2], pv[2];
 #pragma unroll
@@ -338,6 +340,9 @@ __device__ __forceinline__ void attend_split_mfma(const AttnArgs& a, int r, int 
     }
     lrun += __shfl_xor(lrun, 16, WAVE);
     lrun += __shfl_xor(lrun, 32, WAVE);
+  }
+  __syncthreads();  // every wave is done with its V tile
+  if (wave < NWA) {
     if (g4 == 0 && r16 < GT) {
       sm.ms.wm[wave][r16] = mrun;
       sm.ms.wl[wave][r16] = lrun;
@@ -352,7 +357,7 @@ __device__ __forceinline__ void attend_split_mfma(const AttnArgs& a, int r, int 
     }
   }
   __syncthreads();
-  attend_epilogue<bf16_t, D, GT, AM_WAVES, THREADS>(a, r, g, s, sm.ms);
+  attend_epilogue<bf16_t, D, GT, NWA, THREADS>(a, r, g, s, sm.ms);
 }
 
 }  // namespace lisa
