@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--no-batched", action="store_true", help="skip the batch-32 ragged decode leg")
     p.add_argument("--batched-only", action="store_true", help="only the batch-32 ragged decode leg (profiling)")
     p.add_argument("--batched-steps", type=int, default=64)
+    p.add_argument("--no-sweep", action="store_true", help="skip the batch-8 32K M-sweep decode leg")
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
     p.add_argument("--prefill-iters", type=int, default=5)
@@ -190,15 +191,20 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
         return reps * len(sets)
 
     def time_graph(g):
+        """Mean step time over the timed replays, and the per-replay step
+        times (an event pair around every replay) for the spread."""
         run(g, warmup)
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        n = run(g, steps)
-        t1.record()
+        reps = max(1, (steps + len(sets) - 1) // len(sets))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            g.replay()
+            ev[i + 1].record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / n, n
+        per = [ev[i].elapsed_time(ev[i + 1]) / len(sets) for i in range(reps)]
+        time_graph.spread = per
+        return ev[0].elapsed_time(ev[-1]) / (reps * len(sets)), reps * len(sets)
 
     def kernel_times(fn, kids):
         """Average duration of each kernel from HIP events recorded by the
@@ -222,6 +228,7 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
     # ---------------- timed region: graph replays of whole decode steps
     g_main = capture(step)
     ms_step, done = time_graph(g_main)
+    spread = np.array(time_graph.spread) * 1e3
     print(f"# timed {done} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
     # ---------------- per-kernel durations (HIP events on the launch stream)
     dec_kids = (0, 1, 12, 2, 8)
@@ -254,6 +261,9 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
     step_bytes = decode_bytes(cfg, lens, M, B)
     extra = {
         "us_per_step": round(ms_step * 1e3, 3),
+        "us_per_step_median_p10_p90": [round(float(np.median(spread)), 3), round(float(np.percentile(spread, 10)), 3),
+                                       round(float(np.percentile(spread, 90)), 3)],
+        "step_spread_note": f"per graph replay of {len(sets)} steps, {len(spread)} replays",
         "kernel_us": {k: round(v * 1e3, 3) for k, v in per_kernel_ms.items()},
         "kernel_timing": "hipExtLaunchKernel start/stop events on each kernel's dispatch, eager steps "
                          "over the same buffer sets right after the timed graph replays",
@@ -326,6 +336,26 @@ def main():
                                        tok_s=round(cb.B / (bms * 1e-3), 1), **db)
         del db
         torch.cuda.empty_cache()
+    if not args.no_sweep:
+        c4 = CONFIGS[4]
+        sweep = {}
+        for Mv in c4.M_sweep:
+            cm = c4.replace(M=Mv)
+            dm = bench_decode(args, torch, Lb, cm, 4, 2, 32, 4, Mv == c4.M_sweep[0] and not args.no_dense,
+                              f"sweep{Mv}:")
+            dm.pop("inp")
+            mms = dm.pop("ms_step")
+            dm.pop("steps")
+            keep = ("us_per_step", "us_per_step_median_p10_p90", "kernel_us", "step_algorithmic_bytes",
+                    "step_hbm_roofline_frac", "dense_decode_us_per_step", "speedup_vs_dense_decode")
+            sweep[str(Mv)] = dict(tok_s=round(cm.B / (mms * 1e-3), 1), **{k: v for k, v in dm.items() if k in keep})
+            torch.cuda.empty_cache()
+        dense_us = sweep[str(c4.M_sweep[0])].get("dense_decode_us_per_step")
+        if dense_us:
+            for v in sweep.values():
+                v["speedup_vs_dense_decode"] = round(dense_us / v["us_per_step"], 3)
+        extra["m_sweep_decode"] = dict(workload=c4.name, batch=c4.B, context=c4.L, dense_decode_us_per_step=dense_us,
+                                       **sweep)
 
     if not args.no_prefill:
         extra.update(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs))
@@ -438,12 +468,41 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     lin_flops = 2 * cfg.H_L * (n * cfg.d * 64 + 2 * n * cfg.d * cfg.d)  # causal half of A, A V, phi(Q) S, phi(K)^T V
     proofs["prefill_linear_branch"] = kernel_roofline("prefill_linear_branch", lin_us * 1e-3, lin_bytes, "hbm")
     proofs["prefill_linear_branch_mfma"] = kernel_roofline("prefill_linear_branch", lin_us * 1e-3, lin_flops, "mfma")
+    dense = dense_prefill_baseline(torch, t["q"], t["k"], t["v"], cfg, n, args.prefill_iters)
     res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
+           "dense_causal_prefill_attention_ms": dense,
            "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
            "prefill_kernel_roofline": proofs}
     del ws, t, out
     torch.cuda.empty_cache()
     return res
+
+
+def dense_prefill_baseline(torch, q, k, v, cfg, n, iters):
+    """Dense causal attention over the same prefill q, k, v with torch's
+    scaled_dot_product_attention (a library baseline on the same GPU; the
+    fused flash / memory-efficient backends only, never the math path)."""
+    try:
+        import torch.nn.functional as F
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        G = cfg.H_q // cfg.H_kv
+        qh = q.view(1, n, cfg.H_q, cfg.d).transpose(1, 2).contiguous()
+        kh = k.view(1, n, cfg.H_kv, cfg.d).repeat_interleave(G, dim=2).transpose(1, 2).contiguous()
+        vh = v.view(1, n, cfg.H_kv, cfg.d).repeat_interleave(G, dim=2).transpose(1, 2).contiguous()
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            F.scaled_dot_product_attention(qh, kh, vh, is_causal=True)
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(iters):
+                F.scaled_dot_product_attention(qh, kh, vh, is_causal=True)
+            t1.record()
+            torch.cuda.synchronize()
+        return {"ms": round(t0.elapsed_time(t1) / iters, 3), "what": "torch SDPA (flash/efficient backend), causal, "
+                "K/V repeated to the query heads, attention only (no indexer, select, linear branch or gate)"}
+    except Exception as e:  # no fused backend on this build: not reported
+        return {"ms": None, "error": str(e)[:200]}
 
 
 def cpu_baseline(args, inp, M):
@@ -464,9 +523,24 @@ def cpu_baseline(args, inp, M):
             break
     dt = time.perf_counter() - t0
     B = len(inp["seq_lens"])
-    return {"value": round(n * B / dt, 3), "unit": "tok/s", "cores": blas or cores,
-            "kind": "oracle", "sample": f"{n} decode steps of the same workload (fp64 NumPy), {dt:.1f} s",
-            "affinity_cores": cores}
+    res = {"value": round(n * B / dt, 3), "unit": "tok/s", "cores": blas or cores,
+           "kind": "oracle", "sample": f"{n} decode steps of the same workload (fp64 NumPy), {dt:.1f} s",
+           "affinity_cores": cores}
+    try:  # the same oracle on one BLAS thread
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1 = 0
+            t1 = time.perf_counter()
+            while True:
+                oracle.decode_step(inp, M)
+                n1 += 1
+                if time.perf_counter() - t1 > args.cpu_seconds / 3:
+                    break
+            d1 = time.perf_counter() - t1
+        res["single_thread"] = {"value": round(n1 * B / d1, 3), "unit": "tok/s", "sample": f"{n1} steps, {d1:.1f} s"}
+    except Exception as e:  # threadpoolctl missing: report without it
+        res["single_thread"] = {"value": None, "error": str(e)[:200]}
+    return res
 
 
 if __name__ == "__main__":
