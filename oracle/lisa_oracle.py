@@ -30,6 +30,10 @@ function that uses them:
   ``phi(q_t) S_t / (phi(q_t) . z_t)`` ([LISA] §3.1 Linear Attention; §3.3
   Eqs. 3-4, read as inclusive of the current token).  With
   ``normalized=False`` the output is ``phi(q_t) S_t`` (Eq. 4 literally).
+* Sliding-window mode ([LISA] §3.2 Stage 1, Eq. 1: a fixed budget of the M
+  most recent tokens): query t attends to positions max(0, t+1-M)..t and no
+  indexer runs.  With every indexer score equal this is exactly what top-M
+  selects (ties go to the larger position).
 * Gate ``g = sigmoid(x . W_g[:, h])``, one scalar per token and query head,
   and ``out = g * O_sparse + (1-g) * O_linear`` ([LISA] §3.2 Eq. 1 and §3.3
   Eq. 5; the gate weights the sparse branch here, which is Eq. 1 with W_g
@@ -44,7 +48,7 @@ import numpy as np
 __all__ = [
     "phi", "index_scores", "select_topm", "sparse_attention", "gate",
     "linear_recurrent", "linear_rows", "linear_chunked", "linear_state_update",
-    "prefill", "prefill_rows", "decode_step", "dense_decode",
+    "prefill", "prefill_rows", "decode_step", "dense_decode", "window_positions",
 ]
 
 
@@ -240,6 +244,12 @@ def linear_state_update(k_lin, v_lin, S0, z0):
 # ----------------------------------------------------------------------------
 # whole layer
 # ----------------------------------------------------------------------------
+def window_positions(t: int, M: int) -> np.ndarray:
+    """The sliding window of query t: the min(M, t+1) positions ending at t,
+    ascending ([LISA] §3.2 Stage 1, the fixed-budget window of Eq. 1)."""
+    return np.arange(max(0, t + 1 - M), t + 1, dtype=np.int64)
+
+
 def _row_select(q_idx_t, k_idx, w_idx, t: int, M: int, scores_dtype=None):
     s = index_scores(q_idx_t, k_idx[: t + 1], w_idx)
     if scores_dtype is not None:
@@ -249,7 +259,7 @@ def _row_select(q_idx_t, k_idx, w_idx, t: int, M: int, scores_dtype=None):
 
 def prefill_rows(inp: Dict[str, np.ndarray], M: int, rows: Sequence[int],
                  b: int = 0, normalized: bool = True,
-                 select_on=None) -> Dict[str, object]:
+                 select_on=None, window: bool = False) -> Dict[str, object]:
     """Outputs of chosen query rows of a causal prefill of sequence ``b``.
 
     ``inp`` holds the arrays of a prefill input set (shapes [B, n, ...]).
@@ -266,7 +276,10 @@ def prefill_rows(inp: Dict[str, np.ndarray], M: int, rows: Sequence[int],
     g = gate(inp["x"][b][rows], inp["w_gate"])      # [r, H_q]
     out, idx, sc = {}, {}, {}
     for i, t in enumerate(rows):
-        P, s = _row_select(q_idx[t], k_idx, w_idx, t, M, select_on)
+        if window:
+            P, s = window_positions(t, M), None
+        else:
+            P, s = _row_select(q_idx[t], k_idx, w_idx, t, M, select_on)
         o_s = sparse_attention(q[t], K, V, P)
         o_l = lin[t]
         out[t] = g[i][:, None] * o_s + (1.0 - g[i][:, None]) * o_l
@@ -276,7 +289,7 @@ def prefill_rows(inp: Dict[str, np.ndarray], M: int, rows: Sequence[int],
 
 
 def prefill(inp: Dict[str, np.ndarray], M: int, normalized: bool = True,
-            select_on=None) -> Dict[str, object]:
+            select_on=None, window: bool = False) -> Dict[str, object]:
     """Full causal prefill of every sequence (small sizes).
 
     Returns 'out' [B, n, H_q, d], 'idx' list (per b) of lists of arrays,
@@ -295,8 +308,11 @@ def prefill(inp: Dict[str, np.ndarray], M: int, normalized: bool = True,
         g = gate(inp["x"][b], inp["w_gate"])
         idx_b = []
         for t in range(n):
-            P, _ = _row_select(inp["q_idx"][b][t], inp["k_idx"][b], inp["w_idx"], t, M,
-                               select_on)
+            if window:
+                P = window_positions(t, M)
+            else:
+                P, _ = _row_select(inp["q_idx"][b][t], inp["k_idx"][b], inp["w_idx"], t, M,
+                                   select_on)
             o_s = sparse_attention(inp["q"][b][t], inp["k"][b], inp["v"][b], P)
             o_sp[b, t] = o_s
             idx_b.append(P)
@@ -311,7 +327,8 @@ def prefill(inp: Dict[str, np.ndarray], M: int, normalized: bool = True,
 
 
 def decode_step(inp: Dict[str, np.ndarray], M: int, normalized: bool = True,
-                select_on=None, batch: Optional[Iterable[int]] = None) -> Dict[str, object]:
+                select_on=None, batch: Optional[Iterable[int]] = None,
+                window: bool = False) -> Dict[str, object]:
     """One decode step for every sequence (or those in ``batch``).
 
     The caches hold rows 0..L_b-2; the new token's k, v, k_I become row
@@ -332,8 +349,12 @@ def decode_step(inp: Dict[str, np.ndarray], M: int, normalized: bool = True,
         V = np.array(inp["v_cache"][b, :L], dtype=np.float64)
         K[L - 1] = inp["k_new"][b]
         V[L - 1] = inp["v_new"][b]
-        s = index_scores(inp["q_idx"][b], k_idx, inp["w_idx"])
-        P = select_topm(s if select_on is None else s.astype(select_on), M)
+        if window:  # the new token's window: rows L-m .. L-1, no indexer
+            s = None
+            P = window_positions(L - 1, M)
+        else:
+            s = index_scores(inp["q_idx"][b], k_idx, inp["w_idx"])
+            P = select_topm(s if select_on is None else s.astype(select_on), M)
         o_s = sparse_attention(inp["q"][b], K, V, P)
         fk = phi(inp["k_lin"][b])
         S = _f64(inp["S0"][b]) + fk[:, :, None] * _f64(inp["v_lin"][b])[:, None, :]

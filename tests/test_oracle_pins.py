@@ -406,6 +406,64 @@ def test_decode_full_budget_equals_dense():
 
 
 # ----------------------------------------------------------------------------
+# sliding-window mode ([LISA] §3.2 Stage 1, Eq. 1: the M most recent tokens)
+# ----------------------------------------------------------------------------
+def test_window_positions_brute_force():
+    for M in (1, 2, 5, 64):
+        for t in range(0, 70):
+            want = [j for j in range(t + 1) if t - j < M]
+            assert oracle.window_positions(t, M).tolist() == want
+
+
+@pytest.mark.parametrize("M", [1, 7, 64, 300])
+def test_window_prefill_equals_topm_with_tied_scores(M):
+    """With every indexer score equal, top-M keeps the largest positions (the
+    tie rule), which is the sliding window: the windowed layer must equal the
+    indexed layer with all head weights zero."""
+    cfg = CONFIGS[0].replace(n=129, cap=129, M=M)
+    inp = prefill_inputs(cfg, 0)
+    tied = dict(inp, w_idx=np.zeros_like(inp["w_idx"]))
+    a = oracle.prefill(inp, M, window=True)
+    b = oracle.prefill(tied, M)
+    for t in range(cfg.n):
+        assert a["idx"][0][t].tolist() == b["idx"][0][t].tolist()
+    np.testing.assert_array_equal(a["out"], b["out"])
+
+
+def test_window_prefill_full_window_equals_torch_sdpa_causal():
+    """A window at least as long as the sequence is full causal attention."""
+    cfg = CONFIGS[0].replace(n=96, cap=96, M=96)
+    inp = prefill_inputs(cfg, 0)
+    inp["w_gate"] = np.zeros_like(inp["w_gate"])
+    inp["x"] = np.ones_like(inp["x"])
+    inp["w_gate"][0, :] = 300.0                   # g = 1: the sparse branch alone
+    a = oracle.prefill(inp, 96, window=True)
+    rep = cfg.H_q // cfg.H_kv
+    qt = torch.tensor(inp["q"][0], dtype=torch.float64).permute(1, 0, 2)[None]
+    kt = torch.tensor(inp["k"][0], dtype=torch.float64).permute(1, 0, 2).repeat_interleave(rep, dim=0)[None]
+    vt = torch.tensor(inp["v"][0], dtype=torch.float64).permute(1, 0, 2).repeat_interleave(rep, dim=0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(a["out"][0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_window_decode_equals_tied_topm_and_dense_when_wide():
+    cfg = CONFIGS[1].replace(B=3, L=0, L_lo=20, L_hi=90, cap=96, H_q=8, H_kv=2, H_L=8, d=16,
+                             d_I=8, hidden=32)
+    inp = decode_inputs(cfg, 1)
+    tied = dict(inp, w_idx=np.zeros_like(inp["w_idx"]))
+    for M in (1, 16, 50):
+        a = oracle.decode_step(inp, M, window=True)
+        b = oracle.decode_step(tied, M)
+        for i in range(3):
+            L = int(inp["seq_lens"][i])
+            assert a["idx"][i].tolist() == list(range(max(0, L - M), L))
+            assert a["idx"][i].tolist() == b["idx"][i].tolist()
+        np.testing.assert_array_equal(a["out"], b["out"])
+    wide = oracle.decode_step(inp, 10_000, window=True)
+    np.testing.assert_allclose(wide["o_sparse"], oracle.dense_decode(inp), rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
 # input generator
 # ----------------------------------------------------------------------------
 def test_round_bf16_matches_torch():
