@@ -70,6 +70,13 @@ extern "C" {
 
 /* lisa_shape.flags */
 #define LISA_LINEAR_UNNORMALIZED  1u   /* O_L = phi(q) S, no normaliser z */
+/* Sliding-window attention ([LISA] Section 3.2 Stage 1, Eq. 1: a fixed budget
+ * of the M most recent tokens): query t attends to positions
+ * max(0, t+1-M)..t, the indexer does not run, and the indexer arguments
+ * (q_idx, k_idx_new, k_idx_cache, w_idx) are neither read nor written and may
+ * be NULL.  idx_out, if given, receives those positions.  Decode and prefill
+ * only. */
+#define LISA_SLIDING_WINDOW       2u
 
 /* op codes for lisa_workspace_bytes() */
 #define LISA_OP_DECODE           0
@@ -98,7 +105,7 @@ typedef struct lisa_shape {
   int32_t max_len;  /* decode: upper bound of seq_lens[b]; prefill: unused (0)   */
   int32_t chunk;    /* prefill chunk of the linear scan (64; 0 selects 64)       */
   int32_t dtype;    /* LISA_F32 or LISA_BF16                                     */
-  uint32_t flags;   /* LISA_LINEAR_UNNORMALIZED or 0                             */
+  uint32_t flags;   /* LISA_LINEAR_UNNORMALIZED | LISA_SLIDING_WINDOW, or 0      */
 } lisa_shape;
 
 /*

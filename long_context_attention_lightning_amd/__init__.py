@@ -22,7 +22,7 @@ __all__ = [
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
     "lisa_linear_state_update", "lisa_dense_decode", "lisa_status_string",
     "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
-    "workspace", "LISA_F32", "LISA_BF16", "LISA_LINEAR_UNNORMALIZED",
+    "workspace", "LISA_F32", "LISA_BF16", "LISA_LINEAR_UNNORMALIZED", "LISA_SLIDING_WINDOW",
     "LISA_OP_DECODE", "LISA_OP_PREFILL", "LISA_OP_TOPK_DECODE", "LISA_OP_TOPK_PREFILL",
     "LISA_OP_LINEAR_UPDATE", "LISA_OP_DENSE_DECODE", "LISA_ROWS_DECODE", "LISA_ROWS_PREFILL",
     "EXPORTED_SYMBOLS", "LIB_PATH",
@@ -33,6 +33,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblisa.so"
 LISA_OK = 0
 LISA_F32, LISA_BF16 = 0, 1
 LISA_LINEAR_UNNORMALIZED = 1
+LISA_SLIDING_WINDOW = 2
 (LISA_OP_DECODE, LISA_OP_PREFILL, LISA_OP_TOPK_DECODE, LISA_OP_TOPK_PREFILL,
  LISA_OP_LINEAR_UPDATE, LISA_OP_DENSE_DECODE) = range(6)
 LISA_ROWS_DECODE, LISA_ROWS_PREFILL = 0, 1

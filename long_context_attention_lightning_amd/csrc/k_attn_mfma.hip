@@ -102,6 +102,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   const int T0 = (nqt - 1 - uu / G) * AQ;
   // keys up to the last row of the block's highest query tile
   const int tmax = min((nqt - (4 * kblk) / G) * AQ, n) - 1;
+  // sliding window: key tiles before the window of the block's lowest row
+  // hold no selected key
+  const int T0_low = (nqt - 1 - min(4 * kblk + 3, units - 1) / G) * AQ;
+  const int kt0 = a.window ? max(0, T0_low - sh.M + 1) / AK : 0;
 
   const size_t kv_stride = (size_t)sh.H_kv * D;
   const size_t q_stride = (size_t)sh.H_q * D;
@@ -139,6 +143,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   // next tile's K (and V) and mask words, held in registers while the
   // current tile runs
   AttnRegs<D> rg;
+#pragma unroll
+  for (int i = 0; i < AP; ++i) rg.mw[i] = make_uint2(0u, 0u);  // not loaded for a sliding window
   auto prefetch = [&](int kt, bool with_v) {
     const uint32_t tk = (uint32_t)kt * tile_kv_bytes;
 #pragma unroll
@@ -149,9 +155,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       for (int m = 0; m < 2 * AttnRegs<D>::NV; ++m)
         rg.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff[m] + tk, 0, 0));
     }
+    if (!a.window) {
 #pragma unroll
-    for (int i = 0; i < AP; ++i)
-      rg.mw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(mres, moff_b[i] + (uint32_t)kt * 8u, 0, 0));
+      for (int i = 0; i < AP; ++i)
+        rg.mw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(mres, moff_b[i] + (uint32_t)kt * 8u, 0, 0));
+    }
   };
   // Q^T operands, held for the whole block: lane holds Q[T0 + 16 i + r16][32 s + 8 g .. + 7]
   bf16x8 qreg[AP][D / 32];
@@ -181,6 +189,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
       uint32_t wx = mw[i].x, wy = mw[i].y;
+      if (a.window) {  // keys at or past the row's window start (the causal cut follows)
+        const int lo = T0 + 16 * i + r16 - sh.M + 1 - J0;
+        wx = lo <= 0 ? ~0u : (lo >= 32 ? 0u : ~((1u << lo) - 1u));
+        wy = lo <= 32 ? ~0u : (lo >= 64 ? 0u : ~((1u << (lo - 32)) - 1u));
+      }
       if (J0 + AK - 1 > T0) {
         const int lim = T0 + 16 * i + r16 - J0;  // last key of the row inside the tile
         wx &= lim >= 31 ? ~0u : (lim < 0 ? 0u : ((2u << lim) - 1u));
@@ -205,13 +218,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   // barrier per tile.
   auto walk = [&](bool with_v, auto&& body) {
     uint2 mw[AP];
-    prefetch(0, with_v);
-    attn_stage<D>(rg, sm, 0, with_v);
+    prefetch(kt0, with_v);
+    attn_stage<D>(rg, sm, kt0 & 1, with_v);
 #pragma unroll
     for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
     __syncthreads();
-    if (nkt > 1) prefetch(1, with_v);
-    for (int kt = 0; kt < nkt; ++kt) {
+    if (kt0 + 1 < nkt) prefetch(kt0 + 1, with_v);
+    for (int kt = kt0; kt < nkt; ++kt) {
       body(kt, kt & 1, mw);
       if (kt + 1 < nkt) {
         attn_stage<D>(rg, sm, (kt + 1) & 1, with_v);
@@ -254,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
-        if (set_offset && kt == 0) {  // the row's offset: max over the first tile
+        if (set_offset && kt == kt0) {  // the row's offset: max over the first tile
           float m = -INFINITY;
 #pragma unroll
           for (int c = 0; c < 4; ++c) m = fmaxf(m, fmaxf(fmaxf(st[i][c][0], st[i][c][1]), fmaxf(st[i][c][2], st[i][c][3])));

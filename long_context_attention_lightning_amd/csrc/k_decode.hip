@@ -28,6 +28,45 @@ constexpr int LIN_COLS = 32;     // columns of S per linear block
 constexpr int GATE_ROWS = 64;    // hidden rows per gate block
 
 // ---------------------------------------------------------------------------
+// cache append of the new token (row L-1): k, v, and the index key when the
+// indexer runs
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void append_row(const PhaseAArgs& a, int b, int L) {
+  constexpr int VEC = Vec<T>::N;
+  const Shape& sh = a.sh;
+  const size_t row = (size_t)b * sh.cap + (L - 1);
+  if (a.k_idx_new && a.k_idx_cache) {
+    const int E = sh.H_Ik * sh.d_I;
+    T* kic = (T*)a.k_idx_cache + row * E;
+    const T* kin = (const T*)a.k_idx_new + (size_t)b * E;
+    for (int e = threadIdx.x * VEC; e < E; e += PA_THREADS * VEC)
+      *reinterpret_cast<uint4*>(kic + e) = *reinterpret_cast<const uint4*>(kin + e);
+  }
+  const int EK = sh.H_kv * sh.d;
+  T* kcd = (T*)a.k_cache + row * EK;
+  T* vcd = (T*)a.v_cache + row * EK;
+  const T* kn = (const T*)a.k_new + (size_t)b * EK;
+  const T* vn = (const T*)a.v_new + (size_t)b * EK;
+  for (int e = threadIdx.x * VEC; e < EK; e += PA_THREADS * VEC) {
+    *reinterpret_cast<uint4*>(kcd + e) = *reinterpret_cast<const uint4*>(kn + e);
+    *reinterpret_cast<uint4*>(vcd + e) = *reinterpret_cast<const uint4*>(vn + e);
+  }
+}
+
+// Without scoring (sliding window): one block per sequence appends the new
+// token and writes the window's index list.
+template <typename T>
+__device__ __forceinline__ void append_block(const PhaseAArgs& a, int b) {
+  const int L = a.seq_lens[b];
+  if (a.append) append_row<T>(a, b, L);
+  if (a.window_idx) {
+    const int m = min(a.M, L);
+    for (int k = threadIdx.x; k < a.M; k += PA_THREADS) a.window_idx[(size_t)b * a.M + k] = k < m ? L - m + k : -1;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // indexer tile
 // ---------------------------------------------------------------------------
 template <typename T, int R>
@@ -89,22 +128,7 @@ __device__ __forceinline__ void index_tile(const PhaseAArgs& a, int b, int tile,
   }
 
   // append the new token (the tile that holds row L-1)
-  if (a.append && j0 <= L - 1 && L - 1 < j1) {
-    const size_t row = (size_t)b * sh.cap + (L - 1);
-    T* kic = (T*)a.k_idx_cache + row * E;
-    const T* kin = knew;
-    for (int e = threadIdx.x * VEC; e < E; e += PA_THREADS * VEC)
-      *reinterpret_cast<uint4*>(kic + e) = *reinterpret_cast<const uint4*>(kin + e);
-    const int EK = sh.H_kv * sh.d;
-    T* kcd = (T*)a.k_cache + row * EK;
-    T* vcd = (T*)a.v_cache + row * EK;
-    const T* kn = (const T*)a.k_new + (size_t)b * EK;
-    const T* vn = (const T*)a.v_new + (size_t)b * EK;
-    for (int e = threadIdx.x * VEC; e < EK; e += PA_THREADS * VEC) {
-      *reinterpret_cast<uint4*>(kcd + e) = *reinterpret_cast<const uint4*>(kn + e);
-      *reinterpret_cast<uint4*>(vcd + e) = *reinterpret_cast<const uint4*>(vn + e);
-    }
-  }
+  if (a.append && j0 <= L - 1 && L - 1 < j1) append_row<T>(a, b, L);
 }
 
 // ---------------------------------------------------------------------------
@@ -243,6 +267,13 @@ __global__ __launch_bounds__(PA_THREADS) void k_decode_phase_a(PhaseAArgs a, int
     return;
   }
   blk -= n_idx;
+  if (!a.do_scores && (a.append || a.window_idx)) {  // no index tiles: one append block per sequence
+    if (blk < a.sh.B) {
+      append_block<T>(a, blk);
+      return;
+    }
+    blk -= a.sh.B;
+  }
   if (blk < n_lin) {
     const int per_b = a.sh.H_L * slices;
     const int b = blk / per_b, rem = blk % per_b;
@@ -263,7 +294,8 @@ static hipError_t launch_pa(const PhaseAArgs& a, hipStream_t st) {
   const int slices = sh.d / LIN_COLS;
   const int n_lin = a.do_linear ? sh.B * sh.H_L * slices : 0;
   const int n_gate = a.do_gate ? sh.B * a.gate_chunks : 0;
-  const int grid = n_idx + n_lin + n_gate;
+  const int n_app = (!a.do_scores && (a.append || a.window_idx)) ? sh.B : 0;
+  const int grid = n_idx + n_app + n_lin + n_gate;
   if (grid == 0) return hipSuccess;
   klaunch((k_decode_phase_a<T, R>), dim3(grid), dim3(PA_THREADS), 0, st, a, n_idx, tiles, tile_rows,
                      n_lin, slices);
@@ -306,8 +338,9 @@ __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
   const int i0 = s * a.split_len;
   if (i0 >= m) return;  // empty split: the combine skips it
   const int i1 = min(m, i0 + a.split_len);
-  const int32_t* irow = a.dense ? nullptr : a.idx + (size_t)r * a.idx_ld;
-  auto pos_of = [irow](int i) { return irow ? irow[i] : i; };
+  const int32_t* irow = (a.dense || a.window) ? nullptr : a.idx + (size_t)r * a.idx_ld;
+  const int base = a.window ? len - m : 0;  // the window's first position
+  auto pos_of = [irow, base](int i) { return irow ? irow[i] : base + i; };
   if constexpr (MF) attend_split_mfma<D, GT, AT_THREADS, AT_THREADS / WAVE>(a, r, g, s, len, i0, i1, pos_of, ms);
   else attend_split<T, D, GT, AT_THREADS, AT_RP>(a, r, g, s, len, i0, i1, pos_of, ms);
 }

@@ -24,6 +24,7 @@
 //      iterating the set bits of per-thread masks, optionally as a bitmask.
 #include "lisa_common.h"
 #include "lisa_kernels.h"
+#include "lisa_prefill.h"
 #include "lisa_select.h"
 
 namespace lisa {
@@ -69,6 +70,21 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
   const int m = M < len ? M : len;
   if (orow)
     for (int k = m + tid; k < M; k += THREADS) orow[k] = -1;
+}
+
+// Sliding-window index lists ([LISA] Section 3.2 Stage 1): row t gets the
+// min(M, t+1) positions ending at t, ascending, then -1.
+__global__ __launch_bounds__(256) void k_window_index(int32_t* idx, int n, int M) {
+  const int r = blockIdx.x;  // (sequence, row)
+  const int t = r % n;
+  const int m = min(M, t + 1);
+  for (int k = threadIdx.x; k < M; k += 256) idx[(size_t)r * M + k] = k < m ? t + 1 - m + k : -1;
+}
+
+hipError_t launch_window_index(int32_t* idx, int B, int n, int M, hipStream_t st) {
+  if (B <= 0 || n <= 0) return hipSuccess;
+  klaunch(k_window_index, dim3((unsigned)((size_t)B * n)), dim3(256), 0, st, idx, n, M);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {

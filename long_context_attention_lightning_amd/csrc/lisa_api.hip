@@ -54,7 +54,8 @@ constexpr int MAX_ROW = 65536;  // longest score row the select kernel holds
 int check_shape(const lisa_shape* s, Shape& o) {
   if (!s) return fail(LISA_ERR_INVALID_ARG, "shape is NULL");
   if (s->dtype != LISA_F32 && s->dtype != LISA_BF16) return fail(LISA_ERR_INVALID_ARG, "dtype %d", s->dtype);
-  if (s->flags & ~LISA_LINEAR_UNNORMALIZED) return fail(LISA_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
+  if (s->flags & ~(LISA_LINEAR_UNNORMALIZED | LISA_SLIDING_WINDOW))
+    return fail(LISA_ERR_INVALID_ARG, "unknown flags 0x%x", s->flags);
   if (s->B < 1 || s->H_q < 1 || s->H_kv < 1 || s->d < 1 || s->H_I < 1 || s->H_Ik < 1 || s->d_I < 1 ||
       s->H_L < 1 || s->hidden < 1 || s->M < 1 || s->cap < 1)
     return fail(LISA_ERR_INVALID_ARG, "every count must be >= 1");
@@ -310,10 +311,14 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   int rc = check_shape(shape, sh);
   if (rc) return rc;
   if ((rc = check_decode_len(sh))) return rc;
-  REQUIRE_PTR(seq_lens); REQUIRE_PTR(q); REQUIRE_PTR(k_new); REQUIRE_PTR(v_new); REQUIRE_PTR(q_idx);
-  REQUIRE_PTR(k_idx_new); REQUIRE_PTR(q_lin); REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(x);
-  REQUIRE_PTR(w_gate); REQUIRE_PTR(w_idx); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
-  REQUIRE_PTR(k_idx_cache); REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(out); OPTIONAL_PTR(idx_out);
+  const bool window = sh.flags & LISA_SLIDING_WINDOW;  // no indexer: its arguments are not used
+  REQUIRE_PTR(seq_lens); REQUIRE_PTR(q); REQUIRE_PTR(k_new); REQUIRE_PTR(v_new);
+  REQUIRE_PTR(q_lin); REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(out); OPTIONAL_PTR(idx_out);
+  if (!window) {
+    REQUIRE_PTR(q_idx); REQUIRE_PTR(k_idx_new); REQUIRE_PTR(w_idx); REQUIRE_PTR(k_idx_cache);
+  }
   REQUIRE_PTR(ws);
   const DecodeWs w = decode_ws(sh);
   if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
@@ -329,7 +334,22 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   pa.o_lin = at<float>(ws, w.o_lin); pa.lin_den = at<float>(ws, w.lin_den);
   pa.gate_part = at<float>(ws, w.gate); pa.gate_chunks = decode_gate_chunks(sh);
   pa.append = 1; pa.do_scores = 1; pa.do_linear = 1; pa.do_gate = 1; pa.linear_output = 1;
+  if (window) {  // append without scoring; the window's index list if asked for
+    pa.q_idx = nullptr; pa.k_idx_new = nullptr; pa.k_idx_cache = nullptr; pa.w_idx = nullptr;
+    pa.do_scores = 0; pa.window_idx = idx_out; pa.M = sh.M;
+  }
   LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
+  if (window) {
+    AttnArgs aa{};
+    aa.sh = sh; aa.n_rows = sh.B; aa.rows_per_seq = 1; aa.prefill = 0; aa.dense = 0; aa.window = 1;
+    aa.seq_lens = seq_lens; aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = nullptr; aa.idx_ld = 0;
+    aa.nsplit = w.nsplit; aa.split_len = w.split_len; aa.part = at<float>(ws, w.part);
+    aa.gate_part = pa.gate_part; aa.gate_chunks = pa.gate_chunks;
+    aa.o_lin = pa.o_lin; aa.lin_den = (sh.flags & LISA_LINEAR_UNNORMALIZED) ? nullptr : pa.lin_den; aa.out = out;
+    LAUNCH(KID_ATTN, st, launch_attention(aa, st));
+    LAUNCH(KID_ATTN_COMBINE, st, launch_attention_combine(aa, st));
+    return LISA_OK;
+  }
 
   const bool fused = select_attend_supported(sh, w.nsplit, w.split_len);
   int32_t* idx = idx_out ? idx_out : (fused ? nullptr : at<int32_t>(ws, w.idx));
@@ -385,6 +405,7 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n, const i
   if (rc) return rc;
   if (rows_mode != LISA_ROWS_DECODE && rows_mode != LISA_ROWS_PREFILL)
     return fail(LISA_ERR_INVALID_ARG, "rows_mode %d", rows_mode);
+  if (sh.flags & LISA_SLIDING_WINDOW) return fail(LISA_ERR_INVALID_ARG, "a sliding-window shape has no indexer");
   const bool dec = rows_mode == LISA_ROWS_DECODE;
   if (dec) {
     if ((rc = check_decode_len(sh))) return rc;
@@ -478,9 +499,13 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
   int rc = check_shape(shape, sh);
   if (rc) return rc;
   if ((rc = check_prefill_len(sh, n))) return rc;
-  REQUIRE_PTR(q); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(k_idx_cache); REQUIRE_PTR(q_idx);
+  const bool window = sh.flags & LISA_SLIDING_WINDOW;  // no indexer: its arguments are not used
+  REQUIRE_PTR(q); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
   REQUIRE_PTR(q_lin); REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(x); REQUIRE_PTR(w_gate);
-  REQUIRE_PTR(w_idx); REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(out); OPTIONAL_PTR(idx_out); REQUIRE_PTR(ws);
+  REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(out); OPTIONAL_PTR(idx_out); REQUIRE_PTR(ws);
+  if (!window) {
+    REQUIRE_PTR(k_idx_cache); REQUIRE_PTR(q_idx); REQUIRE_PTR(w_idx);
+  }
   const PrefillWs w = prefill_ws(sh, n);
   if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
   hipStream_t st = (hipStream_t)stream;
@@ -512,6 +537,26 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
     LAUNCH(KID_PREFILL_LINEAR, st, launch_copy_f32(z, la.z_out, (size_t)sh.B * sh.H_L * sh.d, st));
   }
 
+  const bool mfma_attn = attn_mfma_supported(sh);
+  if (window) {  // sliding window: no scores, no select; attention over each row's window
+    if (idx_out) LAUNCH(KID_SELECT, st, launch_window_index(idx_out, sh.B, n, sh.M, st));
+    if (mfma_attn) {
+      AttnMaskArgs am{};
+      am.sh = sh; am.n = n; am.q = q; am.k_cache = k_cache; am.v_cache = v_cache; am.mask = nullptr;
+      am.mask_ld = 0; am.scale_log2e = 1.4426950408889634f / sqrtf((float)sh.d);
+      am.gate_part = ga.gate_part; am.o_lin = o_lin; am.out = out; am.window = 1;
+      LAUNCH(KID_PREFILL_ATTN, st, launch_attn_prefill_mfma(am, st));
+      return LISA_OK;
+    }
+    AttnArgs aa{};
+    aa.sh = sh; aa.n_rows = sh.B * n; aa.rows_per_seq = n; aa.prefill = 1; aa.dense = 0; aa.window = 1;
+    aa.seq_lens = nullptr; aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = nullptr; aa.idx_ld = 0;
+    aa.nsplit = 1; aa.split_len = sh.M; aa.part = nullptr;
+    aa.gate_part = ga.gate_part; aa.gate_chunks = 1; aa.o_lin = o_lin; aa.lin_den = nullptr; aa.out = out;
+    LAUNCH(KID_PREFILL_ATTN, st, launch_attention(aa, st));
+    return LISA_OK;
+  }
+
   IndexScoreArgs ia{};
   ia.sh = sh; ia.n = n; ia.q_idx = q_idx; ia.k_idx = k_idx_cache; ia.w_idx = w_idx;
   ia.row0 = n > sh.M ? sh.M : n; ia.stored_rows = n > sh.M ? n - sh.M : 0;
@@ -519,7 +564,6 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
   LAUNCH(KID_PREFILL_INDEX, st, index_mfma_supported(sh) ? launch_index_scores_mfma(ia, st)
                                                          : launch_index_scores(ia, st));
 
-  const bool mfma_attn = attn_mfma_supported(sh);
   int32_t* idx = idx_out ? idx_out : (mfma_attn ? nullptr : at<int32_t>(ws, w.idx));
   SelectArgs sa{};
   sa.n_rows = sh.B * n; sa.rows_per_seq = n; sa.prefill = 1; sa.seq_lens = nullptr;

@@ -67,6 +67,8 @@ struct PhaseAArgs {
   int append;          // write the new token into the caches
   int do_scores, do_linear, do_gate;
   int linear_output;   // write o_lin
+  int32_t* window_idx; // nullable [B, M]: without scoring, the M most recent positions (sliding window)
+  int M;
 };
 hipError_t launch_decode_phase_a(const PhaseAArgs& a, hipStream_t st);
 
@@ -112,6 +114,7 @@ struct AttnArgs {
   const float* o_lin;       // [n_rows, H_q, d] (with gate)
   const float* lin_den;     // nullable [n_rows, H_q]: o_lin is divided by it
   void* out;                // [n_rows, H_q, d] T
+  int window;               // positions len-m .. len-1 (sliding window) instead of idx
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);          // split kernel
 hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t st);  // merge (nsplit > 1)

@@ -72,10 +72,15 @@ struct AttnMaskArgs {
   const float* gate_part;   // [B * n, H_q] gate logits
   const float* o_lin;       // [B, n, H_q, d] linear-branch outputs
   void* out;                // [B, n, H_q, d]
+  int window;               // sliding window of sh.M positions: no mask rows are read, and key
+                            // tiles before every row's window are skipped
 };
 bool attn_mfma_supported(const Shape& sh);
 int64_t attn_mask_ld(int n);
 hipError_t launch_attn_prefill_mfma(const AttnMaskArgs& a, hipStream_t st);
+// Index lists of the sliding window: row t of each of the B sequences gets
+// max(0, t+1-M)..t ascending, then -1 ([B, n, M] int32).
+hipError_t launch_window_index(int32_t* idx, int B, int n, int M, hipStream_t st);
 
 // Index scores and gate logits on bf16 MFMA.
 bool index_mfma_supported(const Shape& sh);
