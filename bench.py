@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--batched-only", action="store_true", help="only the batch-32 ragged decode leg (profiling)")
     p.add_argument("--batched-steps", type=int, default=64)
     p.add_argument("--no-sweep", action="store_true", help="skip the batch-8 32K M-sweep decode leg")
+    p.add_argument("--no-window", action="store_true", help="skip the sliding-window decode leg")
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
     p.add_argument("--prefill-iters", type=int, default=5)
@@ -64,12 +65,13 @@ def _lens(L, B):
     return np.broadcast_to(np.asarray(L, dtype=np.int64), (B,))
 
 
-def decode_bytes(cfg, L, M, B):
-    """Per-step bytes of the whole decode step (all sequences)."""
+def decode_bytes(cfg, L, M, B, indexer=True):
+    """Per-step bytes of the whole decode step (all sequences); without the
+    indexer (sliding window) the index keys are not read."""
     tot = 0
     for l in _lens(L, B):
         m = min(M, int(l))
-        tot += (int(l) * cfg.H_Ik * cfg.d_I * 2                   # index keys
+        tot += (int(l) * cfg.H_Ik * cfg.d_I * 2 * indexer         # index keys
                 + m * cfg.H_kv * cfg.d * 4                        # gathered K and V
                 + 8 * cfg.H_L * cfg.d * (cfg.d + 1)               # S and z, read + write
                 + 2 * (2 * cfg.H_q * cfg.d + 3 * cfg.H_L * cfg.d + cfg.H_I * cfg.d_I
@@ -77,10 +79,10 @@ def decode_bytes(cfg, L, M, B):
     return tot + 2 * cfg.hidden * cfg.H_q
 
 
-def phase_a_bytes(cfg, L, B):
+def phase_a_bytes(cfg, L, B, indexer=True):
     tot = 0
     for l in _lens(L, B):
-        tot += (int(l) * cfg.H_Ik * cfg.d_I * 2 + 8 * cfg.H_L * cfg.d * (cfg.d + 1)
+        tot += (int(l) * cfg.H_Ik * cfg.d_I * 2 * indexer + 8 * cfg.H_L * cfg.d * (cfg.d + 1)
                 + 2 * (3 * cfg.H_L * cfg.d + cfg.H_I * cfg.d_I + cfg.hidden)
                 + 2 * 2 * (2 * cfg.H_kv * cfg.d + cfg.H_Ik * cfg.d_I))   # new rows read + appended
     return tot + 2 * cfg.hidden * cfg.H_q
@@ -127,7 +129,7 @@ def kernel_roofline(name, avg_ms, work, bound, traffic_key=None):
             "algorithmic_work_per_launch": work, "avg_launch_us": round(avg_ms * 1e3, 3)}
 
 
-def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, traffic_prefix=""):
+def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, traffic_prefix="", flags=0):
     """Graph-replayed decode steps of one workload over nbuf buffer sets:
     step time, per-kernel durations and rooflines, the dense baseline."""
     from lisa_inputs import decode_inputs
@@ -146,7 +148,7 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
     seq = torch.from_numpy(inp["seq_lens"].astype(np.int32)).cuda()
     w_idx = up(inp["w_idx"], torch.float32)
     sh = Lb.make_shape(B=B, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, H_I=cfg.H_I, H_Ik=cfg.H_Ik,
-                       d_I=cfg.d_I, hidden=cfg.hidden, M=M, cap=cfg.cap, max_len=Lctx)
+                       d_I=cfg.d_I, hidden=cfg.hidden, M=M, cap=cfg.cap, max_len=Lctx, flags=flags)
     sets = []
     per_set = ("q", "k_new", "v_new", "q_idx", "k_idx_new", "q_lin", "k_lin", "v_lin", "x",
                "k_cache", "v_cache", "k_idx_cache", "S", "z")
@@ -249,7 +251,8 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
         del g_dense
 
     lens = inp["seq_lens"].astype(np.int64)
-    work = {0: (phase_a_bytes(cfg, lens, B), "hbm"),
+    indexer = not (flags & Lb.LISA_SLIDING_WINDOW)
+    work = {0: (phase_a_bytes(cfg, lens, B, indexer), "hbm"),
             1: (SELECT_OPS_PER_KEY * int(lens.sum()), "alu"),
             12: (attention_bytes(cfg, lens, M, B) + 4 * int(lens.sum()), "hbm"),
             2: (attention_bytes(cfg, lens, M, B), "hbm"),
@@ -258,7 +261,7 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
                                                      traffic_key=traffic_prefix + Lb.lisa_kernel_name(k))
              for k in dec_kids}
     roof = roofs[Lb.lisa_kernel_name(dom)]
-    step_bytes = decode_bytes(cfg, lens, M, B)
+    step_bytes = decode_bytes(cfg, lens, M, B, indexer)
     extra = {
         "us_per_step": round(ms_step * 1e3, 3),
         "us_per_step_median_p10_p90": [round(float(np.median(spread)), 3), round(float(np.percentile(spread, 10)), 3),
@@ -335,6 +338,15 @@ def main():
         extra["batched_decode"] = dict(workload=cb.name, batch=cb.B, context=f"{cb.L_lo}..{cb.L_hi} (seeded uniform)",
                                        tok_s=round(cb.B / (bms * 1e-3), 1), **db)
         del db
+        torch.cuda.empty_cache()
+    if not args.no_window:
+        dw = bench_decode(args, torch, Lb, cfg, cid, 8, 160, 16, False, "window:", flags=Lb.LISA_SLIDING_WINDOW)
+        dw.pop("inp")
+        wms = dw.pop("ms_step")
+        dw.pop("steps")
+        extra["window_decode"] = dict(what="sliding-window mode (window M, no indexer or select), same workload",
+                                      tok_s=round(B / (wms * 1e-3), 1), us_per_step=dw["us_per_step"],
+                                      kernel_us=dw["kernel_us"], step_hbm_roofline_frac=dw["step_hbm_roofline_frac"])
         torch.cuda.empty_cache()
     if not args.no_sweep:
         c4 = CONFIGS[4]
@@ -469,8 +481,35 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     proofs["prefill_linear_branch"] = kernel_roofline("prefill_linear_branch", lin_us * 1e-3, lin_bytes, "hbm")
     proofs["prefill_linear_branch_mfma"] = kernel_roofline("prefill_linear_branch", lin_us * 1e-3, lin_flops, "mfma")
     dense = dense_prefill_baseline(torch, t["q"], t["k"], t["v"], cfg, n, args.prefill_iters)
+    # the same prefill in sliding-window mode (no indexer; each row attends to its M most recent keys)
+    shw = Lb.make_shape(B=1, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, H_I=cfg.H_I, H_Ik=cfg.H_Ik,
+                        d_I=cfg.d_I, hidden=cfg.hidden, M=M, cap=n, flags=Lb.LISA_SLIDING_WINDOW)
+
+    def call_w():
+        Lb.lisa_prefill(shw, n, t["q"], t["k"], t["v"], None, None, t["q_lin"], t["k_lin"],
+                        t["v_lin"], t["x"], t["w_gate"], None, S, z, out, None, ws)
+
+    call_w()
+    st_w = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    sp_w = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in st_w + sp_w:
+        e.record()
+    torch.cuda.synchronize()
+    Lb.lisa_timing_enable(6, st_w, sp_w)
+    call_w()
+    torch.cuda.synchronize()
+    attn_w = round(st_w[0].elapsed_time(sp_w[0]) * 1e3, 1) if Lb.lisa_timing_count() else None
+    Lb.lisa_timing_enable(0)
+    t0.record()
+    for _ in range(args.prefill_iters):
+        call_w()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_w = t0.elapsed_time(t1) / args.prefill_iters
     res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
            "dense_causal_prefill_attention_ms": dense,
+           "window_prefill": {"ms": round(ms_w, 3), "tok_s": round(n / (ms_w * 1e-3), 1), "attention_us": attn_w,
+                              "what": "sliding-window mode, window M, no indexer or select"},
            "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
            "prefill_kernel_roofline": proofs}
     del ws, t, out
