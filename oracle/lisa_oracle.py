@@ -49,6 +49,7 @@ __all__ = [
     "phi", "index_scores", "select_topm", "sparse_attention", "gate",
     "linear_recurrent", "linear_rows", "linear_chunked", "linear_state_update",
     "prefill", "prefill_rows", "decode_step", "dense_decode", "window_positions",
+    "segment_correct",
 ]
 
 
@@ -239,6 +240,35 @@ def linear_state_update(k_lin, v_lin, S0, z0):
     S = _f64(S0) + np.einsum("nhd,nhe->hde", fk, v, optimize=True)
     z = _f64(z0) + fk.sum(axis=0)
     return S, z
+
+
+def segment_correct(S, z, S_start, z_start, mean_S, mean_z, t: int, alpha: float):
+    """Segment state correction at the end of the t-th segment (t >= 1)
+    ([LISA] §3.3 "Segment State Update", Eqs. 6-9).
+
+    * Eq. 6: the segment's direction is the state change over it,
+      ``grad = S - S_start`` (S: the state reached at the segment's end).
+    * Eq. 7: the global direction is the plain mean of the raw directions
+      of the segments before it (``mean_S`` holds that mean over segments
+      1..t-1; zero for t = 1).
+    * Eq. 8: ``corrected = (1 - alpha) grad + alpha mean``.
+    * Eq. 9: the state becomes ``S_start + corrected``.
+
+    Readings: the mean averages the raw directions of Eq. 6 (Eq. 7 as
+    printed), and the normaliser z is corrected exactly like S, the pair
+    (S, z) being the state that the branch carries.
+    Returns (S_new, z_new, mean_S_new, mean_z_new): the corrected state, and
+    the mean over segments 1..t; the corrected state is also where the next
+    segment starts.
+    """
+    out = []
+    for cur, start, mean in ((S, S_start, mean_S), (z, z_start, mean_z)):
+        grad = _f64(cur) - _f64(start)
+        prev = _f64(mean) if t > 1 else np.zeros_like(grad)
+        corrected = (1.0 - alpha) * grad + alpha * prev
+        out.append((_f64(start) + corrected, prev + (grad - prev) / t))
+    (S_new, mS), (z_new, mz) = out
+    return S_new, z_new, mS, mz
 
 
 # ----------------------------------------------------------------------------

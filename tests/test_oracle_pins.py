@@ -464,6 +464,55 @@ def test_window_decode_equals_tied_topm_and_dense_when_wide():
 
 
 # ----------------------------------------------------------------------------
+# segment state correction ([LISA] §3.3, Eqs. 6-9)
+# ----------------------------------------------------------------------------
+def test_segment_correct_scalar_by_hand():
+    # segment 2: start 1, end 4 (direction 3); mean of segment 1's direction 1;
+    # alpha 0.5: corrected 0.5*3 + 0.5*1 = 2, state 1 + 2 = 3, new mean (1+3)/2 = 2
+    S, z, mS, mz = oracle.segment_correct(np.array([4.0]), np.array([10.0]), np.array([1.0]), np.array([6.0]),
+                                          np.array([1.0]), np.array([2.0]), 2, 0.5)
+    assert S.tolist() == [3.0] and mS.tolist() == [2.0]
+    # z: direction 4, prior mean 2 -> corrected 3, state 9, mean 3
+    assert z.tolist() == [9.0] and mz.tolist() == [3.0]
+
+
+def test_segment_correct_first_segment_ignores_the_mean_buffer():
+    r = np.random.default_rng(21)
+    S, S0 = r.standard_normal((2, 3, 3)), r.standard_normal((2, 3, 3))
+    z, z0 = r.standard_normal((2, 3)), r.standard_normal((2, 3))
+    junk = np.full((2, 3, 3), 1e30)
+    Sn, zn, mS, mz = oracle.segment_correct(S, z, S0, z0, junk, junk[..., 0], 1, 0.3)
+    np.testing.assert_allclose(Sn, S0 + 0.7 * (S - S0), rtol=1e-14)
+    np.testing.assert_allclose(mS, S - S0, rtol=1e-14)
+    np.testing.assert_allclose(mz, z - z0, rtol=1e-14)
+
+
+def test_segment_correct_invariants_over_a_run():
+    """alpha = 0 leaves every state as reached; a constant direction is left
+    unchanged at any alpha; the mean after t segments is the mean of the raw
+    directions."""
+    r = np.random.default_rng(22)
+    dirs = [r.standard_normal((4, 4)) for _ in range(6)]
+    for alpha in (0.0, 0.35, 1.0):
+        S_start = np.zeros((4, 4))
+        mean = np.zeros((4, 4))
+        for t, dlt in enumerate(dirs, start=1):
+            S_end = S_start + dlt
+            S_new, _, mean, _ = oracle.segment_correct(S_end, np.zeros(1), S_start, np.zeros(1), mean,
+                                                       np.zeros(1), t, alpha)
+            if alpha == 0.0:
+                np.testing.assert_allclose(S_new, S_end, rtol=0, atol=1e-14)
+            want = (1 - alpha) * dlt + alpha * (np.mean(dirs[: t - 1], axis=0) if t > 1 else 0.0)
+            np.testing.assert_allclose(S_new - S_start, want, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(mean, np.mean(dirs[:t], axis=0), rtol=1e-12, atol=1e-12)
+            S_start = S_new
+    const = r.standard_normal((4, 4))
+    S_new, _, _, _ = oracle.segment_correct(5 + const, np.zeros(1), np.full((4, 4), 5.0), np.zeros(1), const,
+                                            np.zeros(1), 4, 0.8)
+    np.testing.assert_allclose(S_new, 5 + const, rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------
 # input generator
 # ----------------------------------------------------------------------------
 def test_round_bf16_matches_torch():
