@@ -198,6 +198,28 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n,
  *   S += sum_t phi(k_lin[t])^T v_lin[t],  z += sum_t phi(k_lin[t]).
  * k_lin, v_lin [B, n_tokens, H_L, d] T; S [B, H_L, d, d], z [B, H_L, d] fp32.
  */
+/*
+ * Segment state correction at the end of segment t ([LISA] Section 3.3
+ * "Segment State Update", Eqs. 6-9), elementwise over S [B, H_L, d, d] and
+ * z [B, H_L, d] (fp32, device, 16-byte aligned):
+ *   grad      = S - S_start                        (Eq. 6)
+ *   corrected = (1 - alpha) grad + alpha mean      (Eq. 8; mean = 0 when t == 1)
+ *   S         = S_start + corrected                (Eq. 9)
+ *   mean      = mean + (grad - mean) / t           (Eq. 7: the mean of the raw
+ *                                                   directions of segments 1..t)
+ *   S_start   = S                                  (where segment t+1 starts)
+ * and the same for z with z_start and mean_z (the normaliser is part of the
+ * state).  S, z: in, the state reached at the segment's end; out, corrected.
+ * S_start, z_start: in, the state at the segment's start; out, the corrected
+ * state.  mean_S, mean_z: in, the mean direction of segments 1..t-1 (not
+ * read when t == 1); out, of segments 1..t.  t >= 1 counts segments of k
+ * tokens; the caller calls this after every k tokens (decode steps or
+ * prefill chunks).  d must be a multiple of 4.  Nothing is allocated; the
+ * call is asynchronous on `stream`.
+ */
+int lisa_segment_correct(const lisa_shape* shape, float* S, float* z, float* S_start, float* z_start,
+                         float* mean_S, float* mean_z, int32_t t, float alpha, void* stream);
+
 int lisa_linear_state_update(const lisa_shape* shape, int32_t n_tokens,
                              const void* k_lin, const void* v_lin,
                              float* S, float* z, void* stream);

@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "LisaError", "LisaLibraryMissing", "lisa_shape", "make_shape", "library",
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
-    "lisa_linear_state_update", "lisa_dense_decode", "lisa_status_string",
+    "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_status_string",
     "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
     "workspace", "LISA_F32", "LISA_BF16", "LISA_LINEAR_UNNORMALIZED", "LISA_SLIDING_WINDOW",
     "LISA_OP_DECODE", "LISA_OP_PREFILL", "LISA_OP_TOPK_DECODE", "LISA_OP_TOPK_PREFILL",
@@ -40,7 +40,7 @@ LISA_ROWS_DECODE, LISA_ROWS_PREFILL = 0, 1
 
 EXPORTED_SYMBOLS = (
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
-    "lisa_linear_state_update", "lisa_dense_decode", "lisa_status_string", "lisa_last_error",
+    "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_status_string", "lisa_last_error",
     "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
 )
 
@@ -99,6 +99,8 @@ def library() -> ctypes.CDLL:
     lib.lisa_indexer_topk.restype = ctypes.c_int
     lib.lisa_linear_state_update.argtypes = [sp, _I32, _P, _P, _P, _P, _P]
     lib.lisa_linear_state_update.restype = ctypes.c_int
+    lib.lisa_segment_correct.argtypes = [sp, _P, _P, _P, _P, _P, _P, _I32, ctypes.c_float, _P]
+    lib.lisa_segment_correct.restype = ctypes.c_int
     lib.lisa_dense_decode.argtypes = [sp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.lisa_dense_decode.restype = ctypes.c_int
     lib.lisa_status_string.argtypes = [ctypes.c_int]
@@ -216,6 +218,16 @@ def lisa_linear_state_update(shape, n_tokens, k_lin, v_lin, S, z, stream=None):
         ctypes.byref(shape), int(n_tokens), _ptr(k_lin, "k_lin", T), _ptr(v_lin, "v_lin", T),
         _ptr(S, "S", torch.float32), _ptr(z, "z", torch.float32), _stream(stream))
     _check(rc, "lisa_linear_state_update")
+
+
+def lisa_segment_correct(shape, S, z, S_start, z_start, mean_S, mean_z, t, alpha, stream=None):
+    """Segment state correction after segment t (all tensors fp32, updated in place)."""
+    f = torch.float32
+    rc = library().lisa_segment_correct(
+        ctypes.byref(shape), _ptr(S, "S", f), _ptr(z, "z", f), _ptr(S_start, "S_start", f),
+        _ptr(z_start, "z_start", f), _ptr(mean_S, "mean_S", f), _ptr(mean_z, "mean_z", f), int(t),
+        float(alpha), _stream(stream))
+    _check(rc, "lisa_segment_correct")
 
 
 def lisa_dense_decode(shape, seq_lens, q, k_cache, v_cache, out, ws, stream=None):

@@ -207,7 +207,8 @@ struct Timing {
 const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
     "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine",
-    "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose", "select_attention"};
+    "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose", "select_attention",
+    "segment_correct"};
 
 thread_local LaunchEvents g_next_launch;
 
@@ -488,6 +489,24 @@ int lisa_linear_state_update(const lisa_shape* shape, int32_t n_tokens, const vo
   la.sh = sh; la.n = n_tokens; la.q_lin = nullptr; la.k_lin = k_lin; la.v_lin = v_lin;
   la.S = S; la.z_in = z; la.z_out = z; la.o_lin = nullptr;  // without outputs only slice 0 touches z
   LAUNCH(KID_LINEAR_UPDATE, st, launch_linear_recurrent(la, st));
+  return LISA_OK;
+}
+
+int lisa_segment_correct(const lisa_shape* shape, float* S, float* z, float* S_start, float* z_start,
+                         float* mean_S, float* mean_z, int32_t t, float alpha, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if (t < 1) return fail(LISA_ERR_INVALID_ARG, "segment number %d (must be >= 1)", t);
+  if (!(alpha == alpha)) return fail(LISA_ERR_INVALID_ARG, "alpha is NaN");
+  REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(S_start); REQUIRE_PTR(z_start); REQUIRE_PTR(mean_S);
+  REQUIRE_PTR(mean_z);
+  if (sh.d % 4) return fail(LISA_ERR_UNSUPPORTED, "head dim %d is not a multiple of 4", sh.d);
+  SegmentArgs a{};
+  a.S = S; a.z = z; a.S_start = S_start; a.z_start = z_start; a.mean_S = mean_S; a.mean_z = mean_z;
+  a.n_S = (size_t)sh.B * sh.H_L * sh.d * sh.d; a.n_z = (size_t)sh.B * sh.H_L * sh.d;
+  a.t = t; a.alpha = alpha;
+  LAUNCH(KID_SEGMENT, (hipStream_t)stream, launch_segment_correct(a, (hipStream_t)stream));
   return LISA_OK;
 }
 

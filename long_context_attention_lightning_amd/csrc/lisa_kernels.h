@@ -44,7 +44,8 @@ enum KernelId {
   KID_PREFILL_LIN_PREFIX = 10,
   KID_PREFILL_GATE_PREP = 11,
   KID_SELECT_ATTN = 12,
-  KID_COUNT = 13
+  KID_SEGMENT = 13,
+  KID_COUNT = 14
 };
 
 // ---------------------------------------------------------------------------
@@ -116,6 +117,19 @@ struct AttnArgs {
   void* out;                // [n_rows, H_q, d] T
   int window;               // positions len-m .. len-1 (sliding window) instead of idx
 };
+// ---------------------------------------------------------------------------
+// segment state correction (elementwise over S and z)
+// ---------------------------------------------------------------------------
+struct SegmentArgs {
+  float *S, *z;              // in: state at the segment's end; out: corrected
+  float *S_start, *z_start;  // in: state at the segment's start; out: the corrected state
+  float *mean_S, *mean_z;    // in: mean direction of segments 1..t-1; out: of 1..t
+  size_t n_S, n_z;           // element counts (multiples of 4)
+  int t;                     // segment number, >= 1
+  float alpha;
+};
+hipError_t launch_segment_correct(const SegmentArgs& a, hipStream_t st);
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);          // split kernel
 hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t st);  // merge (nsplit > 1)
 size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit);

@@ -126,3 +126,15 @@ def test_kernel_names(lib):
     names = [L.lisa_kernel_name(i) for i in range(9)]
     assert names[0] == "decode_phase_a" and None not in names
     assert L.lisa_kernel_name(99) is None
+
+
+def test_segment_correct_rejects_bad_args(lib):
+    sh = _c1()
+    buf = (ctypes.c_float * 64)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    rc = lib.lisa_segment_correct(ctypes.byref(sh), p, p, p, p, p, p, 0, 0.5, None)
+    assert rc == -1 and "segment number" in L.lisa_last_error()
+    rc = lib.lisa_segment_correct(ctypes.byref(sh), p, p, p, p, p, p, 1, float("nan"), None)
+    assert rc == -1 and "alpha" in L.lisa_last_error()
+    rc = lib.lisa_segment_correct(ctypes.byref(sh), p, None, p, p, p, p, 1, 0.5, None)
+    assert rc == -1
