@@ -28,12 +28,11 @@
 #include "lisa_select.h"
 
 namespace lisa {
+// Row t of sequence b (decode: t = 0).
 template <int THREADS, int ITEMS, bool LKEYS>
-__global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
-  __shared__ SelShared<THREADS / WAVE> sm;
-  __shared__ KeyStore<THREADS, ITEMS, LKEYS> ks;
-  const int r = blockIdx.x;
-  const int b = r / a.rows_per_seq, t = r % a.rows_per_seq;
+__device__ __forceinline__ void select_one(const SelectArgs& a, int b, int t, SelShared<THREADS / WAVE>& sm,
+                                           KeyStore<THREADS, ITEMS, LKEYS>& ks) {
+  const size_t r = (size_t)b * a.rows_per_seq + t;
   const int M = a.M;
   const int tid = threadIdx.x;
   int32_t* orow = a.idx ? a.idx + (size_t)r * a.idx_ld : nullptr;  // null: bitmask only
@@ -72,6 +71,32 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
     for (int k = m + tid; k < M; k += THREADS) orow[k] = -1;
 }
 
+template <int THREADS, int ITEMS, bool LKEYS>
+__global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
+  __shared__ SelShared<THREADS / WAVE> sm;
+  __shared__ KeyStore<THREADS, ITEMS, LKEYS> ks;
+  const int r = blockIdx.x;
+  select_one<THREADS, ITEMS, LKEYS>(a, r / a.rows_per_seq, r % a.rows_per_seq, sm, ks);
+}
+
+// Prefill rows of up to 256 * 64 positions: 256 threads per row, with 16,
+// 32 or 64 scores per thread chosen per row by its length (the work of a
+// row scales with the items per thread, not with its length), longest rows
+// first so that the short ones fill the tail of the launch.  Keys are
+// recomputed from the score row, so the block holds only the histogram and
+// several blocks share a CU.
+__global__ __launch_bounds__(256) void k_select_prefill(SelectArgs a) {
+  __shared__ SelShared<256 / WAVE> sm;
+  __shared__ KeyStore<256, 16, false> ks16;
+  __shared__ KeyStore<256, 32, false> ks32;
+  __shared__ KeyStore<256, 64, false> ks64;
+  const int n = a.rows_per_seq;
+  const int b = blockIdx.x / n, t = n - 1 - (int)(blockIdx.x % n);
+  if (t < 256 * 16) select_one<256, 16, false>(a, b, t, sm, ks16);
+  else if (t < 256 * 32) select_one<256, 32, false>(a, b, t, sm, ks32);
+  else select_one<256, 64, false>(a, b, t, sm, ks64);
+}
+
 // Sliding-window index lists ([LISA] Section 3.2 Stage 1): row t gets the
 // min(M, t+1) positions ending at t, ascending, then -1.
 __global__ __launch_bounds__(256) void k_window_index(int32_t* idx, int n, int M) {
@@ -90,7 +115,8 @@ hipError_t launch_window_index(int32_t* idx, int B, int n, int M, hipStream_t st
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)a.n_rows);
-  if (a.max_len <= 256 * 16) klaunch((k_select<256, 16, true>), grid, dim3(256), 0, st, a);
+  if (a.prefill && a.max_len > 256 * 16 && a.max_len <= 256 * 64) klaunch(k_select_prefill, grid, dim3(256), 0, st, a);
+  else if (a.max_len <= 256 * 16) klaunch((k_select<256, 16, true>), grid, dim3(256), 0, st, a);
   else if (a.max_len <= 1024 * 16) klaunch((k_select<1024, 16, true>), grid, dim3(1024), 0, st, a);
   else if (a.max_len <= 1024 * 32) klaunch((k_select<1024, 32, true>), grid, dim3(1024), 0, st, a);
   else if (a.max_len <= 1024 * 64) klaunch((k_select<1024, 64, false>), grid, dim3(1024), 0, st, a);

@@ -3,10 +3,12 @@ same fp32 score rows ("LISA", arXiv 2607.19358v1, Section 3.2 Stage 2; ties
 to the later position, -0.0 equal to +0.0, ascending output, -1 padding)."""
 import numpy as np
 import pytest
+import torch
 
+import long_context_attention_lightning_amd as L
 import oracle
 from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs, row_sample
-from gpu_helpers import gpu_select_rows, padded
+from gpu_helpers import dev, gpu_select_rows, host, padded
 
 pytestmark = pytest.mark.gpu
 
@@ -75,3 +77,25 @@ def test_select_on_oracle_prefill_scores_c3_rows():
         s = oracle.index_scores(inp["q_idx"][0, t], inp["k_idx"][0, : t + 1], inp["w_idx"])
         rows.append(s.astype(np.float32))
     _check(rows, cfg.M, f"C3 {len(rows)} rows")
+
+
+def test_select_prefill_rows_all_item_bands():
+    """Prefill rows from given fp32 scores, one launch: rows of up to 4096,
+    8192 and 16384 positions are selected with different per-thread item
+    counts, longest rows first; every band edge is checked."""
+    n, M = 9000, 2048
+    r = np.random.default_rng(11)
+    sc = (np.round(r.standard_normal((n, n)) * 8) / 8).astype(np.float32)  # many ties
+    sc[5000] = 0.0  # a whole row of ties: the most recent positions win
+    sh = L.make_shape(B=1, H_q=1, H_kv=1, d=32, H_I=1, H_Ik=1, d_I=16, hidden=1, M=M, cap=n, max_len=n)
+    idx = torch.full((1, n, M), -7, dtype=torch.int32, device="cuda")
+    L.lisa_indexer_topk(sh, L.LISA_ROWS_PREFILL, n, None, None, None, None, dev(sc, torch.float32), n, None,
+                        idx, None)
+    torch.cuda.synchronize()
+    got = host(idx)[0]
+    rows = sorted(set(range(0, n, 61)) | {0, 1, 2046, 2047, 2048, 4094, 4095, 4096, 5000, 8190, 8191, 8192,
+                                          n - 1})
+    bad = [t for t in rows if not np.array_equal(got[t], padded(oracle.select_topm(sc[t, : t + 1].astype(np.float64),
+                                                                                    M), M))]
+    print(f"[prefill rows] checked={len(rows)} mismatched={len(bad)}", flush=True)
+    assert not bad, bad[:5]
