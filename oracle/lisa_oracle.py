@@ -38,6 +38,10 @@ function that uses them:
   and ``out = g * O_sparse + (1-g) * O_linear`` ([LISA] §3.2 Eq. 1 and §3.3
   Eq. 5; the gate weights the sparse branch here, which is Eq. 1 with W_g
   negated).
+* Attention coverage ([LISA] §4, "Optimal Window Size M and Attention
+  Coverage", Eq. 10): the share of a query head's dense causal softmax
+  weight that falls on a selected set; its upper bound is the share of that
+  head's own M largest weights.
 """
 from __future__ import annotations
 
@@ -49,7 +53,7 @@ __all__ = [
     "phi", "index_scores", "select_topm", "sparse_attention", "gate",
     "linear_recurrent", "linear_rows", "linear_chunked", "linear_state_update",
     "prefill", "prefill_rows", "decode_step", "dense_decode", "window_positions",
-    "segment_correct",
+    "segment_correct", "attention_mass",
 ]
 
 
@@ -421,3 +425,35 @@ def dense_decode(inp: Dict[str, np.ndarray], batch: Optional[Iterable[int]] = No
         V[L - 1] = inp["v_new"][b]
         outs.append(sparse_attention(inp["q"][b], K, V, np.arange(L)))
     return np.stack(outs)
+
+
+# ----------------------------------------------------------------------------
+# attention coverage ([LISA] §4, Eq. 10)
+# ----------------------------------------------------------------------------
+def attention_mass(q, K, P, M: int):
+    """Coverage of one query row by a selected set, per query head.
+
+    q: [H_q, d]; K: [L, H_kv, d], the keys of positions 0..L-1 (every key at
+    or before the query); P: selected positions (distinct, any order).  For
+    query head h reading KV head g = h*H_kv//H_q, the dense weights are
+    a_j = exp(q_h . K[j, g] / sqrt(d)) over all L keys, and
+      mass[h]  = sum_{j in P} a_j / sum_j a_j                    (Eq. 10)
+      bound[h] = (sum of the M largest a_j) / sum_j a_j
+    The bound is the coverage of the head's own best M-set, which no set of
+    M positions shared by the heads can exceed (the paper's upper bound of
+    the indexer's mass, read here per head).  Returns (mass, bound), [H_q].
+    """
+    q = _f64(q)
+    H_q, d = q.shape
+    H_kv = K.shape[1]
+    P = np.asarray(P, dtype=np.int64)
+    mass = np.zeros(H_q)
+    bound = np.zeros(H_q)
+    for h in range(H_q):
+        g = (h * H_kv) // H_q
+        a = _f64(K[:, g, :]) @ q[h] / np.sqrt(d)   # logits of every key
+        w = np.exp(a - a.max())                    # the common factor cancels
+        total = w.sum()
+        mass[h] = w[P].sum() / total
+        bound[h] = np.sort(w)[::-1][: int(M)].sum() / total
+    return mass, bound

@@ -533,3 +533,80 @@ def test_generator_is_seeded_and_shaped():
     assert a["k_cache"].shape == (4, 64, 4, 128)
     assert np.all((a["seq_lens"] >= 5) & (a["seq_lens"] <= 60))
     assert np.all(round_bf16(a["q"]) == a["q"])
+
+
+# ---------------------------------------------------------------------------
+# attention coverage ([LISA] §4, Eq. 10)
+# ---------------------------------------------------------------------------
+def test_mass_by_hand():
+    """Logits 0, ln 2, ln 4 give weights in the ratio 1 : 2 : 4 (of 7)."""
+    d = 4
+    q = np.array([[2.0, 0.0, 0.0, 0.0]])  # q . k / sqrt(d) = k[0]
+    K = np.zeros((3, 1, d))
+    K[:, 0, 0] = [0.0, math.log(2.0), math.log(4.0)]
+    for P, M, mass, bound in (([0, 2], 1, 5 / 7, 4 / 7), ([1], 2, 2 / 7, 6 / 7), ([2, 1, 0], 3, 1.0, 1.0),
+                              ([], 1, 0.0, 4 / 7)):
+        m, b = oracle.attention_mass(q, K, P, M)
+        assert m[0] == pytest.approx(mass, abs=1e-15) and b[0] == pytest.approx(bound, abs=1e-15), (P, M)
+
+
+def test_mass_bound_is_the_best_m_set_brute_force():
+    r = np.random.default_rng(4)
+    L, M = 7, 3
+    q = r.standard_normal((2, 8)) * 2
+    K = r.standard_normal((L, 1, 8))
+    _, bound = oracle.attention_mass(q, K, [], M)
+    best = np.zeros(2)
+    for P in itertools.combinations(range(L), M):
+        m, _ = oracle.attention_mass(q, K, list(P), M)
+        assert np.all(m <= bound + 1e-15)
+        best = np.maximum(best, m)
+    np.testing.assert_allclose(best, bound, rtol=0, atol=1e-15)
+
+
+def test_mass_uniform_weights_and_full_set():
+    r = np.random.default_rng(5)
+    K = r.standard_normal((50, 2, 16))
+    q0 = np.zeros((4, 16))  # every logit 0: uniform weights
+    m, b = oracle.attention_mass(q0, K, oracle.window_positions(49, 20), 20)
+    np.testing.assert_allclose(m, 20 / 50, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(b, 20 / 50, rtol=0, atol=1e-15)
+    q = r.standard_normal((4, 16))
+    m, b = oracle.attention_mass(q, K, np.arange(50), 50)
+    np.testing.assert_allclose(m, 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(b, 1.0, rtol=0, atol=1e-15)
+
+
+def test_mass_splits_dense_attention():
+    """Dense attention is the mass-weighted mix of attention over P and over
+    the rest: out_dense = m out_P + (1 - m) out_rest, per head, with the
+    attention outputs from the oracle's sparse attention and from torch's
+    scaled-dot-product attention in float64."""
+    r = np.random.default_rng(6)
+    L, H_q, H_kv, d = 40, 6, 2, 16
+    q = r.standard_normal((H_q, d))
+    K = r.standard_normal((L, H_kv, d))
+    V = r.standard_normal((L, H_kv, d))
+    P = r.choice(L, 13, replace=False)
+    rest = np.setdiff1d(np.arange(L), P)
+    m, _ = oracle.attention_mass(q, K, P, 13)
+    mix = m[:, None] * oracle.sparse_attention(q, K, V, P) + (1 - m[:, None]) * oracle.sparse_attention(q, K, V, rest)
+    G = H_q // H_kv
+    tq = torch.from_numpy(q)[:, None, :]                                   # [H_q, 1, d]
+    tk = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(G, dim=0)  # [H_q, L, d]
+    tv = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    dense = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)[:, 0].numpy()
+    np.testing.assert_allclose(mix, dense, rtol=0, atol=1e-12)
+
+
+def test_mass_reads_the_grouped_kv_head():
+    """Heads 0-1 read KV head 0, whose keys point the query at position 0;
+    heads 2-3 read KV head 1, pointing at position 1."""
+    d = 8
+    q = np.zeros((4, d))
+    q[:, 0] = 10.0
+    K = np.zeros((3, 2, d))
+    K[0, 0, 0] = 10.0
+    K[1, 1, 0] = 10.0
+    m, _ = oracle.attention_mass(q, K, [0], 1)
+    assert np.all(m[:2] > 0.999) and np.all(m[2:] < 1e-3), m
