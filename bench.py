@@ -129,9 +129,11 @@ def kernel_roofline(name, avg_ms, work, bound, traffic_key=None):
             "algorithmic_work_per_launch": work, "avg_launch_us": round(avg_ms * 1e3, 3)}
 
 
-def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, traffic_prefix="", flags=0):
+def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, traffic_prefix="", flags=0,
+                 with_mass=False):
     """Graph-replayed decode steps of one workload over nbuf buffer sets:
-    step time, per-kernel durations and rooflines, the dense baseline."""
+    step time, per-kernel durations and rooflines, the dense baseline, and
+    optionally the attention coverage of the steps' selections."""
     from lisa_inputs import decode_inputs
     B, Lctx, M = cfg.B, (cfg.L or cfg.L_hi), cfg.M
     T = torch.bfloat16
@@ -250,6 +252,10 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
         dense_kernel_us = {Lb.lisa_kernel_name(k): round(v * 1e3, 3) for k, v in kd.items()}
         del g_dense
 
+    if with_mass:
+        mass_leg = bench_mass(torch, Lb, cfg, sh, seq, sets, capture, time_graph, kernel_times,
+                              inp["seq_lens"].astype(np.int64), traffic_prefix)
+
     lens = inp["seq_lens"].astype(np.int64)
     indexer = not (flags & Lb.LISA_SLIDING_WINDOW)
     work = {0: (phase_a_bytes(cfg, lens, B, indexer), "hbm"),
@@ -279,11 +285,59 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
                       "dense_decode_kernel_us": dense_kernel_us,
                       "dense_decode_tok_s": round(B / (ms_dense * 1e-3), 1),
                       "speedup_vs_dense_decode": round(ms_dense / ms_step, 3)})
+    if with_mass:
+        extra["attention_mass"] = mass_leg
     del g_main
     sets.clear()
     torch.cuda.empty_cache()
     extra.update(inp=inp, ms_step=ms_step, steps=done, roofline=roof)
     return extra
+
+
+def bench_mass(torch, Lb, cfg, sh, seq, sets, capture, time_graph, kernel_times, lens, traffic_prefix):
+    """Attention coverage (mass and the per-head top-M bound) of every
+    sequence's selection after the decode steps, over the same buffer sets:
+    the call's time, its kernels and the logits kernel's roofline."""
+    B = cfg.B
+    for s in sets:
+        s["mass"] = torch.empty((B, cfg.H_q), dtype=torch.float32, device="cuda")
+        s["bound"] = torch.empty((B, cfg.H_q), dtype=torch.float32, device="cuda")
+        s["ws_mass"] = Lb.workspace(sh, Lb.LISA_OP_MASS, B)
+
+    def mass_call(s):
+        Lb.lisa_attention_mass(sh, B, None, seq, s["q"], s["k_cache"], s["idx"], s["mass"], s["bound"],
+                               s["ws_mass"])
+
+    g = capture(mass_call)
+    ms, _ = time_graph(g)
+    del g
+    kids = (14, 15, 16)
+    kt = kernel_times(mass_call, kids)
+    torch.cuda.synchronize()
+    key_bytes = int(lens.sum()) * cfg.H_kv * cfg.d * 2
+    logits_work = key_bytes + B * cfg.H_q * cfg.d * 2
+    op_bytes = logits_work + B * cfg.M * 4 + 2 * B * cfg.H_q * 4
+    m = sets[0]["mass"].cpu().numpy()
+    bnd = sets[0]["bound"].cpu().numpy()
+    for s in sets:
+        for k in ("mass", "bound", "ws_mass"):
+            del s[k]
+    return {
+        "what": "coverage of each sequence's selected M positions by the dense softmax weights, per query "
+                "head, and the per-head top-M bound (LISA Section 4, Eq. 10); synthetic N(0,1) data, so the "
+                "values are not comparable with trained-model figures",
+        "us_per_call": round(ms * 1e3, 3),
+        "kernel_us": {Lb.lisa_kernel_name(k): round(v * 1e3, 3) for k, v in kt.items()},
+        "call_algorithmic_bytes": op_bytes,
+        "call_hbm_roofline_frac": round(op_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_roofline": {"mass_logits": kernel_roofline("mass_logits", kt[14], logits_work, "hbm",
+                                                           traffic_key=traffic_prefix + "mass_logits"),
+                            "mass_select": kernel_roofline("mass_select", kt[15],
+                                                           SELECT_OPS_PER_KEY * int(lens.sum()) * cfg.H_q, "alu",
+                                                           traffic_key=traffic_prefix + "mass_select")},
+        "mean_mass": round(float(m.mean()), 5),
+        "mean_bound": round(float(bnd.mean()), 5),
+    }
 
 
 # ----------------------------------------------------------------------------
@@ -319,7 +373,8 @@ def main():
         return
     if args.batched_only:
         cb = CONFIGS[2]
-        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense, "batched:")
+        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense, "batched:",
+                          with_mass=True)
         db.pop("inp")
         print(json.dumps({k: v for k, v in db.items()}), flush=True)
         return
@@ -331,7 +386,8 @@ def main():
     extra["pages_context"] = "about 50% end-to-end inference speedup at 16K context (other hardware, whole model)"
     if not args.no_batched:
         cb = CONFIGS[2]
-        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense, "batched:")
+        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense, "batched:",
+                          with_mass=True)
         db.pop("inp")
         bms = db.pop("ms_step")
         db.pop("steps")

@@ -85,6 +85,7 @@ extern "C" {
 #define LISA_OP_TOPK_PREFILL     3
 #define LISA_OP_LINEAR_UPDATE    4
 #define LISA_OP_DENSE_DECODE     5
+#define LISA_OP_MASS             6
 
 /* rows_mode of lisa_indexer_topk() */
 #define LISA_ROWS_DECODE   0
@@ -110,8 +111,9 @@ typedef struct lisa_shape {
 
 /*
  * Bytes of workspace an operation needs.  `n` is the prefill length (tokens
- * per sequence) for LISA_OP_PREFILL / LISA_OP_TOPK_PREFILL / and the token
- * count for LISA_OP_LINEAR_UPDATE; it is ignored otherwise.  Returns 0 for an
+ * per sequence) for LISA_OP_PREFILL / LISA_OP_TOPK_PREFILL, the token count
+ * for LISA_OP_LINEAR_UPDATE and the number of query rows for LISA_OP_MASS;
+ * it is ignored otherwise.  Returns 0 for an
  * invalid shape or op (lisa_last_error() says why).
  */
 size_t lisa_workspace_bytes(const lisa_shape* shape, int op, int32_t n);
@@ -194,11 +196,6 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n,
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Linear-state update over n_tokens tokens ([LISA] Section 3.3 Eq. 3):
- *   S += sum_t phi(k_lin[t])^T v_lin[t],  z += sum_t phi(k_lin[t]).
- * k_lin, v_lin [B, n_tokens, H_L, d] T; S [B, H_L, d, d], z [B, H_L, d] fp32.
- */
-/*
  * Segment state correction at the end of segment t ([LISA] Section 3.3
  * "Segment State Update", Eqs. 6-9), elementwise over S [B, H_L, d, d] and
  * z [B, H_L, d] (fp32, device, 16-byte aligned):
@@ -220,6 +217,11 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n,
 int lisa_segment_correct(const lisa_shape* shape, float* S, float* z, float* S_start, float* z_start,
                          float* mean_S, float* mean_z, int32_t t, float alpha, void* stream);
 
+/*
+ * Linear-state update over n_tokens tokens ([LISA] Section 3.3 Eq. 3):
+ *   S += sum_t phi(k_lin[t])^T v_lin[t],  z += sum_t phi(k_lin[t]).
+ * k_lin, v_lin [B, n_tokens, H_L, d] T; S [B, H_L, d, d], z [B, H_L, d] fp32.
+ */
 int lisa_linear_state_update(const lisa_shape* shape, int32_t n_tokens,
                              const void* k_lin, const void* v_lin,
                              float* S, float* z, void* stream);
@@ -233,6 +235,38 @@ int lisa_linear_state_update(const lisa_shape* shape, int32_t n_tokens,
 int lisa_dense_decode(const lisa_shape* shape, const int32_t* seq_lens,
                       const void* q, const void* k_cache, const void* v_cache,
                       void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Attention coverage of a selection ([LISA] Section 4, "Optimal Window Size
+ * M and Attention Coverage", Eq. 10).  For query row r and query head h
+ * (KV head g = h H_kv / H_q), with dense weights
+ *   a_j = exp(q[r, h] . k[j, g] / sqrt(d)),  j = 0 .. row_len[r]-1,
+ *   mass[r, h]  = sum over the positions in idx[r, :] of a_j / sum_j a_j
+ *   bound[r, h] = sum of the M largest a_j / sum_j a_j
+ * The bound is the coverage of the head's own best M positions, which no
+ * set of M positions shared by the heads can exceed.
+ *
+ * n_rows   query rows, 0 <= n_rows <= 65535 (0: nothing is enqueued).
+ * row_seq  nullable [n_rows] int32, device: the cache sequence of row r
+ *          (NULL: sequence r).  Several rows may share a sequence, e.g.
+ *          sampled prefill rows.
+ * row_len  [n_rows] int32, device: the row attends to cache rows
+ *          0 .. row_len[r]-1 (its own key included); 1 <= row_len[r] <=
+ *          shape.max_len <= cap (not checked on the device).
+ * q        [n_rows, H_q, d] T.       k_cache [*, cap, H_kv, d] T.
+ * idx      [n_rows, M] int32: distinct positions (any order); entries
+ *          outside [0, row_len[r]), such as the -1 padding, are skipped.
+ *          The idx_out of lisa_decode_step or lisa_prefill fits as it is.
+ * mass     [n_rows, H_q] fp32.       bound  nullable [n_rows, H_q] fp32.
+ * ws       workspace of lisa_workspace_bytes(shape, LISA_OP_MASS, n_rows)
+ *          bytes (fp32 logits of every row and head, the bound's index sets).
+ * shape.B is not used; shape.M is the budget of the bound; every other
+ * field as for lisa_decode_step.  Asynchronous on `stream`.
+ */
+int lisa_attention_mass(const lisa_shape* shape, int32_t n_rows, const int32_t* row_seq,
+                        const int32_t* row_len, const void* q, const void* k_cache,
+                        const int32_t* idx, float* mass, float* bound,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Text of a status code. */
 const char* lisa_status_string(int status);

@@ -20,11 +20,11 @@ import torch
 __all__ = [
     "LisaError", "LisaLibraryMissing", "lisa_shape", "make_shape", "library",
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
-    "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_status_string",
-    "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
+    "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_attention_mass",
+    "lisa_status_string", "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
     "workspace", "LISA_F32", "LISA_BF16", "LISA_LINEAR_UNNORMALIZED", "LISA_SLIDING_WINDOW",
     "LISA_OP_DECODE", "LISA_OP_PREFILL", "LISA_OP_TOPK_DECODE", "LISA_OP_TOPK_PREFILL",
-    "LISA_OP_LINEAR_UPDATE", "LISA_OP_DENSE_DECODE", "LISA_ROWS_DECODE", "LISA_ROWS_PREFILL",
+    "LISA_OP_LINEAR_UPDATE", "LISA_OP_DENSE_DECODE", "LISA_OP_MASS", "LISA_ROWS_DECODE", "LISA_ROWS_PREFILL",
     "EXPORTED_SYMBOLS", "LIB_PATH",
 ]
 
@@ -35,13 +35,13 @@ LISA_F32, LISA_BF16 = 0, 1
 LISA_LINEAR_UNNORMALIZED = 1
 LISA_SLIDING_WINDOW = 2
 (LISA_OP_DECODE, LISA_OP_PREFILL, LISA_OP_TOPK_DECODE, LISA_OP_TOPK_PREFILL,
- LISA_OP_LINEAR_UPDATE, LISA_OP_DENSE_DECODE) = range(6)
+ LISA_OP_LINEAR_UPDATE, LISA_OP_DENSE_DECODE, LISA_OP_MASS) = range(7)
 LISA_ROWS_DECODE, LISA_ROWS_PREFILL = 0, 1
 
 EXPORTED_SYMBOLS = (
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
-    "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_status_string", "lisa_last_error",
-    "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
+    "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_attention_mass",
+    "lisa_status_string", "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
 )
 
 
@@ -103,6 +103,8 @@ def library() -> ctypes.CDLL:
     lib.lisa_segment_correct.restype = ctypes.c_int
     lib.lisa_dense_decode.argtypes = [sp, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.lisa_dense_decode.restype = ctypes.c_int
+    lib.lisa_attention_mass.argtypes = [sp, _I32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.lisa_attention_mass.restype = ctypes.c_int
     lib.lisa_status_string.argtypes = [ctypes.c_int]
     lib.lisa_status_string.restype = ctypes.c_char_p
     lib.lisa_last_error.argtypes = []
@@ -237,6 +239,18 @@ def lisa_dense_decode(shape, seq_lens, q, k_cache, v_cache, out, ws, stream=None
         _ptr(k_cache, "k_cache", T), _ptr(v_cache, "v_cache", T), _ptr(out, "out", T),
         _ptr(ws, "ws"), 0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "lisa_dense_decode")
+
+
+def lisa_attention_mass(shape, n_rows, row_seq, row_len, q, k_cache, idx, mass, bound, ws, stream=None):
+    """Attention coverage of each row's selected set, per query head (and the
+    per-head top-M bound when ``bound`` is given)."""
+    T = _act(shape)
+    rc = library().lisa_attention_mass(
+        ctypes.byref(shape), int(n_rows), _ptr(row_seq, "row_seq", torch.int32),
+        _ptr(row_len, "row_len", torch.int32), _ptr(q, "q", T), _ptr(k_cache, "k_cache", T),
+        _ptr(idx, "idx", torch.int32), _ptr(mass, "mass", torch.float32), _ptr(bound, "bound", torch.float32),
+        _ptr(ws, "ws"), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "lisa_attention_mass")
 
 
 def lisa_timing_enable(kernel_id: int, starts=None, stops=None) -> None:

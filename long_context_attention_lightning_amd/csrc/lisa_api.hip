@@ -174,6 +174,23 @@ PrefillWs prefill_ws(const Shape& sh, int n) {
   return w;
 }
 
+struct MassWs {
+  size_t logits, lens, bidx, total;
+};
+
+int64_t mass_logits_ld(const Shape& sh) { return (int64_t)align_up((size_t)sh.max_len, 64); }
+
+MassWs mass_ws(const Shape& sh, int n_rows) {
+  MassWs w;
+  Layout L;
+  const size_t rows = (size_t)n_rows * sh.H_q;
+  w.logits = L.take(rows * mass_logits_ld(sh) * 4);
+  w.lens = L.take(rows * 4);
+  w.bidx = L.take(rows * sh.M * 4);
+  w.total = L.off;
+  return w;
+}
+
 struct TopkWs {
   size_t scores, total;
 };
@@ -208,7 +225,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
     "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine",
     "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose", "select_attention",
-    "segment_correct"};
+    "segment_correct", "mass_logits", "mass_select", "mass_reduce"};
 
 thread_local LaunchEvents g_next_launch;
 
@@ -295,6 +312,9 @@ size_t lisa_workspace_bytes(const lisa_shape* shape, int op, int32_t n) {
     case LISA_OP_TOPK_PREFILL:
       if (check_prefill_len(sh, n) != LISA_OK) return 0;
       return topk_ws(sh, LISA_ROWS_PREFILL, n).total;
+    case LISA_OP_MASS:
+      if (check_decode_len(sh) != LISA_OK || n < 1) return 0;
+      return mass_ws(sh, n).total;
     case LISA_OP_LINEAR_UPDATE:
       return 256;  // no workspace is used; a nonzero size marks a valid shape
     default:
@@ -507,6 +527,38 @@ int lisa_segment_correct(const lisa_shape* shape, float* S, float* z, float* S_s
   a.n_S = (size_t)sh.B * sh.H_L * sh.d * sh.d; a.n_z = (size_t)sh.B * sh.H_L * sh.d;
   a.t = t; a.alpha = alpha;
   LAUNCH(KID_SEGMENT, (hipStream_t)stream, launch_segment_correct(a, (hipStream_t)stream));
+  return LISA_OK;
+}
+
+int lisa_attention_mass(const lisa_shape* shape, int32_t n_rows, const int32_t* row_seq, const int32_t* row_len,
+                        const void* q, const void* k_cache, const int32_t* idx, float* mass, float* bound,
+                        void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if ((rc = check_decode_len(sh))) return rc;
+  if (n_rows < 0 || n_rows > 65535) return fail(LISA_ERR_INVALID_ARG, "n_rows %d outside [0, 65535]", n_rows);
+  if (n_rows == 0) return LISA_OK;
+  OPTIONAL_PTR(row_seq); REQUIRE_PTR(row_len); REQUIRE_PTR(q); REQUIRE_PTR(k_cache); REQUIRE_PTR(idx);
+  REQUIRE_PTR(mass); OPTIONAL_PTR(bound); REQUIRE_PTR(ws);
+  if ((size_t)n_rows * sh.H_q > 0x7fffffffu) return fail(LISA_ERR_UNSUPPORTED, "n_rows * H_q too large");
+  const MassWs w = mass_ws(sh, n_rows);
+  if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  hipStream_t st = (hipStream_t)stream;
+  MassArgs a{};
+  a.sh = sh; a.n_rows = n_rows; a.row_seq = row_seq; a.row_len = row_len; a.q = q; a.k_cache = k_cache;
+  a.idx = idx; a.scale = 1.f / sqrtf((float)sh.d);
+  a.logits = at<float>(ws, w.logits); a.ld = mass_logits_ld(sh); a.lens = at<int32_t>(ws, w.lens);
+  a.bidx = bound ? at<int32_t>(ws, w.bidx) : nullptr; a.mass = mass; a.bound = bound;
+  LAUNCH(KID_MASS_LOGITS, st, launch_mass_logits(a, sh.max_len, st));
+  if (bound) {
+    SelectArgs sa{};
+    sa.n_rows = n_rows * sh.H_q; sa.rows_per_seq = 1; sa.prefill = 0; sa.seq_lens = a.lens;
+    sa.scores = a.logits; sa.ld = a.ld; sa.first_row = 0; sa.stored_rows = 1; sa.M = sh.M;
+    sa.max_len = sh.max_len; sa.idx = at<int32_t>(ws, w.bidx); sa.idx_ld = sh.M; sa.mask = nullptr;
+    LAUNCH(KID_MASS_SELECT, st, launch_select(sa, st));
+  }
+  LAUNCH(KID_MASS_REDUCE, st, launch_mass_reduce(a, st));
   return LISA_OK;
 }
 

@@ -45,7 +45,10 @@ enum KernelId {
   KID_PREFILL_GATE_PREP = 11,
   KID_SELECT_ATTN = 12,
   KID_SEGMENT = 13,
-  KID_COUNT = 14
+  KID_MASS_LOGITS = 14,
+  KID_MASS_SELECT = 15,
+  KID_MASS_REDUCE = 16,
+  KID_COUNT = 17
 };
 
 // ---------------------------------------------------------------------------
@@ -129,6 +132,28 @@ struct SegmentArgs {
   float alpha;
 };
 hipError_t launch_segment_correct(const SegmentArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// attention coverage of a selection (mass and its per-head top-M bound)
+// ---------------------------------------------------------------------------
+struct MassArgs {
+  Shape sh;
+  int n_rows;               // query rows
+  const int32_t* row_seq;   // nullable [n_rows]: cache sequence of each row (NULL: row r)
+  const int32_t* row_len;   // [n_rows]: the row attends to positions 0..len-1
+  const void* q;            // [n_rows, H_q, d]
+  const void* k_cache;      // [*, cap, H_kv, d]
+  const int32_t* idx;       // [n_rows, M] selected positions, -1 padded
+  float scale;              // 1/sqrt(d)
+  float* logits;            // workspace [n_rows * H_q, ld]
+  int64_t ld;
+  int32_t* lens;            // workspace [n_rows * H_q]: row lengths for the bound's select
+  const int32_t* bidx;      // workspace [n_rows * H_q, M]: each head's own top-M
+  float* mass;              // [n_rows, H_q]
+  float* bound;             // nullable [n_rows, H_q]
+};
+hipError_t launch_mass_logits(const MassArgs& a, int max_len, hipStream_t st);
+hipError_t launch_mass_reduce(const MassArgs& a, hipStream_t st);
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);          // split kernel
 hipError_t launch_attention_combine(const AttnArgs& a, hipStream_t st);  // merge (nsplit > 1)

@@ -138,3 +138,23 @@ def test_segment_correct_rejects_bad_args(lib):
     assert rc == -1 and "alpha" in L.lisa_last_error()
     rc = lib.lisa_segment_correct(ctypes.byref(sh), p, None, p, p, p, p, 1, 0.5, None)
     assert rc == -1
+
+
+def test_attention_mass_workspace_and_rejections(lib):
+    sh = _c1()
+    ws = L.lisa_workspace_bytes(sh, L.LISA_OP_MASS, 3)
+    assert ws >= 3 * 28 * 16384 * 4 + 3 * 28 * 2048 * 4  # logits and the bound's index sets
+    assert L.lisa_workspace_bytes(sh, L.LISA_OP_MASS, 0) == 0
+    buf = (ctypes.c_float * 64)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    rc = lib.lisa_attention_mass(ctypes.byref(sh), -1, None, p, p, p, p, p, None, p, 1 << 40, None)
+    assert rc == -1 and "n_rows" in L.lisa_last_error()
+    rc = lib.lisa_attention_mass(ctypes.byref(sh), 3, None, None, p, p, p, p, None, p, 1 << 40, None)
+    assert rc == -1 and "row_len" in L.lisa_last_error()
+    rc = lib.lisa_attention_mass(ctypes.byref(sh), 3, None, p, p, p, p, p, None, p, ws - 1, None)
+    assert rc == -3
+    assert lib.lisa_attention_mass(ctypes.byref(sh), 0, None, None, None, None, None, None, None, None, 0,
+                                   None) == 0  # no rows: nothing to do
+    bad = _c1(max_len=0)
+    rc = lib.lisa_attention_mass(ctypes.byref(bad), 3, None, p, p, p, p, p, None, p, 1 << 40, None)
+    assert rc == -1 and "max_len" in L.lisa_last_error()
