@@ -4,35 +4,56 @@
 // the selected positions, and the share of the head's own M largest weights
 // (the bound no shared M-set can exceed).
 //
-//  1. k_mass_logits: the fp32 logits q_h . k_j / sqrt(d) of every key of the
-//     row, for the G query heads of one KV head per block, so each key row
-//     is read once per row (HBM-bound on the key reads).  Four lanes share a
-//     key: each reads a quarter of the row in 16-byte pieces (64 contiguous
-//     bytes per key and load), the query heads come from LDS as broadcasts,
-//     and a quad reduction finishes each dot product.
-//  2. top-M of each head's logit row (the exp is monotone, so the M largest
+//  1. logits: q_h . k_j / sqrt(d) in fp32 for every key of the row and the G
+//     query heads of one KV head per block, so each key row is read once
+//     per row (HBM-bound on the key reads).  Each block also leaves, per
+//     head, the max of its 256 logits and the sum of exp(logit - max), so
+//     the row's softmax normaliser needs no second pass over the logits.
+//       bf16: the logits are MFMA tiles [16 keys x 16 heads] (heads past G
+//       are zero columns), key rows loaded straight into the A operand and
+//       the query heads held as B operands for the whole block.
+//       fp32: four lanes share a key, each reading a quarter of the row;
+//       query heads come from LDS as broadcasts; a quad sum finishes each
+//       dot product.
+//  2. top-M of each head's logit row (exp is monotone, so the M largest
 //     logits carry the M largest weights), only when the bound is asked for.
-//  3. k_mass_reduce: per (row, head) the maximum, the sum of exp(s - max)
-//     over the row, and the same sum over the selected and the bound sets.
+//  3. reduce: per (row, head) the blocks' (max, sum) pairs are merged, and
+//     exp(logit - max) is summed over the selected and the bound positions.
 #include <math.h>
 
 #include "lisa_common.h"
 #include "lisa_kernels.h"
+#include "lisa_mfma.h"
 
 namespace lisa {
 
 constexpr int MS_KEYS = 256;  // keys per logits block (4 waves x 4 passes x 16 keys)
 
+// (m, s) := the pair for the union of two key sets, where each pair is the
+// max logit of its set and the sum of exp(logit - max) over the set
+// (m = -inf, s = 0 for an empty set).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * expf(m - mn) + s2 * expf(m2 - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void lse_merge_xor(float& m, float& s, int mask) {
+  const float m2 = __shfl_xor(m, mask, WAVE), s2 = __shfl_xor(s, mask, WAVE);
+  lse_merge(m, s, m2, s2);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_mass_logits(MassArgs a) {
   __shared__ float qs[8][D];
   const Shape& sh = a.sh;
-  const int r = blockIdx.x, kvh = blockIdx.y;
+  const int r = blockIdx.z, kvh = blockIdx.x;
   const int G = sh.H_q / sh.H_kv;
   const int len = a.row_len[r];
   const int tid = threadIdx.x;
-  if (blockIdx.z == 0 && tid < G) a.lens[(size_t)r * sh.H_q + kvh * G + tid] = len;
-  const int j0 = MS_KEYS * blockIdx.z;
+  if (blockIdx.y == 0 && tid < G) a.lens[(size_t)r * sh.H_q + kvh * G + tid] = len;
+  const int j0 = MS_KEYS * blockIdx.y;
   if (j0 >= len) return;
   const int seq = a.row_seq ? a.row_seq[r] : r;
   const T* qr = (const T*)a.q + ((size_t)r * sh.H_q + (size_t)kvh * G) * D;
@@ -46,6 +67,9 @@ __global__ __launch_bounds__(256) void k_mass_logits(MassArgs a) {
   const size_t kstride = (size_t)sh.H_kv * D;
   const float scale = a.scale;
   float* lrow = a.logits + ((size_t)r * sh.H_q + (size_t)kvh * G) * a.ld;
+  float pm[8], ps[8];  // running (max, sum) per head over this quad's keys
+#pragma unroll
+  for (int h = 0; h < 8; ++h) { pm[h] = -INFINITY; ps[h] = 0.f; }
 #pragma unroll 1
   for (int p = 0; p < 4; ++p) {
     const int jb = j0 + 64 * wave + 16 * p;
@@ -72,9 +96,120 @@ __global__ __launch_bounds__(256) void k_mass_logits(MassArgs a) {
 #pragma unroll
     for (int h = 0; h < 8; ++h) {
       if (h >= G) break;
-      const float s = group_sum(acc[h], 4);  // the four quarters of key j
-      if (j < len && (h & 3) == kq) lrow[(size_t)h * a.ld + j] = s * scale;
+      const float s = group_sum(acc[h], 4) * scale;  // the four quarters of key j
+      if (j < len) {
+        if ((h & 3) == kq) lrow[(size_t)h * a.ld + j] = s;
+        lse_merge(pm[h], ps[h], s, 1.f);
+      }
     }
+  }
+  // merge the 16 quads of the wave (all four lanes of a quad hold the same
+  // pairs), then the four waves
+  __shared__ float wm[4][8], wsum[4][8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    if (h >= G) break;
+    lse_merge_xor(pm[h], ps[h], 4);
+    lse_merge_xor(pm[h], ps[h], 8);
+    lse_merge_xor(pm[h], ps[h], 16);
+    lse_merge_xor(pm[h], ps[h], 32);
+    if (lane == 0) { wm[wave][h] = pm[h]; wsum[wave][h] = ps[h]; }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float m = wm[0][tid], sm = wsum[0][tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) lse_merge(m, sm, wm[w][tid], wsum[w][tid]);
+    a.part[((size_t)r * sh.H_q + (size_t)kvh * G + tid) * a.part_ld + blockIdx.y] = make_float2(m, sm);
+  }
+}
+
+// bf16 logits on MFMA.  Wave w of the block takes keys j0 + 64 w .. + 63 as
+// four 16-key tiles; lane (r16, g) loads 16 bytes of key r16's row per
+// 32-element step (A operand) and holds query head r16 as B operands, so the
+// accumulator gives lane (r16, g) the logits of keys 4 g .. 4 g + 3 of the
+// tile for head r16.
+template <int D>
+__global__ __launch_bounds__(256) void k_mass_logits_mfma(MassArgs a) {
+  __shared__ float wm[4][16], wsum[4][16];
+  const Shape& sh = a.sh;
+  const int r = blockIdx.z, kvh = blockIdx.x;
+  const int G = sh.H_q / sh.H_kv;
+  const int len = a.row_len[r];
+  const int tid = threadIdx.x;
+  if (blockIdx.y == 0 && tid < G) a.lens[(size_t)r * sh.H_q + kvh * G + tid] = len;
+  const int j0 = MS_KEYS * blockIdx.y;
+  if (j0 >= len) return;
+  const int seq = a.row_seq ? a.row_seq[r] : r;
+  const int lane = tid & (WAVE - 1), wave = tid / WAVE, r16 = lane & 15, g = lane >> 4;
+  constexpr int KS = D / 32;
+  bf16x8 qf[KS];
+  {
+    const bf16_t* qh = (const bf16_t*)a.q + ((size_t)r * sh.H_q + (size_t)kvh * G + min(r16, G - 1)) * D + 8 * g;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint4 v = ld16(qh + 32 * k);
+      if (r16 >= G) v = make_uint4(0u, 0u, 0u, 0u);
+      qf[k] = as_bf16x8(v);
+    }
+  }
+  const bf16_t* kbase = (const bf16_t*)a.k_cache + ((size_t)seq * sh.cap * sh.H_kv + kvh) * D + 8 * g;
+  const size_t kstride = (size_t)sh.H_kv * D;
+  const int jw = j0 + 64 * wave;
+  uint4 kf[4][KS];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int key = jw + 16 * t + r16;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      kf[t][k] = key < len ? ld16(kbase + (size_t)key * kstride + 32 * k) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  const float scale = a.scale;
+  float v[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int k = 0; k < KS; ++k) acc = mfma16(as_bf16x8(kf[t][k]), qf[k], acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[t][e] = acc[e] * scale;
+  }
+  // stores: keys jw + 16 t + 4 g + e of head r16
+  float* lrow = a.logits + ((size_t)r * sh.H_q + (size_t)kvh * G + r16) * a.ld;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k0 = jw + 16 * t + 4 * g;
+    if (r16 < G) {
+      if (k0 + 3 < len) {
+        *reinterpret_cast<float4*>(lrow + k0) = make_float4(v[t][0], v[t][1], v[t][2], v[t][3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (k0 + e < len) lrow[k0 + e] = v[t][e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (k0 + e < len) mx = fmaxf(mx, v[t][e]);
+  }
+  float sm = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (jw + 16 * t + 4 * g + e < len) sm += expf(v[t][e] - mx);
+  }
+  lse_merge_xor(mx, sm, 16);  // the four lane groups g of head r16
+  lse_merge_xor(mx, sm, 32);
+  if (g == 0) { wm[wave][r16] = mx; wsum[wave][r16] = sm; }
+  __syncthreads();
+  if (tid < G) {
+    float m = wm[0][tid], s2 = wsum[0][tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) lse_merge(m, s2, wm[w][tid], wsum[w][tid]);
+    a.part[((size_t)r * sh.H_q + (size_t)kvh * G + tid) * a.part_ld + blockIdx.y] = make_float2(m, s2);
   }
 }
 
@@ -99,17 +234,26 @@ __device__ __forceinline__ float block_max256(float v, float* red) {
 }
 
 __global__ __launch_bounds__(256) void k_mass_reduce(MassArgs a) {
-  __shared__ float red[4];
+  __shared__ float red[4], rm[4], rs[4];
   const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int H_q = a.sh.H_q, M = a.sh.M;
   const int len = a.row_len[r];
   const float* s = a.logits + ((size_t)r * H_q + h) * a.ld;
-  float mx = -INFINITY;
-  for (int j = tid; j < len; j += 256) mx = fmaxf(mx, s[j]);
-  mx = block_max256(mx, red);
-  float z = 0.f;
-  for (int j = tid; j < len; j += 256) z += expf(s[j] - mx);
-  z = block_sum256(z, red);
+  // the row's (max, sum of exp) from the logits blocks' pairs
+  const int nkb = (len + MS_KEYS - 1) / MS_KEYS;
+  const float2* part = a.part + ((size_t)r * H_q + h) * a.part_ld;
+  float mx = -INFINITY, z = 0.f;
+  for (int k = tid; k < nkb; k += 256) {
+    const float2 p = part[k];
+    lse_merge(mx, z, p.x, p.y);
+  }
+#pragma unroll
+  for (int mask = 1; mask < WAVE; mask <<= 1) lse_merge_xor(mx, z, mask);
+  if ((tid & (WAVE - 1)) == 0) { rm[tid / WAVE] = mx; rs[tid / WAVE] = z; }
+  __syncthreads();
+  mx = rm[0]; z = rs[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) lse_merge(mx, z, rm[w], rs[w]);
   float num = 0.f;
   const int32_t* sel = a.idx + (size_t)r * M;
   for (int k = tid; k < M; k += 256) {
@@ -132,20 +276,24 @@ __global__ __launch_bounds__(256) void k_mass_reduce(MassArgs a) {
   }
 }
 
+int mass_key_blocks(int max_len) { return (max_len + MS_KEYS - 1) / MS_KEYS; }
+
 hipError_t launch_mass_logits(const MassArgs& a, int max_len, hipStream_t st) {
-  const dim3 grid((unsigned)a.n_rows, (unsigned)a.sh.H_kv, (unsigned)((max_len + MS_KEYS - 1) / MS_KEYS));
+  // KV heads fastest: the blocks that read the H_kv parts of the same key
+  // rows are dispatched together
+  const dim3 grid((unsigned)a.sh.H_kv, (unsigned)mass_key_blocks(max_len), (unsigned)a.n_rows);
   const bool bf = a.sh.dtype == 1;
   switch (a.sh.d) {
     case 32:
-      if (bf) klaunch((k_mass_logits<bf16_t, 32>), grid, dim3(256), 0, st, a);
+      if (bf) klaunch((k_mass_logits_mfma<32>), grid, dim3(256), 0, st, a);
       else klaunch((k_mass_logits<float, 32>), grid, dim3(256), 0, st, a);
       break;
     case 64:
-      if (bf) klaunch((k_mass_logits<bf16_t, 64>), grid, dim3(256), 0, st, a);
+      if (bf) klaunch((k_mass_logits_mfma<64>), grid, dim3(256), 0, st, a);
       else klaunch((k_mass_logits<float, 64>), grid, dim3(256), 0, st, a);
       break;
     default:
-      if (bf) klaunch((k_mass_logits<bf16_t, 128>), grid, dim3(256), 0, st, a);
+      if (bf) klaunch((k_mass_logits_mfma<128>), grid, dim3(256), 0, st, a);
       else klaunch((k_mass_logits<float, 128>), grid, dim3(256), 0, st, a);
       break;
   }

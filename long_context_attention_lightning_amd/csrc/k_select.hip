@@ -79,21 +79,31 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
   select_one<THREADS, ITEMS, LKEYS>(a, r / a.rows_per_seq, r % a.rows_per_seq, sm, ks);
 }
 
-// Prefill rows of up to 256 * 64 positions: 256 threads per row, with 16,
-// 32 or 64 scores per thread chosen per row by its length (the work of a
-// row scales with the items per thread, not with its length), longest rows
-// first so that the short ones fill the tail of the launch.  Keys are
-// recomputed from the score row, so the block holds only the histogram and
-// several blocks share a CU.
-__global__ __launch_bounds__(256) void k_select_prefill(SelectArgs a) {
+// Many rows of up to 256 * 64 positions (prefill rows, or a large batch of
+// decode rows): 256 threads per row, with 16, 32 or 64 scores per thread
+// chosen per row by its length (the work of a row scales with the items per
+// thread, not with its length); prefill rows go longest first so that the
+// short ones fill the tail of the launch.  Keys are recomputed from the
+// score row, so the block holds only the histogram and several blocks share
+// a CU.
+__global__ __launch_bounds__(256) void k_select_rows256(SelectArgs a) {
   __shared__ SelShared<256 / WAVE> sm;
   __shared__ KeyStore<256, 16, false> ks16;
   __shared__ KeyStore<256, 32, false> ks32;
   __shared__ KeyStore<256, 64, false> ks64;
-  const int n = a.rows_per_seq;
-  const int b = blockIdx.x / n, t = n - 1 - (int)(blockIdx.x % n);
-  if (t < 256 * 16) select_one<256, 16, false>(a, b, t, sm, ks16);
-  else if (t < 256 * 32) select_one<256, 32, false>(a, b, t, sm, ks32);
+  int b, t, len;
+  if (a.prefill) {
+    const int n = a.rows_per_seq;
+    b = blockIdx.x / n;
+    t = n - 1 - (int)(blockIdx.x % n);
+    len = t + 1;
+  } else {
+    b = blockIdx.x;
+    t = 0;
+    len = a.seq_lens[b];
+  }
+  if (len <= 256 * 16) select_one<256, 16, false>(a, b, t, sm, ks16);
+  else if (len <= 256 * 32) select_one<256, 32, false>(a, b, t, sm, ks32);
   else select_one<256, 64, false>(a, b, t, sm, ks64);
 }
 
@@ -115,7 +125,9 @@ hipError_t launch_window_index(int32_t* idx, int B, int n, int M, hipStream_t st
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
   const dim3 grid((unsigned)a.n_rows);
-  if (a.prefill && a.max_len > 256 * 16 && a.max_len <= 256 * 64) klaunch(k_select_prefill, grid, dim3(256), 0, st, a);
+  // one 1024-thread block per row while the rows do not fill the chip
+  const bool many = a.prefill || a.n_rows >= 512;
+  if (many && a.max_len > 256 * 16 && a.max_len <= 256 * 64) klaunch(k_select_rows256, grid, dim3(256), 0, st, a);
   else if (a.max_len <= 256 * 16) klaunch((k_select<256, 16, true>), grid, dim3(256), 0, st, a);
   else if (a.max_len <= 1024 * 16) klaunch((k_select<1024, 16, true>), grid, dim3(1024), 0, st, a);
   else if (a.max_len <= 1024 * 32) klaunch((k_select<1024, 32, true>), grid, dim3(1024), 0, st, a);

@@ -175,7 +175,7 @@ PrefillWs prefill_ws(const Shape& sh, int n) {
 }
 
 struct MassWs {
-  size_t logits, lens, bidx, total;
+  size_t logits, lens, bidx, part, total;
 };
 
 int64_t mass_logits_ld(const Shape& sh) { return (int64_t)align_up((size_t)sh.max_len, 64); }
@@ -187,6 +187,7 @@ MassWs mass_ws(const Shape& sh, int n_rows) {
   w.logits = L.take(rows * mass_logits_ld(sh) * 4);
   w.lens = L.take(rows * 4);
   w.bidx = L.take(rows * sh.M * 4);
+  w.part = L.take(rows * mass_key_blocks(sh.max_len) * 8);
   w.total = L.off;
   return w;
 }
@@ -550,6 +551,7 @@ int lisa_attention_mass(const lisa_shape* shape, int32_t n_rows, const int32_t* 
   a.idx = idx; a.scale = 1.f / sqrtf((float)sh.d);
   a.logits = at<float>(ws, w.logits); a.ld = mass_logits_ld(sh); a.lens = at<int32_t>(ws, w.lens);
   a.bidx = bound ? at<int32_t>(ws, w.bidx) : nullptr; a.mass = mass; a.bound = bound;
+  a.part = at<float2>(ws, w.part); a.part_ld = mass_key_blocks(sh.max_len);
   LAUNCH(KID_MASS_LOGITS, st, launch_mass_logits(a, sh.max_len, st));
   if (bound) {
     SelectArgs sa{};

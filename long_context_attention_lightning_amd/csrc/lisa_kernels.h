@@ -149,9 +149,12 @@ struct MassArgs {
   int64_t ld;
   int32_t* lens;            // workspace [n_rows * H_q]: row lengths for the bound's select
   const int32_t* bidx;      // workspace [n_rows * H_q, M]: each head's own top-M
+  float2* part;             // workspace [n_rows * H_q, part_ld]: (max, sum of exp) per 256-key block
+  int64_t part_ld;
   float* mass;              // [n_rows, H_q]
   float* bound;             // nullable [n_rows, H_q]
 };
+int mass_key_blocks(int max_len);
 hipError_t launch_mass_logits(const MassArgs& a, int max_len, hipStream_t st);
 hipError_t launch_mass_reduce(const MassArgs& a, hipStream_t st);
 

@@ -99,3 +99,13 @@ def test_select_prefill_rows_all_item_bands():
                                                                                     M), M))]
     print(f"[prefill rows] checked={len(rows)} mismatched={len(bad)}", flush=True)
     assert not bad, bad[:5]
+
+
+def test_select_many_decode_rows_one_launch():
+    """600 decode rows (a launch of at least 512 rows takes 256-thread blocks
+    with per-row item counts) of lengths spread over 1..16384."""
+    r = np.random.default_rng(12)
+    lens = np.concatenate([[1, 2047, 2048, 2049, 4096, 4097, 8192, 8193, 16384], r.integers(1, 16385, 591)])
+    rows = [(np.round(r.standard_normal(int(n)) * 8) / 8).astype(np.float32) for n in lens]
+    rows[5][:] = 0.0  # all ties
+    _check(rows, 2048, "600 decode rows")
