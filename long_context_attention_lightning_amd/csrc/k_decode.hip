@@ -359,45 +359,49 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
   const int r = blockIdx.x / sh.H_q;
   const int g = h / G, hh = h % G;
   const int b = r / a.rows_per_seq, t = r % a.rows_per_seq;
-  const int len = a.prefill ? t + 1 : a.seq_lens[b];
-  const int m = a.dense ? len : min(sh.M, len);
-  const int nvalid = (m + a.split_len - 1) / a.split_len;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1);
   const int dim = min(tid, D - 1);
   const int GD = G * D, PS = GD + 2 * G;
+  const size_t oi = ((size_t)r * sh.H_q + h) * D + dim;
+  // Every load is issued before the row length arrives: the partials of all
+  // nsplit splits (those past the row's valid splits are masked below), the
+  // gate partials and the linear output.
+  const int len = a.prefill ? t + 1 : a.seq_lens[b];
   const float* p0 = a.part + ((size_t)r * sh.H_kv + g) * a.nsplit * PS;
   float ov[AT_MAX_SPLITS];
 #pragma unroll
-  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) ov[sp] = p0[(size_t)min(sp, nvalid - 1) * PS + hh * D + dim];
-  const int ls = min(lane, nvalid - 1);
-  const float m_l = p0[(size_t)ls * PS + GD + hh];
-  const float l_l = p0[(size_t)ls * PS + GD + G + hh];
-  float g_l = 0.f;
+  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) ov[sp] = p0[(size_t)min(sp, a.nsplit - 1) * PS + hh * D + dim];
+  const int ls = min(lane, a.nsplit - 1);
+  const float m_raw = p0[(size_t)ls * PS + GD + hh];
+  const float l_raw = p0[(size_t)ls * PS + GD + G + hh];
+  float g_l = 0.f, ol = 0.f, den = 1.f;
   if (a.gate_part) {
     const float* gp = a.gate_part + (size_t)r * a.gate_chunks * sh.H_q + h;
     const float g0 = gp[(size_t)min(lane, a.gate_chunks - 1) * sh.H_q];
     const float g1 = gp[(size_t)min(lane + WAVE, a.gate_chunks - 1) * sh.H_q];
     g_l = (lane < a.gate_chunks ? g0 : 0.f) + (lane + WAVE < a.gate_chunks ? g1 : 0.f);
     for (int c = lane + 2 * WAVE; c < a.gate_chunks; c += WAVE) g_l += gp[(size_t)c * sh.H_q];
+    ol = a.o_lin[oi];
+    if (a.lin_den) den = a.lin_den[(size_t)r * sh.H_q + h];
   }
+  const int m = a.dense ? len : min(sh.M, len);
+  const int nvalid = (m + a.split_len - 1) / a.split_len;
   const bool live = lane < nvalid;
-  const float mx = group_max(live ? m_l : -INFINITY, WAVE);
-  const float f_l = live ? scale_from(m_l, mx) : 0.f;  // weight of split `lane`
-  const float l = group_sum(l_l * f_l, WAVE);
+  const float mx = group_max(live ? m_raw : -INFINITY, WAVE);
+  const float f_l = live ? scale_from(m_raw, mx) : 0.f;  // weight of split `lane`
+  const float l = group_sum(live ? l_raw * f_l : 0.f, WAVE);
   float o = 0.f;
 #pragma unroll
   for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) {
     const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_l), sp));
-    o = fmaf(ov[sp], f, o);
+    o = fmaf(sp < nvalid ? ov[sp] : 0.f, f, o);  // stale partials past the row never enter
   }
+  const float gsum = group_sum(g_l, WAVE);  // every lane of the wave takes part
   if (tid >= D) return;
   o = o / l;
-  const size_t oi = ((size_t)r * sh.H_q + h) * D + tid;
   if (a.gate_part) {
-    const float gv = sigmoidf(group_sum(g_l, WAVE));
-    float ol = a.o_lin[oi];
-    if (a.lin_den) ol = ol / a.lin_den[(size_t)r * sh.H_q + h];
-    o = gv * o + (1.f - gv) * ol;
+    const float gv = sigmoidf(gsum);
+    o = gv * o + (1.f - gv) * (ol / den);
   }
   st1<T>((T*)a.out + oi, o);
 }
