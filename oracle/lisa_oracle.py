@@ -42,6 +42,14 @@ function that uses them:
   Coverage", Eq. 10): the share of a query head's dense causal softmax
   weight that falls on a selected set; its upper bound is the share of that
   head's own M largest weights.
+* Indexer training objective ([LISA] §3.2 Stage 2, Eq. 2): per indexer head
+  j and row t, KL(T || softmax(S)) over the causal keys, where S is head j's
+  unweighted ReLU score row and T the mean of the causal attention rows of
+  the teacher heads j*H_q/H_I .. (j+1)*H_q/H_I - 1 (the layer's own query
+  heads; a sum of distributions renormalised is their mean).  Candidate
+  dropout ([LISA] §3.2 Stage 2): the top C candidates (1.2 M in the paper),
+  each dropped when its caller-drawn uniform is below p, and the M best of
+  the survivors kept.
 """
 from __future__ import annotations
 
@@ -53,7 +61,7 @@ __all__ = [
     "phi", "index_scores", "select_topm", "sparse_attention", "gate",
     "linear_recurrent", "linear_rows", "linear_chunked", "linear_state_update",
     "prefill", "prefill_rows", "decode_step", "dense_decode", "window_positions",
-    "segment_correct", "attention_mass",
+    "segment_correct", "attention_mass", "indexer_kl", "candidate_dropout",
 ]
 
 
@@ -457,3 +465,71 @@ def attention_mass(q, K, P, M: int):
         mass[h] = w[P].sum() / total
         bound[h] = np.sort(w)[::-1][: int(M)].sum() / total
     return mass, bound
+
+
+# ----------------------------------------------------------------------------
+# indexer training ([LISA] §3.2 Stage 2, Eq. 2 and the candidate dropout)
+# ----------------------------------------------------------------------------
+def _log_softmax(x) -> np.ndarray:
+    x = _f64(x)
+    m = x.max()
+    return x - (m + np.log(np.exp(x - m).sum()))
+
+
+def indexer_kl(q, K, q_idx, k_idx, rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Per-row, per-indexer-head KL of Eq. 2 for one sequence.
+
+    q: [n, H_q, d]; K: [n, H_kv, d] (the teacher's queries and keys);
+    q_idx: [n, H_I, d_I]; k_idx: [n, H_Ik, d_I].  For row t and indexer head
+    j, over the keys 0..t:
+      S_k      = max(0, q_idx[t, j] . k_idx[k, j*H_Ik//H_I])    (no head weight)
+      log Q    = log softmax(S)
+      A_h      = softmax(q[t, h] . K[:, h*H_kv//H_q] / sqrt(d)) for the G_T =
+                 H_q/H_I teacher heads h = j*G_T .. (j+1)*G_T - 1
+      T        = (sum_h A_h) / G_T                   (the renormalised sum)
+      KL[t, j] = sum_k T_k (log T_k - log Q_k), with 0 log 0 = 0.
+    Returns [len(rows), H_I].  The loss of Eq. 2 is the mean over rows and
+    heads.
+    """
+    q = _f64(q)
+    n, H_q, d = q.shape
+    H_kv = K.shape[1]
+    H_I = q_idx.shape[1]
+    H_Ik = k_idx.shape[1]
+    assert H_q % H_I == 0, "teacher heads split evenly over the indexer heads"
+    G_T = H_q // H_I
+    rows = list(range(n)) if rows is None else list(rows)
+    out = np.zeros((len(rows), H_I))
+    for i, t in enumerate(rows):
+        for j in range(H_I):
+            S = np.maximum(0.0, _f64(k_idx[: t + 1, (j * H_Ik) // H_I]) @ _f64(q_idx[t, j]))
+            logQ = _log_softmax(S)
+            T = np.zeros(t + 1)
+            for h in range(j * G_T, (j + 1) * G_T):
+                a = _f64(K[: t + 1, (h * H_kv) // H_q]) @ q[t, h] / np.sqrt(d)
+                T += np.exp(_log_softmax(a))
+            T /= G_T
+            pos = T > 0
+            out[i, j] = float(np.sum(T[pos] * (np.log(T[pos]) - logQ[pos])))
+    return out
+
+
+def candidate_dropout(scores, M: int, n_cand: int, p, u) -> np.ndarray:
+    """Indexer candidates with dropout, ascending positions.
+
+    The top C = min(L, n_cand) positions by (score desc, position desc) are
+    the candidates (the paper takes n_cand = 1.2 M early in training);
+    candidate j is dropped when u[j] < p (u holds the caller's uniform draws
+    in [0, 1), one per position; p is the dropout ratio, annealed by the
+    caller); of the survivors the min(M, #survivors) best in the same order
+    are kept.
+    """
+    s = np.asarray(scores)
+    u = np.asarray(u)
+    C = min(s.shape[0], int(n_cand))
+    cand = select_topm(s, C)
+    surv = np.array([j for j in cand if u[j] >= p], dtype=np.int64)
+    if surv.size <= M:
+        return surv
+    keep = select_topm(s[surv], M)   # indices into surv, in survivor order
+    return np.sort(surv[keep])

@@ -610,3 +610,87 @@ def test_mass_reads_the_grouped_kv_head():
     K[1, 1, 0] = 10.0
     m, _ = oracle.attention_mass(q, K, [0], 1)
     assert np.all(m[:2] > 0.999) and np.all(m[2:] < 1e-3), m
+
+
+# ---------------------------------------------------------------------------
+# indexer training objective ([LISA] §3.2 Stage 2, Eq. 2) and candidate dropout
+# ---------------------------------------------------------------------------
+def test_indexer_kl_by_hand():
+    """Row 1 has keys 0 and 1: teacher logits 0 and ln 2 give T = (1/3, 2/3);
+    equal indexer scores give Q = (1/2, 1/2).  Row 0 has one key: KL = 0."""
+    d, dI = 4, 2
+    q = np.zeros((2, 1, d))
+    q[:, 0, 0] = 2.0                      # q . k / sqrt(d) = k[0]
+    K = np.zeros((2, 1, d))
+    K[:, 0, 0] = [0.0, math.log(2.0)]
+    qi = np.zeros((2, 1, dI))
+    qi[:, 0, 0] = 1.0
+    ki = np.zeros((2, 1, dI))
+    ki[:, 0, 0] = 1.0                     # S = (1, 1)
+    kl = oracle.indexer_kl(q, K, qi, ki)
+    want = (1 / 3) * math.log((1 / 3) / (1 / 2)) + (2 / 3) * math.log((2 / 3) / (1 / 2))
+    assert kl[0, 0] == pytest.approx(0.0, abs=1e-15)
+    assert kl[1, 0] == pytest.approx(want, abs=1e-15)
+
+
+def test_indexer_kl_zero_when_the_indexer_matches_the_teacher():
+    """One teacher head per indexer head, index query q/sqrt(d) and index key
+    k with positive entries: ReLU is inactive and S equals the teacher's
+    logits, so the two distributions coincide."""
+    r = np.random.default_rng(14)
+    n, d = 30, 8
+    q = r.random((n, 2, d))
+    K = r.random((n, 1, d))
+    kl = oracle.indexer_kl(q, K, q / np.sqrt(d), K)
+    np.testing.assert_allclose(kl, 0.0, atol=1e-14)
+
+
+def test_indexer_kl_matches_torch_kl_div():
+    """Grouped teacher (three heads per indexer head, two KV heads, one shared
+    index key) against torch: softmax / log_softmax / kl_div in float64."""
+    r = np.random.default_rng(15)
+    n, H_q, H_kv, d, H_I, dI = 25, 6, 2, 16, 2, 8
+    q = r.standard_normal((n, H_q, d))
+    K = r.standard_normal((n, H_kv, d))
+    qi = r.standard_normal((n, H_I, dI))
+    ki = r.standard_normal((n, 1, dI))
+    kl = oracle.indexer_kl(q, K, qi, ki)
+    tq, tk, tqi, tki = (torch.from_numpy(a) for a in (q, K, qi, ki))
+    for t in range(n):
+        for j in range(H_I):
+            heads = range(3 * j, 3 * j + 3)
+            T = sum(torch.softmax(tk[: t + 1, h * H_kv // H_q] @ tq[t, h] / math.sqrt(d), 0) for h in heads) / 3
+            logQ = torch.log_softmax(torch.relu(tki[: t + 1, 0] @ tqi[t, j]), 0)
+            want = torch.nn.functional.kl_div(logQ, T, reduction="sum").item()
+            assert kl[t, j] == pytest.approx(want, abs=1e-12), (t, j)
+    assert np.all(kl >= -1e-15)
+
+
+def _dropout_brute(s, M, C, p, u):
+    order = sorted(range(len(s)), key=lambda j: (-s[j], -j))
+    surv = [j for j in order[:C] if u[j] >= p]
+    return sorted(surv[:M])
+
+
+def test_candidate_dropout_brute_force():
+    r = np.random.default_rng(16)
+    for trial in range(300):
+        L = int(r.integers(1, 12))
+        M = int(r.integers(1, 6))
+        C = int(r.integers(M, 9))
+        s = (np.round(r.standard_normal(L) * 2) / 2).astype(np.float32)  # ties
+        u = r.random(L).astype(np.float32)
+        p = np.float32(r.choice([0.0, 0.2, 0.5, 1.0]))
+        got = oracle.candidate_dropout(s.astype(np.float64), M, C, p, u)
+        assert got.tolist() == _dropout_brute(s.tolist(), M, C, p, u.tolist()), (trial, s, u, p, M, C)
+
+
+def test_candidate_dropout_special_cases():
+    r = np.random.default_rng(17)
+    s = r.standard_normal(500)
+    u = r.random(500)
+    np.testing.assert_array_equal(oracle.candidate_dropout(s, 40, 48, 0.0, u), oracle.select_topm(s, 40))
+    assert oracle.candidate_dropout(s, 40, 48, 1.0, u).size == 0
+    got = oracle.candidate_dropout(s, 40, 48, 0.2, u)
+    cand = set(oracle.select_topm(s, 48).tolist())
+    assert set(got.tolist()) <= cand and np.all(u[got] >= 0.2) and got.size == min(40, sum(u[j] >= 0.2 for j in cand))
