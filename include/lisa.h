@@ -268,6 +268,29 @@ int lisa_attention_mass(const lisa_shape* shape, int32_t n_rows, const int32_t* 
                         const int32_t* idx, float* mass, float* bound,
                         void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Indexer training objective ([LISA] Section 3.2 Stage 2, Eq. 2), forward
+ * only, over the n prefill rows of every sequence.  For row t and indexer
+ * head j, over the keys k = 0..t:
+ *   S_k  = max(0, q_idx[t, j] . k_idx[k, j H_Ik / H_I])     (no head weight)
+ *   Q    = softmax(S)
+ *   T    = mean over the teacher heads h = j G_T .. (j+1) G_T - 1,
+ *          G_T = H_q / H_I, of softmax_k(q[t, h] . k[k, h H_kv / H_q] / sqrt(d))
+ *          (the sum of the teacher rows renormalised)
+ *   kl_out[b, t, j] = KL(T || Q) = sum_k T_k (ln T_k - ln Q_k)
+ *   loss_out[0]     = the mean of kl_out over b, t and j          (Eq. 2)
+ * The teacher is the layer's own full attention: q [B, n, H_q, d] and
+ * k_cache [B, cap, H_kv, d] (rows 0..n-1); q_idx [B, n, H_I, d_I] and
+ * k_idx_cache [B, cap, H_Ik, d_I] (rows 0..n-1) are the indexer's.
+ * kl_out [B, n, H_I] fp32; loss_out nullable [1] fp32.  Requires H_q to be a
+ * multiple of H_I.  bf16 with d = 128, d_I = 64 and each teacher group inside
+ * one KV head runs on the matrix cores; other shapes run a slower vector
+ * kernel.  No workspace; asynchronous on `stream`.
+ */
+int lisa_indexer_kl(const lisa_shape* shape, int32_t n, const void* q, const void* k_cache,
+                    const void* q_idx, const void* k_idx_cache, float* kl_out, float* loss_out,
+                    void* stream);
+
 /* Text of a status code. */
 const char* lisa_status_string(int status);
 

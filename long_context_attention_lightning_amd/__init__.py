@@ -21,7 +21,7 @@ __all__ = [
     "LisaError", "LisaLibraryMissing", "lisa_shape", "make_shape", "library",
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
     "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_attention_mass",
-    "lisa_status_string", "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
+    "lisa_indexer_kl", "lisa_status_string", "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
     "workspace", "LISA_F32", "LISA_BF16", "LISA_LINEAR_UNNORMALIZED", "LISA_SLIDING_WINDOW",
     "LISA_OP_DECODE", "LISA_OP_PREFILL", "LISA_OP_TOPK_DECODE", "LISA_OP_TOPK_PREFILL",
     "LISA_OP_LINEAR_UPDATE", "LISA_OP_DENSE_DECODE", "LISA_OP_MASS", "LISA_ROWS_DECODE", "LISA_ROWS_PREFILL",
@@ -41,7 +41,7 @@ LISA_ROWS_DECODE, LISA_ROWS_PREFILL = 0, 1
 EXPORTED_SYMBOLS = (
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
     "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_attention_mass",
-    "lisa_status_string", "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
+    "lisa_indexer_kl", "lisa_status_string", "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
 )
 
 
@@ -105,6 +105,8 @@ def library() -> ctypes.CDLL:
     lib.lisa_dense_decode.restype = ctypes.c_int
     lib.lisa_attention_mass.argtypes = [sp, _I32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.lisa_attention_mass.restype = ctypes.c_int
+    lib.lisa_indexer_kl.argtypes = [sp, _I32, _P, _P, _P, _P, _P, _P, _P]
+    lib.lisa_indexer_kl.restype = ctypes.c_int
     lib.lisa_status_string.argtypes = [ctypes.c_int]
     lib.lisa_status_string.restype = ctypes.c_char_p
     lib.lisa_last_error.argtypes = []
@@ -251,6 +253,16 @@ def lisa_attention_mass(shape, n_rows, row_seq, row_len, q, k_cache, idx, mass, 
         _ptr(idx, "idx", torch.int32), _ptr(mass, "mass", torch.float32), _ptr(bound, "bound", torch.float32),
         _ptr(ws, "ws"), 0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "lisa_attention_mass")
+
+
+def lisa_indexer_kl(shape, n, q, k_cache, q_idx, k_idx_cache, kl_out, loss_out=None, stream=None):
+    """Per-row, per-indexer-head KL of the indexer training objective (and its mean)."""
+    T = _act(shape)
+    rc = library().lisa_indexer_kl(
+        ctypes.byref(shape), int(n), _ptr(q, "q", T), _ptr(k_cache, "k_cache", T), _ptr(q_idx, "q_idx", T),
+        _ptr(k_idx_cache, "k_idx_cache", T), _ptr(kl_out, "kl_out", torch.float32),
+        _ptr(loss_out, "loss_out", torch.float32), _stream(stream))
+    _check(rc, "lisa_indexer_kl")
 
 
 def lisa_timing_enable(kernel_id: int, starts=None, stops=None) -> None:

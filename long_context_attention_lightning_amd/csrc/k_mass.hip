@@ -29,21 +29,6 @@ namespace lisa {
 
 constexpr int MS_KEYS = 256;  // keys per logits block (4 waves x 4 passes x 16 keys)
 
-// (m, s) := the pair for the union of two key sets, where each pair is the
-// max logit of its set and the sum of exp(logit - max) over the set
-// (m = -inf, s = 0 for an empty set).
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-  const float mn = fmaxf(m, m2);
-  if (mn == -INFINITY) return;
-  s = s * expf(m - mn) + s2 * expf(m2 - mn);
-  m = mn;
-}
-
-__device__ __forceinline__ void lse_merge_xor(float& m, float& s, int mask) {
-  const float m2 = __shfl_xor(m, mask, WAVE), s2 = __shfl_xor(s, mask, WAVE);
-  lse_merge(m, s, m2, s2);
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_mass_logits(MassArgs a) {
   __shared__ float qs[8][D];
@@ -211,26 +196,6 @@ __global__ __launch_bounds__(256) void k_mass_logits_mfma(MassArgs a) {
     for (int w = 1; w < 4; ++w) lse_merge(m, s2, wm[w][tid], wsum[w][tid]);
     a.part[((size_t)r * sh.H_q + (size_t)kvh * G + tid) * a.part_ld + blockIdx.y] = make_float2(m, s2);
   }
-}
-
-// Block-wide sum / max of one value per thread (256 threads); every thread
-// receives the result.  `red` holds four floats and is free again on return.
-__device__ __forceinline__ float block_sum256(float v, float* red) {
-  v = group_sum(v, WAVE);
-  if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
-  __syncthreads();
-  const float s = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
-  return s;
-}
-
-__device__ __forceinline__ float block_max256(float v, float* red) {
-  v = group_max(v, WAVE);
-  if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
-  __syncthreads();
-  const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return s;
 }
 
 __global__ __launch_bounds__(256) void k_mass_reduce(MassArgs a) {

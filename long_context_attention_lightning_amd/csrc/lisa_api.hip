@@ -226,7 +226,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
     "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine",
     "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose", "select_attention",
-    "segment_correct", "mass_logits", "mass_select", "mass_reduce"};
+    "segment_correct", "mass_logits", "mass_select", "mass_reduce", "indexer_kl"};
 
 thread_local LaunchEvents g_next_launch;
 
@@ -561,6 +561,32 @@ int lisa_attention_mass(const lisa_shape* shape, int32_t n_rows, const int32_t* 
     LAUNCH(KID_MASS_SELECT, st, launch_select(sa, st));
   }
   LAUNCH(KID_MASS_REDUCE, st, launch_mass_reduce(a, st));
+  return LISA_OK;
+}
+
+int lisa_indexer_kl(const lisa_shape* shape, int32_t n, const void* q, const void* k_cache, const void* q_idx,
+                    const void* k_idx_cache, float* kl_out, float* loss_out, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if ((rc = check_prefill_len(sh, n))) return rc;
+  if (sh.flags & LISA_SLIDING_WINDOW) return fail(LISA_ERR_INVALID_ARG, "a sliding-window shape has no indexer");
+  if (sh.H_q % sh.H_I)
+    return fail(LISA_ERR_UNSUPPORTED, "H_q (%d) is not a multiple of H_I (%d): teacher heads cannot be grouped",
+                sh.H_q, sh.H_I);
+  REQUIRE_PTR(q); REQUIRE_PTR(k_cache); REQUIRE_PTR(q_idx); REQUIRE_PTR(k_idx_cache); REQUIRE_PTR(kl_out);
+  OPTIONAL_PTR(loss_out);
+  if ((size_t)sh.B * n * sh.H_I > 0x7fffffffu) return fail(LISA_ERR_UNSUPPORTED, "B * n * H_I too large");
+  if (sh.B > 65535) return fail(LISA_ERR_UNSUPPORTED, "B %d > 65535", sh.B);
+  hipStream_t st = (hipStream_t)stream;
+  KlArgs a{};
+  a.sh = sh; a.n = n; a.q = q; a.k_cache = k_cache; a.q_idx = q_idx; a.k_idx = k_idx_cache;
+  a.scale = 1.f / sqrtf((float)sh.d); a.kl = kl_out; a.loss = loss_out;
+  LAUNCH(KID_INDEXER_KL, st, launch_indexer_kl(a, st));
+  if (loss_out) {
+    const hipError_t e = launch_indexer_kl_loss(a, st);
+    if (e != hipSuccess) return fail_hip(e, "indexer_kl_loss");
+  }
   return LISA_OK;
 }
 

@@ -178,4 +178,39 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Log-sum-exp pairs: (m, s) stands for a set of logits with max m and
+// sum of exp(logit - m) s (m = -inf, s = 0 for the empty set).  Merging two
+// pairs gives the pair of the union.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * expf(m - mn) + s2 * expf(m2 - mn);
+  m = mn;
+}
+
+__device__ __forceinline__ void lse_merge_xor(float& m, float& s, int mask) {
+  const float m2 = __shfl_xor(m, mask, WAVE), s2 = __shfl_xor(s, mask, WAVE);
+  lse_merge(m, s, m2, s2);
+}
+
+// Block-wide sum / max of one value per thread (256 threads); every thread
+// receives the result.  `red` holds four floats and is free again on return.
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = group_sum(v, WAVE);
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
+  __syncthreads();
+  const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return s;
+}
+
+__device__ __forceinline__ float block_max256(float v, float* red) {
+  v = group_max(v, WAVE);
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = v;
+  __syncthreads();
+  const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return s;
+}
+
 }  // namespace lisa

@@ -48,7 +48,8 @@ enum KernelId {
   KID_MASS_LOGITS = 14,
   KID_MASS_SELECT = 15,
   KID_MASS_REDUCE = 16,
-  KID_COUNT = 17
+  KID_INDEXER_KL = 17,
+  KID_COUNT = 18
 };
 
 // ---------------------------------------------------------------------------
@@ -154,6 +155,24 @@ struct MassArgs {
   float* mass;              // [n_rows, H_q]
   float* bound;             // nullable [n_rows, H_q]
 };
+// ---------------------------------------------------------------------------
+// indexer training objective (per-row, per-head KL against the teacher)
+// ---------------------------------------------------------------------------
+struct KlArgs {
+  Shape sh;
+  int n;                    // prefill rows per sequence
+  const void* q;            // [B, n, H_q, d] teacher queries
+  const void* k_cache;      // [B, cap, H_kv, d] teacher keys (rows 0..n-1)
+  const void* q_idx;        // [B, n, H_I, d_I]
+  const void* k_idx;        // [B, cap, H_Ik, d_I]
+  float scale;              // 1/sqrt(d)
+  float* kl;                // [B, n, H_I]
+  float* loss;              // nullable [1]: mean of kl
+};
+bool kl_mfma_supported(const Shape& sh);
+hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t st);
+hipError_t launch_indexer_kl_loss(const KlArgs& a, hipStream_t st);
+
 int mass_key_blocks(int max_len);
 hipError_t launch_mass_logits(const MassArgs& a, int max_len, hipStream_t st);
 hipError_t launch_mass_reduce(const MassArgs& a, hipStream_t st);

@@ -158,3 +158,19 @@ def test_attention_mass_workspace_and_rejections(lib):
     bad = _c1(max_len=0)
     rc = lib.lisa_attention_mass(ctypes.byref(bad), 3, None, p, p, p, p, p, None, p, 1 << 40, None)
     assert rc == -1 and "max_len" in L.lisa_last_error()
+
+
+def test_indexer_kl_rejections(lib):
+    buf = (ctypes.c_float * 64)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    sh = _c1(H_I=8, H_Ik=8)  # 28 teacher heads do not split over 8 indexer heads
+    rc = lib.lisa_indexer_kl(ctypes.byref(sh), 64, p, p, p, p, p, None, None)
+    assert rc == -2 and "H_I" in L.lisa_last_error()
+    sh = _c1()
+    rc = lib.lisa_indexer_kl(ctypes.byref(sh), 64, p, p, p, p, None, None, None)
+    assert rc == -1 and "kl_out" in L.lisa_last_error()
+    rc = lib.lisa_indexer_kl(ctypes.byref(sh), 0, p, p, p, p, p, None, None)
+    assert rc == -1
+    win = _c1(flags=L.LISA_SLIDING_WINDOW)
+    rc = lib.lisa_indexer_kl(ctypes.byref(win), 64, p, p, p, p, p, None, None)
+    assert rc == -1 and "sliding-window" in L.lisa_last_error()
