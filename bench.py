@@ -562,15 +562,60 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     t1.record()
     torch.cuda.synchronize()
     ms_w = t0.elapsed_time(t1) / args.prefill_iters
+    indexer_kl = bench_indexer_kl(args, torch, Lb, cfg, sh, t, n)
     res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
            "dense_causal_prefill_attention_ms": dense,
            "window_prefill": {"ms": round(ms_w, 3), "tok_s": round(n / (ms_w * 1e-3), 1), "attention_us": attn_w,
                               "what": "sliding-window mode, window M, no indexer or select"},
            "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
-           "prefill_kernel_roofline": proofs}
+           "prefill_kernel_roofline": proofs, "indexer_kl": indexer_kl}
     del ws, t, out
     torch.cuda.empty_cache()
     return res
+
+
+def bench_indexer_kl(args, torch, Lb, cfg, sh, t, n):
+    """The indexer training objective over the same prefill: per-row,
+    per-head KL against the grouped teacher attention and the loss."""
+    kl = torch.empty((1, n, cfg.H_I), dtype=torch.float32, device="cuda")
+    loss = torch.empty((1,), dtype=torch.float32, device="cuda")
+
+    def call():
+        Lb.lisa_indexer_kl(sh, n, t["q"], t["k"], t["q_idx"], t["k_idx"], kl, loss)
+
+    call()
+    torch.cuda.synchronize()
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    sp = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in st + sp:
+        e.record()
+    torch.cuda.synchronize()
+    Lb.lisa_timing_enable(17, st, sp)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    cnt = Lb.lisa_timing_count()
+    Lb.lisa_timing_enable(0)
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])]))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    iters = max(1, args.prefill_iters // 2)
+    t0.record()
+    for _ in range(iters):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / iters
+    pairs = n * (n + 1) // 2
+    # logits of every causal pair: the teacher heads over d and the index heads over d_I
+    flops = 2 * pairs * (cfg.H_q * cfg.d + cfg.H_I * cfg.d_I)
+    roof = kernel_roofline("indexer_kl", k_ms, flops, "mfma", traffic_key="prefill:indexer_kl")
+    return {"what": "indexer training objective forward (LISA Eq. 2): KL of each row's indexer softmax from the "
+                    "mean of its 7 teacher heads' causal attention, all 16384 rows x 4 heads, and the loss",
+            "ms_per_call": round(ms, 3), "kernel_us": round(k_ms * 1e3, 1),
+            "note": "two passes over every causal pair (the row's teacher log-sum-exps first); the roofline counts "
+                    "one pass of logits, so executed MFMA work is twice the algorithmic",
+            "kernel_roofline": roof, "loss": round(float(loss.item()), 6)}
 
 
 def dense_prefill_baseline(torch, q, k, v, cfg, n, iters):

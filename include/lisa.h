@@ -86,6 +86,8 @@ extern "C" {
 #define LISA_OP_LINEAR_UPDATE    4
 #define LISA_OP_DENSE_DECODE     5
 #define LISA_OP_MASS             6
+#define LISA_OP_DROPOUT_DECODE   7
+#define LISA_OP_DROPOUT_PREFILL  8
 
 /* rows_mode of lisa_indexer_topk() */
 #define LISA_ROWS_DECODE   0
@@ -112,8 +114,9 @@ typedef struct lisa_shape {
 /*
  * Bytes of workspace an operation needs.  `n` is the prefill length (tokens
  * per sequence) for LISA_OP_PREFILL / LISA_OP_TOPK_PREFILL, the token count
- * for LISA_OP_LINEAR_UPDATE and the number of query rows for LISA_OP_MASS;
- * it is ignored otherwise.  Returns 0 for an
+ * for LISA_OP_LINEAR_UPDATE and the number of query rows for LISA_OP_MASS,
+ * and the prefill length for LISA_OP_DROPOUT_PREFILL; it is ignored
+ * otherwise.  Returns 0 for an
  * invalid shape or op (lisa_last_error() says why).
  */
 size_t lisa_workspace_bytes(const lisa_shape* shape, int op, int32_t n);
@@ -290,6 +293,32 @@ int lisa_attention_mass(const lisa_shape* shape, int32_t n_rows, const int32_t* 
 int lisa_indexer_kl(const lisa_shape* shape, int32_t n, const void* q, const void* k_cache,
                     const void* q_idx, const void* k_idx_cache, float* kl_out, float* loss_out,
                     void* stream);
+
+/*
+ * Indexer candidate dropout ([LISA] Section 3.2 Stage 2: early in training
+ * the top 1.2 M candidates are taken and a random 20% of them masked out
+ * before the sparse attention is filled; the ratio is lowered over
+ * training).  Per score row of length len:
+ *   1. candidates: the top min(len, n_cand) positions (order as for top-M:
+ *      score descending, ties to the later position, -0.0 == +0.0);
+ *   2. candidate j survives iff u[j] >= p (u: the caller's uniform draws in
+ *      [0, 1), one per position, same layout as the scores);
+ *   3. idx_out: the min(M, #survivors) best survivors in that order,
+ *      ascending, -1 padded.
+ * rows_mode, n, seq_lens and the score layout as for lisa_indexer_topk
+ * (prefill rows: row t of each sequence has length t+1, scores
+ * [B, n, scores_ld]; decode: [B, scores_ld]); scores_ld a multiple of 4 and
+ * at least the longest row.  Scores must be finite and above -FLT_MAX.
+ * n_cand >= 1 (the paper's 1.2 M is ceil(1.2 M)); p is the dropout ratio
+ * (p <= 0 keeps every candidate, p > 1 none).  idx_out [rows, M] int32.
+ * ws: lisa_workspace_bytes(shape, LISA_OP_DROPOUT_DECODE, 0) or
+ * lisa_workspace_bytes(shape, LISA_OP_DROPOUT_PREFILL, n) bytes (the top
+ * n_cand bitmask, the survivor scores and their top-M).  Asynchronous on
+ * `stream`.
+ */
+int lisa_candidate_dropout(const lisa_shape* shape, int rows_mode, int32_t n, const int32_t* seq_lens,
+                           const float* scores, const float* u, int64_t scores_ld, int32_t n_cand,
+                           float p, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Text of a status code. */
 const char* lisa_status_string(int status);

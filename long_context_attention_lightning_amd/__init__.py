@@ -21,10 +21,12 @@ __all__ = [
     "LisaError", "LisaLibraryMissing", "lisa_shape", "make_shape", "library",
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
     "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_attention_mass",
-    "lisa_indexer_kl", "lisa_status_string", "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
+    "lisa_indexer_kl", "lisa_candidate_dropout", "lisa_status_string", "lisa_last_error", "lisa_timing_enable",
+    "lisa_timing_count", "lisa_kernel_name",
     "workspace", "LISA_F32", "LISA_BF16", "LISA_LINEAR_UNNORMALIZED", "LISA_SLIDING_WINDOW",
     "LISA_OP_DECODE", "LISA_OP_PREFILL", "LISA_OP_TOPK_DECODE", "LISA_OP_TOPK_PREFILL",
-    "LISA_OP_LINEAR_UPDATE", "LISA_OP_DENSE_DECODE", "LISA_OP_MASS", "LISA_ROWS_DECODE", "LISA_ROWS_PREFILL",
+    "LISA_OP_LINEAR_UPDATE", "LISA_OP_DENSE_DECODE", "LISA_OP_MASS",
+    "LISA_OP_DROPOUT_DECODE", "LISA_OP_DROPOUT_PREFILL", "LISA_ROWS_DECODE", "LISA_ROWS_PREFILL",
     "EXPORTED_SYMBOLS", "LIB_PATH",
 ]
 
@@ -35,13 +37,15 @@ LISA_F32, LISA_BF16 = 0, 1
 LISA_LINEAR_UNNORMALIZED = 1
 LISA_SLIDING_WINDOW = 2
 (LISA_OP_DECODE, LISA_OP_PREFILL, LISA_OP_TOPK_DECODE, LISA_OP_TOPK_PREFILL,
- LISA_OP_LINEAR_UPDATE, LISA_OP_DENSE_DECODE, LISA_OP_MASS) = range(7)
+ LISA_OP_LINEAR_UPDATE, LISA_OP_DENSE_DECODE, LISA_OP_MASS, LISA_OP_DROPOUT_DECODE,
+ LISA_OP_DROPOUT_PREFILL) = range(9)
 LISA_ROWS_DECODE, LISA_ROWS_PREFILL = 0, 1
 
 EXPORTED_SYMBOLS = (
     "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
     "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_attention_mass",
-    "lisa_indexer_kl", "lisa_status_string", "lisa_last_error", "lisa_timing_enable", "lisa_timing_count", "lisa_kernel_name",
+    "lisa_indexer_kl", "lisa_candidate_dropout", "lisa_status_string", "lisa_last_error", "lisa_timing_enable",
+    "lisa_timing_count", "lisa_kernel_name",
 )
 
 
@@ -107,6 +111,9 @@ def library() -> ctypes.CDLL:
     lib.lisa_attention_mass.restype = ctypes.c_int
     lib.lisa_indexer_kl.argtypes = [sp, _I32, _P, _P, _P, _P, _P, _P, _P]
     lib.lisa_indexer_kl.restype = ctypes.c_int
+    lib.lisa_candidate_dropout.argtypes = [sp, ctypes.c_int, _I32, _P, _P, _P, ctypes.c_int64, _I32, ctypes.c_float,
+                                           _P, _P, ctypes.c_size_t, _P]
+    lib.lisa_candidate_dropout.restype = ctypes.c_int
     lib.lisa_status_string.argtypes = [ctypes.c_int]
     lib.lisa_status_string.restype = ctypes.c_char_p
     lib.lisa_last_error.argtypes = []
@@ -263,6 +270,17 @@ def lisa_indexer_kl(shape, n, q, k_cache, q_idx, k_idx_cache, kl_out, loss_out=N
         _ptr(k_idx_cache, "k_idx_cache", T), _ptr(kl_out, "kl_out", torch.float32),
         _ptr(loss_out, "loss_out", torch.float32), _stream(stream))
     _check(rc, "lisa_indexer_kl")
+
+
+def lisa_candidate_dropout(shape, rows_mode, n, seq_lens, scores, u, scores_ld, n_cand, p, idx_out, ws,
+                           stream=None):
+    """Top n_cand candidates per score row, dropped where u < p, the M best survivors kept."""
+    f = torch.float32
+    rc = library().lisa_candidate_dropout(
+        ctypes.byref(shape), int(rows_mode), int(n), _ptr(seq_lens, "seq_lens", torch.int32),
+        _ptr(scores, "scores", f), _ptr(u, "u", f), int(scores_ld), int(n_cand), float(p),
+        _ptr(idx_out, "idx_out", torch.int32), _ptr(ws, "ws"), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "lisa_candidate_dropout")
 
 
 def lisa_timing_enable(kernel_id: int, starts=None, stops=None) -> None:

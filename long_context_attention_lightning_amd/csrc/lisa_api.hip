@@ -192,6 +192,24 @@ MassWs mass_ws(const Shape& sh, int n_rows) {
   return w;
 }
 
+struct DropoutWs {
+  size_t mask, s2, idx2, total;
+};
+
+// own strides of the workspace rows, from the longest row
+int64_t dropout_ld2(int longest) { return (int64_t)align_up((size_t)longest, 64); }
+int64_t dropout_mask_ld(int longest) { return (longest + 31) / 32; }
+
+DropoutWs dropout_ws(const Shape& sh, int64_t rows, int longest) {
+  DropoutWs w;
+  Layout L;
+  w.mask = L.take((size_t)rows * dropout_mask_ld(longest) * 4);
+  w.s2 = L.take((size_t)rows * dropout_ld2(longest) * 4);
+  w.idx2 = L.take((size_t)rows * sh.M * 4);
+  w.total = L.off;
+  return w;
+}
+
 struct TopkWs {
   size_t scores, total;
 };
@@ -226,7 +244,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
     "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine",
     "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose", "select_attention",
-    "segment_correct", "mass_logits", "mass_select", "mass_reduce", "indexer_kl"};
+    "segment_correct", "mass_logits", "mass_select", "mass_reduce", "indexer_kl", "candidate_dropout_scores"};
 
 thread_local LaunchEvents g_next_launch;
 
@@ -316,6 +334,12 @@ size_t lisa_workspace_bytes(const lisa_shape* shape, int op, int32_t n) {
     case LISA_OP_MASS:
       if (check_decode_len(sh) != LISA_OK || n < 1) return 0;
       return mass_ws(sh, n).total;
+    case LISA_OP_DROPOUT_DECODE:
+      if (check_decode_len(sh) != LISA_OK) return 0;
+      return dropout_ws(sh, sh.B, sh.max_len).total;
+    case LISA_OP_DROPOUT_PREFILL:
+      if (check_prefill_len(sh, n) != LISA_OK) return 0;
+      return dropout_ws(sh, (int64_t)sh.B * n, n).total;
     case LISA_OP_LINEAR_UPDATE:
       return 256;  // no workspace is used; a nonzero size marks a valid shape
     default:
@@ -561,6 +585,53 @@ int lisa_attention_mass(const lisa_shape* shape, int32_t n_rows, const int32_t* 
     LAUNCH(KID_MASS_SELECT, st, launch_select(sa, st));
   }
   LAUNCH(KID_MASS_REDUCE, st, launch_mass_reduce(a, st));
+  return LISA_OK;
+}
+
+int lisa_candidate_dropout(const lisa_shape* shape, int rows_mode, int32_t n, const int32_t* seq_lens,
+                           const float* scores, const float* u, int64_t scores_ld, int32_t n_cand, float p,
+                           int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if (rows_mode != LISA_ROWS_DECODE && rows_mode != LISA_ROWS_PREFILL)
+    return fail(LISA_ERR_INVALID_ARG, "rows_mode %d", rows_mode);
+  const bool dec = rows_mode == LISA_ROWS_DECODE;
+  if (dec) {
+    if ((rc = check_decode_len(sh))) return rc;
+    REQUIRE_PTR(seq_lens);
+  } else if ((rc = check_prefill_len(sh, n))) {
+    return rc;
+  }
+  const int longest = dec ? sh.max_len : n;
+  if (n_cand < 1) return fail(LISA_ERR_INVALID_ARG, "n_cand %d (must be >= 1)", n_cand);
+  if (!(p == p)) return fail(LISA_ERR_INVALID_ARG, "p is NaN");
+  REQUIRE_PTR(scores); REQUIRE_PTR(u); REQUIRE_PTR(idx_out); REQUIRE_PTR(ws);
+  if (scores_ld < longest || scores_ld % 4)
+    return fail(LISA_ERR_INVALID_ARG, "scores_ld %lld must be a multiple of 4 and >= the longest row %d",
+                (long long)scores_ld, longest);
+  const int64_t rows = dec ? sh.B : (int64_t)sh.B * n;
+  if (rows > 0x7fffffff) return fail(LISA_ERR_UNSUPPORTED, "too many rows");
+  const DropoutWs w = dropout_ws(sh, rows, longest);
+  if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  hipStream_t st = (hipStream_t)stream;
+  SelectArgs sa{};
+  sa.n_rows = (int)rows; sa.rows_per_seq = dec ? 1 : n; sa.prefill = dec ? 0 : 1; sa.seq_lens = dec ? seq_lens : nullptr;
+  sa.scores = scores; sa.ld = scores_ld; sa.first_row = 0; sa.stored_rows = dec ? 1 : n; sa.max_len = longest;
+  sa.M = n_cand; sa.idx = nullptr; sa.idx_ld = 0;
+  sa.mask = at<uint32_t>(ws, w.mask); sa.mask_ld = dropout_mask_ld(longest);
+  LAUNCH(KID_SELECT, st, launch_select(sa, st));  // 1. candidates
+  DropoutArgs da{};
+  da.n_rows = (int)rows; da.rows_per_seq = sa.rows_per_seq; da.prefill = sa.prefill; da.seq_lens = sa.seq_lens;
+  da.scores = scores; da.u = u; da.ld = scores_ld; da.p = p; da.mask = sa.mask; da.mask_ld = sa.mask_ld;
+  da.s2 = at<float>(ws, w.s2); da.ld2 = dropout_ld2(longest); da.idx2 = at<int32_t>(ws, w.idx2); da.M = sh.M;
+  da.idx_out = idx_out;
+  LAUNCH(KID_DROPOUT, st, launch_dropout_scores(da, longest, st));  // 2. survivor scores
+  SelectArgs sb = sa;
+  sb.scores = da.s2; sb.ld = da.ld2; sb.M = sh.M; sb.idx = at<int32_t>(ws, w.idx2); sb.idx_ld = sh.M; sb.mask = nullptr;
+  LAUNCH(KID_SELECT, st, launch_select(sb, st));  // 3. the M best of them
+  const hipError_t e = launch_dropout_filter(da, st);  // 4. drop non-survivors, pad
+  if (e != hipSuccess) return fail_hip(e, "dropout_filter");
   return LISA_OK;
 }
 

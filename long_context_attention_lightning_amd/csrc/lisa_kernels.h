@@ -49,7 +49,8 @@ enum KernelId {
   KID_MASS_SELECT = 15,
   KID_MASS_REDUCE = 16,
   KID_INDEXER_KL = 17,
-  KID_COUNT = 18
+  KID_DROPOUT = 18,
+  KID_COUNT = 19
 };
 
 // ---------------------------------------------------------------------------
@@ -172,6 +173,29 @@ struct KlArgs {
 bool kl_mfma_supported(const Shape& sh);
 hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t st);
 hipError_t launch_indexer_kl_loss(const KlArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// indexer candidate dropout (top n_cand, random mask, the M best survivors)
+// ---------------------------------------------------------------------------
+struct DropoutArgs {
+  int n_rows;
+  int rows_per_seq;         // prefill: n (row r has length r % n + 1)
+  int prefill;
+  const int32_t* seq_lens;  // decode lengths
+  const float* scores;      // [n_rows, ld]
+  const float* u;           // [n_rows, ld] uniforms in [0, 1)
+  int64_t ld;
+  float p;                  // dropout ratio: candidate j survives iff u[j] >= p
+  const uint32_t* mask;     // workspace [n_rows, mask_ld]: the top-n_cand bitmask
+  int64_t mask_ld;
+  float* s2;                // workspace [n_rows, ld2]: survivor scores, others the lowest float
+  int64_t ld2;
+  const int32_t* idx2;      // workspace [n_rows, M]: top-M of s2
+  int M;
+  int32_t* idx_out;         // [n_rows, M]
+};
+hipError_t launch_dropout_scores(const DropoutArgs& a, int max_len, hipStream_t st);
+hipError_t launch_dropout_filter(const DropoutArgs& a, hipStream_t st);
 
 int mass_key_blocks(int max_len);
 hipError_t launch_mass_logits(const MassArgs& a, int max_len, hipStream_t st);

@@ -174,3 +174,21 @@ def test_indexer_kl_rejections(lib):
     win = _c1(flags=L.LISA_SLIDING_WINDOW)
     rc = lib.lisa_indexer_kl(ctypes.byref(win), 64, p, p, p, p, p, None, None)
     assert rc == -1 and "sliding-window" in L.lisa_last_error()
+
+
+def test_candidate_dropout_rejections(lib):
+    buf = (ctypes.c_float * 64)()
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    sh = _c1()
+    ws = L.lisa_workspace_bytes(sh, L.LISA_OP_DROPOUT_DECODE)
+    assert ws >= 16384 * 4 + 2048 * 4
+    assert L.lisa_workspace_bytes(sh, L.LISA_OP_DROPOUT_PREFILL, 4096) > 4096 * 4096 * 4
+    f = lib.lisa_candidate_dropout
+    assert f(ctypes.byref(sh), 0, 0, p, p, p, 16384, 0, ctypes.c_float(0.2), p, p, ws, None) == -1
+    assert "n_cand" in L.lisa_last_error()
+    assert f(ctypes.byref(sh), 0, 0, p, p, p, 16384, 2458, ctypes.c_float(float("nan")), p, p, ws, None) == -1
+    assert f(ctypes.byref(sh), 0, 0, p, p, p, 16382, 2458, ctypes.c_float(0.2), p, p, ws, None) == -1
+    assert "scores_ld" in L.lisa_last_error()
+    assert f(ctypes.byref(sh), 0, 0, p, p, None, 16384, 2458, ctypes.c_float(0.2), p, p, ws, None) == -1
+    assert f(ctypes.byref(sh), 0, 0, p, p, p, 16384, 2458, ctypes.c_float(0.2), p, p, ws - 1, None) == -3
+    assert f(ctypes.byref(sh), 7, 0, p, p, p, 16384, 2458, ctypes.c_float(0.2), p, p, ws, None) == -1
