@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--batched-only", action="store_true", help="only the batch-32 ragged decode leg (profiling)")
     p.add_argument("--batched-steps", type=int, default=64)
     p.add_argument("--no-sweep", action="store_true", help="skip the batch-8 32K M-sweep decode leg")
-    p.add_argument("--no-window", action="store_true", help="skip the sliding-window decode leg")
+    p.add_argument("--no-window", action="store_true", help="skip the sliding-window decode and prefill legs")
+    p.add_argument("--no-kl", action="store_true", help="skip the indexer training-objective leg")
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
     p.add_argument("--prefill-iters", type=int, default=5)
@@ -538,6 +539,20 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     proofs["prefill_linear_branch_mfma"] = kernel_roofline("prefill_linear_branch", lin_us * 1e-3, lin_flops, "mfma")
     dense = dense_prefill_baseline(torch, t["q"], t["k"], t["v"], cfg, n, args.prefill_iters)
     # the same prefill in sliding-window mode (no indexer; each row attends to its M most recent keys)
+    window = None if args.no_window else bench_window_prefill(args, torch, Lb, cfg, t, S, z, out, ws, n, M)
+    indexer_kl = None if args.no_kl else bench_indexer_kl(args, torch, Lb, cfg, sh, t, n)
+    res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
+           "dense_causal_prefill_attention_ms": dense, "window_prefill": window,
+           "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
+           "prefill_kernel_roofline": proofs, "indexer_kl": indexer_kl}
+    del ws, t, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_window_prefill(args, torch, Lb, cfg, t, S, z, out, ws, n, M):
+    """The prefill in sliding-window mode: no indexer or select, each row
+    attends to its M most recent keys."""
     shw = Lb.make_shape(B=1, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, H_I=cfg.H_I, H_Ik=cfg.H_Ik,
                         d_I=cfg.d_I, hidden=cfg.hidden, M=M, cap=n, flags=Lb.LISA_SLIDING_WINDOW)
 
@@ -556,22 +571,16 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     torch.cuda.synchronize()
     attn_w = round(st_w[0].elapsed_time(sp_w[0]) * 1e3, 1) if Lb.lisa_timing_count() else None
     Lb.lisa_timing_enable(0)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(args.prefill_iters):
         call_w()
     t1.record()
     torch.cuda.synchronize()
     ms_w = t0.elapsed_time(t1) / args.prefill_iters
-    indexer_kl = bench_indexer_kl(args, torch, Lb, cfg, sh, t, n)
-    res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
-           "dense_causal_prefill_attention_ms": dense,
-           "window_prefill": {"ms": round(ms_w, 3), "tok_s": round(n / (ms_w * 1e-3), 1), "attention_us": attn_w,
-                              "what": "sliding-window mode, window M, no indexer or select"},
-           "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
-           "prefill_kernel_roofline": proofs, "indexer_kl": indexer_kl}
-    del ws, t, out
-    torch.cuda.empty_cache()
-    return res
+    return {"ms": round(ms_w, 3), "tok_s": round(n / (ms_w * 1e-3), 1), "attention_us": attn_w,
+            "what": "sliding-window mode, window M, no indexer or select"}
 
 
 def bench_indexer_kl(args, torch, Lb, cfg, sh, t, n):
