@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--batched-steps", type=int, default=64)
     p.add_argument("--no-sweep", action="store_true", help="skip the batch-8 32K M-sweep decode leg")
     p.add_argument("--no-window", action="store_true", help="skip the sliding-window decode and prefill legs")
-    p.add_argument("--no-kl", action="store_true", help="skip the indexer training-objective leg")
+    p.add_argument("--no-kl", action="store_true",
+                   help="skip the legs of the adjacent operations (indexer KL, candidate dropout, segment correction)")
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
     p.add_argument("--prefill-iters", type=int, default=5)
@@ -426,6 +427,8 @@ def main():
         extra["m_sweep_decode"] = dict(workload=c4.name, batch=c4.B, context=c4.L, dense_decode_us_per_step=dense_us,
                                        **sweep)
 
+    if not args.no_kl:
+        extra["segment_correct"] = bench_segment(torch, Lb, CONFIGS[2])
     if not args.no_prefill:
         extra.update(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs))
 
@@ -541,11 +544,14 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     # the same prefill in sliding-window mode (no indexer; each row attends to its M most recent keys)
     window = None if args.no_window else bench_window_prefill(args, torch, Lb, cfg, t, S, z, out, ws, n, M)
     indexer_kl = None if args.no_kl else bench_indexer_kl(args, torch, Lb, cfg, sh, t, n)
+    del ws
+    torch.cuda.empty_cache()
+    dropout = None if args.no_kl else bench_dropout(torch, Lb, cfg, sh, t, w_idx, n, M)
     res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
            "dense_causal_prefill_attention_ms": dense, "window_prefill": window,
            "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
-           "prefill_kernel_roofline": proofs, "indexer_kl": indexer_kl}
-    del ws, t, out
+           "prefill_kernel_roofline": proofs, "indexer_kl": indexer_kl, "candidate_dropout": dropout}
+    del t, out
     torch.cuda.empty_cache()
     return res
 
@@ -625,6 +631,84 @@ def bench_indexer_kl(args, torch, Lb, cfg, sh, t, n):
             "note": "two passes over every causal pair (the row's teacher log-sum-exps first); the roofline counts "
                     "one pass of logits, so executed MFMA work is twice the algorithmic",
             "kernel_roofline": roof, "loss": round(float(loss.item()), 6)}
+
+
+def bench_dropout(torch, Lb, cfg, sh, t, w_idx, n, M):
+    """Candidate dropout over every row of the prefill: the indexer's own
+    scores of the 16K tokens, uniform draws from torch, ceil(1.2 M)
+    candidates and p = 0.2 (the paper's early-training setting)."""
+    ld = (n + 3) // 4 * 4
+    scores = torch.zeros((1, n, ld), dtype=torch.float32, device="cuda")
+    idx0 = torch.empty((1, n, M), dtype=torch.int32, device="cuda")
+    Lb.lisa_indexer_topk(sh, Lb.LISA_ROWS_PREFILL, n, None, t["q_idx"], t["k_idx"], w_idx, None, ld, scores, idx0,
+                         None)
+    del idx0
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    u = torch.rand((1, n, ld), dtype=torch.float32, device="cuda", generator=g)
+    idx = torch.empty((1, n, M), dtype=torch.int32, device="cuda")
+    ws = Lb.workspace(sh, Lb.LISA_OP_DROPOUT_PREFILL, n)
+    n_cand = -(-6 * M // 5)
+
+    def call():
+        Lb.lisa_candidate_dropout(sh, Lb.LISA_ROWS_PREFILL, n, None, scores, u, ld, n_cand, 0.2, idx, ws)
+
+    call()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    iters = 4
+    t0.record()
+    for _ in range(iters):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / iters
+    kept = float((idx >= 0).sum(dim=2).float().mean().item())
+    rows_len = n * (n + 1) // 2
+    # two selections over every row (candidates, then survivors) plus the survivor mask pass
+    work = 2 * SELECT_OPS_PER_KEY * rows_len
+    res = {"what": "indexer candidate dropout over all 16384 prefill rows: top ceil(1.2 M) = %d candidates, "
+                   "uniform draws, p = 0.2, the M best survivors" % n_cand,
+           "ms_per_call": round(ms, 3), "mean_kept_per_row": round(kept, 1),
+           "roofline": kernel_roofline("candidate_dropout", ms, work, "alu"),
+           "note": "call time (two select launches, the survivor-score pass and the compaction); integer work "
+                   "counted as for the top-M select"}
+    del scores, u, idx, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_segment(torch, Lb, cfg):
+    """Segment state correction of the linear state of a 32-sequence batch
+    (elementwise over S and z: 24 bytes per state element)."""
+    B = 32
+    sh = Lb.make_shape(B=B, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, H_I=cfg.H_I, H_Ik=cfg.H_Ik, d_I=cfg.d_I,
+                       hidden=cfg.hidden, M=cfg.M, cap=cfg.cap, max_len=cfg.cap)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    mk = lambda *shape: torch.randn(shape, dtype=torch.float32, device="cuda", generator=g)
+    S, S0, mS = (mk(B, cfg.H_L, cfg.d, cfg.d) for _ in range(3))
+    z, z0, mz = (mk(B, cfg.H_L, cfg.d) for _ in range(3))
+    st = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    sp = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for e in st + sp:
+        e.record()
+    torch.cuda.synchronize()
+    Lb.lisa_timing_enable(13, st, sp)
+    for i in range(8):
+        Lb.lisa_segment_correct(sh, S, z, S0, z0, mS, mz, i + 2, 0.3)
+    torch.cuda.synchronize()
+    cnt = Lb.lisa_timing_count()
+    Lb.lisa_timing_enable(0)
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(st[:cnt], sp[:cnt])]))
+    elems = B * cfg.H_L * cfg.d * (cfg.d + 1)
+    res = {"what": "segment state correction (LISA Eqs. 6-9) of 32 sequences' 28 x 128 x 128 states and "
+                   "normalisers", "kernel_us": round(k_ms * 1e3, 2),
+           "roofline": kernel_roofline("segment_correct", k_ms, 24 * elems, "hbm")}
+    del S, S0, mS, z, z0, mz
+    torch.cuda.empty_cache()
+    return res
 
 
 def dense_prefill_baseline(torch, q, k, v, cfg, n, iters):

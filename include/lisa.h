@@ -312,9 +312,11 @@ int lisa_indexer_kl(const lisa_shape* shape, int32_t n, const void* q, const voi
  * n_cand >= 1 (the paper's 1.2 M is ceil(1.2 M)); p is the dropout ratio
  * (p <= 0 keeps every candidate, p > 1 none).  idx_out [rows, M] int32.
  * ws: lisa_workspace_bytes(shape, LISA_OP_DROPOUT_DECODE, 0) or
- * lisa_workspace_bytes(shape, LISA_OP_DROPOUT_PREFILL, n) bytes (the top
- * n_cand bitmask, the survivor scores and their top-M).  Asynchronous on
- * `stream`.
+ * lisa_workspace_bytes(shape, LISA_OP_DROPOUT_PREFILL, n) bytes, which
+ * covers any n_cand (the top-n_cand bitmask, each row's survivors as a short
+ * row of scores and positions, and their top-M); a smaller n_cand needs
+ * less, and a workspace short of what the given n_cand needs is rejected.
+ * Asynchronous on `stream`.
  */
 int lisa_candidate_dropout(const lisa_shape* shape, int rows_mode, int32_t n, const int32_t* seq_lens,
                            const float* scores, const float* u, int64_t scores_ld, int32_t n_cand,

@@ -3,16 +3,12 @@
 // is masked out, and the sparse attention is filled from the rest, the ratio
 // being lowered as training goes on).  Per score row:
 //   1. the top n_cand positions (the library's select, as a bitmask);
-//   2. k_dropout_scores: survivors (candidates whose caller-drawn uniform u
-//      is at least p) keep their score, every other position gets the
-//      lowest float, so
-//   3. the top-M select of that row takes the M best survivors, or every
-//      survivor and then non-survivors when fewer than M survive;
-//   4. k_dropout_filter drops the non-survivors from each ascending list and
-//      pads with -1.
-// Steps 2 and 4 are elementwise / per-row passes.
-#include <float.h>
-
+//   2. k_dropout_compact: the survivors (candidates whose caller-drawn
+//      uniform u is at least p), in position order, as a short row of their
+//      scores and positions, with its length;
+//   3. the top-M select of each short row (ties go to the later entry, which
+//      is the later position);
+//   4. k_dropout_gather: the selected entries' positions, ascending, -1 padded.
 #include "lisa_common.h"
 #include "lisa_kernels.h"
 
@@ -22,31 +18,28 @@ __device__ __forceinline__ int dropout_row_len(const DropoutArgs& a, int r) {
   return a.prefill ? r % a.rows_per_seq + 1 : a.seq_lens[r];
 }
 
-__device__ __forceinline__ bool dropout_survives(const DropoutArgs& a, int r, int p) {
-  const uint32_t word = a.mask[(size_t)r * a.mask_ld + (p >> 5)];
-  return ((word >> (p & 31)) & 1u) && a.u[(size_t)r * a.ld + p] >= a.p;
-}
-
-__global__ __launch_bounds__(256) void k_dropout_scores(DropoutArgs a) {
-  const int r = blockIdx.x;
-  const int j = blockIdx.y * 256 + threadIdx.x;
-  if (j >= dropout_row_len(a, r)) return;
-  a.s2[(size_t)r * a.ld2 + j] = dropout_survives(a, r, j) ? a.scores[(size_t)r * a.ld + j] : -FLT_MAX;
-}
-
-__global__ __launch_bounds__(256) void k_dropout_filter(DropoutArgs a) {
+// One block per row; thread k takes a contiguous run of mask words, so the
+// survivors come out in position order after one block scan of the counts.
+__global__ __launch_bounds__(256) void k_dropout_compact(DropoutArgs a) {
   __shared__ uint32_t wsum[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
-  const int M = a.M;
-  const int32_t* in = a.idx2 + (size_t)r * M;
-  int32_t* out = a.idx_out + (size_t)r * M;
-  const int per = (M + 255) / 256, k0 = min(tid * per, M), k1 = min(k0 + per, M);
-  auto keep = [&](int k) {
-    const int p = in[k];
-    return p >= 0 && dropout_survives(a, r, p);
+  const int len = dropout_row_len(a, r);
+  const int words = (len + 31) / 32;
+  const int per = (words + 255) / 256, w0 = min(tid * per, words), w1 = min(w0 + per, words);
+  const uint32_t* mrow = a.mask + (size_t)r * a.mask_ld;
+  const float* urow = a.u + (size_t)r * a.ld;
+  auto survivors = [&](int w) {  // survivor bits of word w
+    uint32_t m = mrow[w];
+    if (32 * w + 32 > len) m &= (len - 32 * w >= 32) ? ~0u : ((1u << (len - 32 * w)) - 1u);
+    uint32_t keep = 0;
+    for (uint32_t x = m; x; x &= x - 1) {
+      const int bit = __builtin_ctz(x);
+      if (urow[32 * w + bit] >= a.p) keep |= 1u << bit;
+    }
+    return keep;
   };
   uint32_t cnt = 0;
-  for (int k = k0; k < k1; ++k) cnt += keep(k) ? 1u : 0u;
+  for (int w = w0; w < w1; ++w) cnt += (uint32_t)__builtin_popcount(survivors(w));
   const uint32_t incl = wave_incl_scan_u32(cnt);
   if (lane == WAVE - 1) wsum[wave] = incl;
   __syncthreads();
@@ -56,20 +49,38 @@ __global__ __launch_bounds__(256) void k_dropout_filter(DropoutArgs a) {
     if (w < wave) o += wsum[w];
     total += wsum[w];
   }
-  for (int k = k0; k < k1; ++k) {  // the chunks are contiguous and in thread order: ascending stays ascending
-    const int p = in[k];
-    if (p >= 0 && dropout_survives(a, r, p)) out[o++] = p;
+  const float* srow = a.scores + (size_t)r * a.ld;
+  float* cs = a.cscore + (size_t)r * a.cld;
+  int32_t* cp = a.cpos + (size_t)r * a.cld;
+  for (int w = w0; w < w1; ++w) {
+    for (uint32_t x = survivors(w); x; x &= x - 1) {
+      const int p = 32 * w + __builtin_ctz(x);
+      cs[o] = srow[p];
+      cp[o] = p;
+      ++o;
+    }
   }
-  for (int k = (int)total + tid; k < M; k += 256) out[k] = -1;
+  if (tid == 0) a.cnt[r] = (int32_t)total;
 }
 
-hipError_t launch_dropout_scores(const DropoutArgs& a, int max_len, hipStream_t st) {
-  klaunch(k_dropout_scores, dim3((unsigned)a.n_rows, (unsigned)((max_len + 255) / 256)), dim3(256), 0, st, a);
+__global__ __launch_bounds__(256) void k_dropout_gather(DropoutArgs a) {
+  const int r = blockIdx.x;
+  const int32_t* in = a.idx2 + (size_t)r * a.M;
+  const int32_t* cp = a.cpos + (size_t)r * a.cld;
+  int32_t* out = a.idx_out + (size_t)r * a.M;
+  for (int k = threadIdx.x; k < a.M; k += 256) {
+    const int e = in[k];
+    out[k] = e >= 0 ? cp[e] : -1;
+  }
+}
+
+hipError_t launch_dropout_compact(const DropoutArgs& a, hipStream_t st) {
+  klaunch(k_dropout_compact, dim3((unsigned)a.n_rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_dropout_filter(const DropoutArgs& a, hipStream_t st) {
-  klaunch(k_dropout_filter, dim3((unsigned)a.n_rows), dim3(256), 0, st, a);
+hipError_t launch_dropout_gather(const DropoutArgs& a, hipStream_t st) {
+  klaunch(k_dropout_gather, dim3((unsigned)a.n_rows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -193,18 +193,21 @@ MassWs mass_ws(const Shape& sh, int n_rows) {
 }
 
 struct DropoutWs {
-  size_t mask, s2, idx2, total;
+  size_t mask, cnt, cscore, cpos, idx2, total;
 };
 
-// own strides of the workspace rows, from the longest row
-int64_t dropout_ld2(int longest) { return (int64_t)align_up((size_t)longest, 64); }
+// Survivor rows hold at most min(n_cand, longest) entries; the workspace
+// query sizes them for the longest row (any n_cand).
+int64_t dropout_cld(int cmax) { return (int64_t)align_up((size_t)cmax, 64); }
 int64_t dropout_mask_ld(int longest) { return (longest + 31) / 32; }
 
-DropoutWs dropout_ws(const Shape& sh, int64_t rows, int longest) {
+DropoutWs dropout_ws(const Shape& sh, int64_t rows, int longest, int cmax) {
   DropoutWs w;
   Layout L;
   w.mask = L.take((size_t)rows * dropout_mask_ld(longest) * 4);
-  w.s2 = L.take((size_t)rows * dropout_ld2(longest) * 4);
+  w.cnt = L.take((size_t)rows * 4);
+  w.cscore = L.take((size_t)rows * dropout_cld(cmax) * 4);
+  w.cpos = L.take((size_t)rows * dropout_cld(cmax) * 4);
   w.idx2 = L.take((size_t)rows * sh.M * 4);
   w.total = L.off;
   return w;
@@ -244,7 +247,7 @@ const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
     "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine",
     "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose", "select_attention",
-    "segment_correct", "mass_logits", "mass_select", "mass_reduce", "indexer_kl", "candidate_dropout_scores"};
+    "segment_correct", "mass_logits", "mass_select", "mass_reduce", "indexer_kl", "candidate_dropout_compact"};
 
 thread_local LaunchEvents g_next_launch;
 
@@ -336,10 +339,10 @@ size_t lisa_workspace_bytes(const lisa_shape* shape, int op, int32_t n) {
       return mass_ws(sh, n).total;
     case LISA_OP_DROPOUT_DECODE:
       if (check_decode_len(sh) != LISA_OK) return 0;
-      return dropout_ws(sh, sh.B, sh.max_len).total;
+      return dropout_ws(sh, sh.B, sh.max_len, sh.max_len).total;
     case LISA_OP_DROPOUT_PREFILL:
       if (check_prefill_len(sh, n) != LISA_OK) return 0;
-      return dropout_ws(sh, (int64_t)sh.B * n, n).total;
+      return dropout_ws(sh, (int64_t)sh.B * n, n, n).total;
     case LISA_OP_LINEAR_UPDATE:
       return 256;  // no workspace is used; a nonzero size marks a valid shape
     default:
@@ -612,7 +615,8 @@ int lisa_candidate_dropout(const lisa_shape* shape, int rows_mode, int32_t n, co
                 (long long)scores_ld, longest);
   const int64_t rows = dec ? sh.B : (int64_t)sh.B * n;
   if (rows > 0x7fffffff) return fail(LISA_ERR_UNSUPPORTED, "too many rows");
-  const DropoutWs w = dropout_ws(sh, rows, longest);
+  const int cmax = min(n_cand, longest);
+  const DropoutWs w = dropout_ws(sh, rows, longest, cmax);
   if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
   hipStream_t st = (hipStream_t)stream;
   SelectArgs sa{};
@@ -624,14 +628,16 @@ int lisa_candidate_dropout(const lisa_shape* shape, int rows_mode, int32_t n, co
   DropoutArgs da{};
   da.n_rows = (int)rows; da.rows_per_seq = sa.rows_per_seq; da.prefill = sa.prefill; da.seq_lens = sa.seq_lens;
   da.scores = scores; da.u = u; da.ld = scores_ld; da.p = p; da.mask = sa.mask; da.mask_ld = sa.mask_ld;
-  da.s2 = at<float>(ws, w.s2); da.ld2 = dropout_ld2(longest); da.idx2 = at<int32_t>(ws, w.idx2); da.M = sh.M;
-  da.idx_out = idx_out;
-  LAUNCH(KID_DROPOUT, st, launch_dropout_scores(da, longest, st));  // 2. survivor scores
-  SelectArgs sb = sa;
-  sb.scores = da.s2; sb.ld = da.ld2; sb.M = sh.M; sb.idx = at<int32_t>(ws, w.idx2); sb.idx_ld = sh.M; sb.mask = nullptr;
-  LAUNCH(KID_SELECT, st, launch_select(sb, st));  // 3. the M best of them
-  const hipError_t e = launch_dropout_filter(da, st);  // 4. drop non-survivors, pad
-  if (e != hipSuccess) return fail_hip(e, "dropout_filter");
+  da.cnt = at<int32_t>(ws, w.cnt); da.cscore = at<float>(ws, w.cscore); da.cpos = at<int32_t>(ws, w.cpos);
+  da.cld = dropout_cld(cmax); da.idx2 = at<int32_t>(ws, w.idx2); da.M = sh.M; da.idx_out = idx_out;
+  LAUNCH(KID_DROPOUT, st, launch_dropout_compact(da, st));  // 2. survivor rows
+  SelectArgs sb{};  // 3. the M best of each survivor row (decode rows of length cnt)
+  sb.n_rows = (int)rows; sb.rows_per_seq = 1; sb.prefill = 0; sb.seq_lens = da.cnt;
+  sb.scores = da.cscore; sb.ld = da.cld; sb.first_row = 0; sb.stored_rows = 1; sb.max_len = cmax;
+  sb.M = sh.M; sb.idx = at<int32_t>(ws, w.idx2); sb.idx_ld = sh.M; sb.mask = nullptr;
+  LAUNCH(KID_SELECT, st, launch_select(sb, st));
+  const hipError_t e = launch_dropout_gather(da, st);  // 4. positions
+  if (e != hipSuccess) return fail_hip(e, "dropout_gather");
   return LISA_OK;
 }
 

@@ -188,14 +188,16 @@ struct DropoutArgs {
   float p;                  // dropout ratio: candidate j survives iff u[j] >= p
   const uint32_t* mask;     // workspace [n_rows, mask_ld]: the top-n_cand bitmask
   int64_t mask_ld;
-  float* s2;                // workspace [n_rows, ld2]: survivor scores, others the lowest float
-  int64_t ld2;
-  const int32_t* idx2;      // workspace [n_rows, M]: top-M of s2
+  int32_t* cnt;             // workspace [n_rows]: survivors per row
+  float* cscore;            // workspace [n_rows, cld]: survivor scores in position order
+  int32_t* cpos;            // workspace [n_rows, cld]: their positions
+  int64_t cld;
+  const int32_t* idx2;      // workspace [n_rows, M]: top-M entries of each survivor row
   int M;
   int32_t* idx_out;         // [n_rows, M]
 };
-hipError_t launch_dropout_scores(const DropoutArgs& a, int max_len, hipStream_t st);
-hipError_t launch_dropout_filter(const DropoutArgs& a, hipStream_t st);
+hipError_t launch_dropout_compact(const DropoutArgs& a, hipStream_t st);
+hipError_t launch_dropout_gather(const DropoutArgs& a, hipStream_t st);
 
 int mass_key_blocks(int max_len);
 hipError_t launch_mass_logits(const MassArgs& a, int max_len, hipStream_t st);

@@ -190,5 +190,5 @@ def test_candidate_dropout_rejections(lib):
     assert f(ctypes.byref(sh), 0, 0, p, p, p, 16382, 2458, ctypes.c_float(0.2), p, p, ws, None) == -1
     assert "scores_ld" in L.lisa_last_error()
     assert f(ctypes.byref(sh), 0, 0, p, p, None, 16384, 2458, ctypes.c_float(0.2), p, p, ws, None) == -1
-    assert f(ctypes.byref(sh), 0, 0, p, p, p, 16384, 2458, ctypes.c_float(0.2), p, p, ws - 1, None) == -3
+    assert f(ctypes.byref(sh), 0, 0, p, p, p, 16384, 2458, ctypes.c_float(0.2), p, p, 100, None) == -3
     assert f(ctypes.byref(sh), 7, 0, p, p, p, 16384, 2458, ctypes.c_float(0.2), p, p, ws, None) == -1
