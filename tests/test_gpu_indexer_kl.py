@@ -64,6 +64,15 @@ def test_kl_mfma_two_teacher_heads_batch2():
     _check(cfg, inp, n, list(range(n)), "mfma G_T=2 B=2")
 
 
+@pytest.mark.parametrize("gt,H_q,H_kv,n", [(1, 4, 2, 150), (4, 16, 4, 131), (8, 32, 4, 140)])
+def test_kl_mfma_teacher_group_sizes(gt, H_q, H_kv, n):
+    """Matrix-core path for other teacher-group sizes (4 indexer heads)."""
+    cfg = CONFIGS[3].replace(n=n, cap=n, H_q=H_q, H_kv=H_kv, H_L=H_q, H_I=4, H_Ik=4)
+    assert H_q // 4 == gt
+    inp = prefill_inputs(cfg, 3, n=n, salt=36 + gt)
+    _check(cfg, inp, n, list(range(n)), f"mfma G_T={gt}")
+
+
 @pytest.mark.parametrize("label,cid,over,n", [
     ("valu fp32 C0", 0, {}, 256),
     ("valu bf16 d64 shared key", 3, dict(H_q=6, H_kv=2, H_L=6, d=64, H_I=2, H_Ik=1, d_I=32, hidden=96), 150),
