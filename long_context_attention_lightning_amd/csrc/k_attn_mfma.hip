@@ -38,7 +38,7 @@ constexpr int AQ = 16 * AP;
 template <int D>
 struct AttnShared {
   bf16_t k[2][AK][D + 8];
-  bf16_t vt[2][D + 16][AK + 8];  // rows D .. D + 15 hold ones: P V also yields the row sums
+  bf16_t vt[2][D][AK + 8];
 };
 
 // Column of key j in the V tile: key 32 s + 16 h + 4 g + r sits at
@@ -208,9 +208,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   // all-ones where bit r of w is set, else zero
   auto bitmask = [](uint32_t w, int r) -> uint32_t { return (uint32_t)__builtin_amdgcn_sbfe((int)w, r, 1); };
 
-  // the ones rows of both V buffers (written once; staging never touches them)
-  for (int e = tid; e < 2 * 16 * (AK + 8); e += 256)
-    sm.vt[e / (16 * (AK + 8))][D + (e / (AK + 8)) % 16][e % (AK + 8)] = (bf16_t)0x3f80;
+  // the V operand of the row-sum block: every entry 1.0 (a constant, not an LDS read)
+  const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
   // Walks the key tiles: body(kt, buf, mw) computes tile kt from LDS buffer
   // buf with the mask words mw of the wave's rows, while tile kt + 1 (loaded
@@ -302,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 vf = as_bf16x8(lds_read16(&sm.vt[buf][16 * q + r16][32 * s + 8 * g]));
+          const bf16x8 vf = q < NQ - 1 ? as_bf16x8(lds_read16(&sm.vt[buf][16 * q + r16][32 * s + 8 * g])) : ones;
 #pragma unroll
           for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf, o[i][q]);
         }
