@@ -162,6 +162,13 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens,
  * out       [B, n, H_q, d] T
  * idx_out   nullable [B, n, M] int32: per row, ascending positions, -1 padded.
  * ws        workspace of lisa_workspace_bytes(shape, LISA_OP_PREFILL, n) bytes.
+ * The gate and the linear branch run on an internal side stream next to the
+ * indexer and the select, forked from and joined back into `stream` with
+ * events, so the call keeps the ordering of `stream` and can be captured in
+ * a graph.  The library creates one side stream and two events per device
+ * and caller stream on the first call outside a capture, and keeps them
+ * until the process ends.  Without one (the first call made inside a
+ * capture, sliding-window mode), everything runs on `stream`.
  */
 int lisa_prefill(const lisa_shape* shape, int32_t n,
                  const void* q, const void* k_cache, const void* v_cache,

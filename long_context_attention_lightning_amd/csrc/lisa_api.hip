@@ -6,7 +6,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "lisa.h"
 #include "lisa_kernels.h"
@@ -233,6 +236,40 @@ TopkWs topk_ws(const Shape& sh, int rows_mode, int n) {
 template <typename P> P* at(void* ws, size_t off) { return reinterpret_cast<P*>(static_cast<char*>(ws) + off); }
 
 // ---------------------------------------------------------------------------
+// side streams: a prefill forks its linear branch and gate onto a second
+// stream (default priority, non-blocking) that joins back before the
+// attention, so they overlap the indexer and the select.  One side stream
+// and event pair per (device, caller stream), created on first use outside
+// a graph capture; while none exists (or creation fails) the work stays on
+// the caller's stream.
+// ---------------------------------------------------------------------------
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+SideStream* side_stream(hipStream_t caller) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, SideStream> table;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = table.find({dev, caller});
+  if (it != table.end()) return &it->second;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+  SideStream ss;
+  if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+    if (ss.fork) (void)hipEventDestroy(ss.fork);
+    (void)hipStreamDestroy(ss.s);
+    return nullptr;
+  }
+  return &(table[{dev, caller}] = ss);
+}
+
+// ---------------------------------------------------------------------------
 // timing hook
 // ---------------------------------------------------------------------------
 struct Timing {
@@ -252,6 +289,7 @@ const char* const kKernelNames[KID_COUNT] = {
 thread_local LaunchEvents g_next_launch;
 
 bool timing_on(int kid) { return g_timing.kid == kid && g_timing.count < g_timing.n; }
+bool timing_armed() { return g_timing.kid >= 0 && g_timing.count < g_timing.n; }
 
 // A timed launch hands its event pair to the kernel's own dispatch
 // (hipExtLaunchKernel); the pair counts once the launcher has consumed it.
@@ -685,15 +723,26 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
   const PrefillWs w = prefill_ws(sh, n);
   if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
   hipStream_t st = (hipStream_t)stream;
+  // the gate and the linear branch depend on neither the indexer nor the
+  // select: with a side stream they run next to them (not while the timing
+  // hook is armed, so that a timed kernel runs alone)
+  SideStream* side = (window || timing_armed()) ? nullptr : side_stream(st);
+  hipStream_t sst = st;
+  if (side) {
+    hipError_t e = hipEventRecord(side->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return fail_hip(e, "prefill fork");
+    sst = side->s;
+  }
 
   GateArgs ga{};
   ga.sh = sh; ga.n_rows = sh.B * n; ga.x = x; ga.w_gate = w_gate; ga.gate_part = at<float>(ws, w.gate);
   if (gate_mfma_supported(sh)) {
     ga.w_t = at<bf16_t>(ws, w.w_t);
-    LAUNCH(KID_PREFILL_GATE_PREP, st, launch_gate_transpose(ga, st));
-    LAUNCH(KID_PREFILL_GATE, st, launch_gate_mfma(ga, st));
+    LAUNCH(KID_PREFILL_GATE_PREP, sst, launch_gate_transpose(ga, sst));
+    LAUNCH(KID_PREFILL_GATE, sst, launch_gate_mfma(ga, sst));
   } else {
-    LAUNCH(KID_PREFILL_GATE, st, launch_gate_logits(ga, st));
+    LAUNCH(KID_PREFILL_GATE, sst, launch_gate_logits(ga, sst));
   }
 
   float* o_lin = at<float>(ws, w.o_lin);
@@ -702,15 +751,15 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
     lc.sh = sh; lc.n = n; lc.q_lin = q_lin; lc.k_lin = k_lin; lc.v_lin = v_lin; lc.S = S; lc.z = z;
     lc.seg_state = at<float>(ws, w.seg); lc.in_place = 0; lc.o_lin = o_lin;
     linear_segments(sh, n, lc.nseg, lc.seg_len);
-    LAUNCH(KID_PREFILL_LIN_SUMS, st, launch_linear_seg_sums(lc, st));
-    LAUNCH(KID_PREFILL_LIN_PREFIX, st, launch_linear_seg_prefix(lc, st));
-    LAUNCH(KID_PREFILL_LINEAR, st, launch_linear_chunks(lc, st));
+    LAUNCH(KID_PREFILL_LIN_SUMS, sst, launch_linear_seg_sums(lc, sst));
+    LAUNCH(KID_PREFILL_LIN_PREFIX, sst, launch_linear_seg_prefix(lc, sst));
+    LAUNCH(KID_PREFILL_LINEAR, sst, launch_linear_chunks(lc, sst));
   } else {
     LinearArgs la{};
     la.sh = sh; la.n = n; la.q_lin = q_lin; la.k_lin = k_lin; la.v_lin = v_lin; la.S = S;
     la.z_in = z; la.z_out = at<float>(ws, w.z_tmp); la.o_lin = o_lin;
-    LAUNCH(KID_PREFILL_LINEAR, st, launch_linear_recurrent(la, st));
-    LAUNCH(KID_PREFILL_LINEAR, st, launch_copy_f32(z, la.z_out, (size_t)sh.B * sh.H_L * sh.d, st));
+    LAUNCH(KID_PREFILL_LINEAR, sst, launch_linear_recurrent(la, sst));
+    LAUNCH(KID_PREFILL_LINEAR, sst, launch_copy_f32(z, la.z_out, (size_t)sh.B * sh.H_L * sh.d, sst));
   }
 
   const bool mfma_attn = attn_mfma_supported(sh);
@@ -747,6 +796,11 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
   sa.M = sh.M; sa.max_len = n; sa.idx = idx; sa.idx_ld = sh.M;
   sa.mask = mfma_attn ? at<uint32_t>(ws, w.mask) : nullptr; sa.mask_ld = attn_mask_ld(n);
   LAUNCH(KID_SELECT, st, launch_select(sa, st));
+  if (side) {  // join: the attention reads the gate logits and the linear outputs
+    hipError_t e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
+    if (e != hipSuccess) return fail_hip(e, "prefill join");
+  }
 
   if (mfma_attn) {
     AttnMaskArgs am{};

@@ -195,3 +195,47 @@ def test_prefill_c3_qwen7b_16k_sampled_rows():
     print(f"[C3] recall={rc:.6f}")
     assert rc >= RECALL_MIN
     assert_state_close(g["S"][0], g["z"][0], ref["S"], ref["z"], "C3 state")
+
+
+def test_prefill_graph_replays_match_eager():
+    """The prefill runs its gate and linear branch on a side stream next to
+    the indexer and select.  Captured in a graph (the fork and the join become
+    graph edges), every replay must reproduce the eager result bit for bit,
+    with eager work (state resets) between the replays."""
+    n = 700
+    cfg = CONFIGS[3].replace(n=n, cap=n)
+    inp = prefill_inputs(cfg, 3, n=n, salt=77)
+    T = tdtype(cfg)
+    sh = shape_of(cfg, cap=n)
+    t = {k: dev(inp[k], T) for k in ("q", "k", "v", "k_idx", "q_idx", "q_lin", "k_lin", "v_lin", "x", "w_gate")}
+    w_idx = dev(inp["w_idx"], torch.float32)
+    S0, z0 = dev(inp["S0"], torch.float32), dev(inp["z0"], torch.float32)
+    ws = L.workspace(sh, L.LISA_OP_PREFILL, n)
+
+    def run(S, z, out):
+        L.lisa_prefill(sh, n, t["q"], t["k"], t["v"], t["k_idx"], t["q_idx"], t["q_lin"], t["k_lin"], t["v_lin"],
+                       t["x"], t["w_gate"], w_idx, S, z, out, None, ws)
+
+    s = torch.cuda.Stream()
+    S_e, z_e = S0.clone(), z0.clone()
+    out_e = torch.empty((1, n, cfg.H_q, cfg.d), dtype=T, device="cuda")
+    with torch.cuda.stream(s):  # eager, on the stream the graph is captured on
+        run(S_e, z_e, out_e)
+    torch.cuda.synchronize()
+    S_g, z_g = S0.clone(), z0.clone()
+    out_g = torch.empty_like(out_e)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run(S_g, z_g, out_g)
+    for rep in range(3):
+        S_g.copy_(S0)
+        z_g.copy_(z0)
+        out_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), rep
+        assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e), rep
+    ref = oracle.prefill_rows(inp, cfg.M, [0, 350, n - 1])
+    assert_out_close(cfg, host(out_e)[0, [0, 350, n - 1]], np.stack([ref["out"][t_] for t_ in (0, 350, n - 1)]),
+                     "eager prefill")
