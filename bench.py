@@ -433,6 +433,11 @@ def main():
         extra.update(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs))
 
     cpu = None if args.no_cpu else cpu_baseline(args, inp, M)
+    if not args.no_dense:
+        peaks = achievable_peaks(torch)
+        extra["achievable_peaks"] = peaks
+        if roof["unit"] == "GB/s":
+            roof["frac_of_achievable"] = round(roof["achieved"] / peaks["hbm_copy_GBs"], 5)
 
     rec = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1,
@@ -677,6 +682,46 @@ def bench_dropout(torch, Lb, cfg, sh, t, w_idx, n, M):
     del scores, u, idx, ws
     torch.cuda.empty_cache()
     return res
+
+
+def achievable_peaks(torch):
+    """What this GPU delivers to plain library work, next to the published
+    peaks: a 1 GiB device-to-device copy (HBM read + write) and an 8192^3
+    bf16 GEMM through torch (2-D, contiguous operands)."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * 4 * n * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), device="cuda").to(torch.bfloat16).contiguous()
+    b = torch.randn((m, m), device="cuda").to(torch.bfloat16).contiguous()
+    c = torch.empty((m, m), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBs": round(copy_gbs, 1), "hbm_copy_frac_of_published": round(copy_gbs / HBM_PEAK_GBS, 3),
+            "bf16_gemm_TFLOPs": round(gemm_tf, 1),
+            "bf16_gemm_frac_of_published": round(gemm_tf / MFMA_BF16_PEAK_TFLOPS, 3),
+            "what": "torch device copy of 1 GiB (read + write) and torch.matmul of two 8192 x 8192 bf16 matrices, "
+                    "10 timed runs each"}
 
 
 def bench_segment(torch, Lb, cfg):
