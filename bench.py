@@ -52,7 +52,7 @@ def parse():
                    help="skip the legs of the adjacent operations (indexer KL, candidate dropout, segment correction)")
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
-    p.add_argument("--prefill-iters", type=int, default=5)
+    p.add_argument("--prefill-iters", type=int, default=20)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run four 256 MiB device copies (a counter-scaling reference)")
@@ -518,14 +518,14 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
         cnt = Lb.lisa_timing_count()
         Lb.lisa_timing_enable(0)
         kern[Lb.lisa_kernel_name(kid)] = round(st[0].elapsed_time(sp[0]) * 1e3, 1) if cnt else 0.0
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(args.prefill_iters):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.prefill_iters + 1)]
+    ev[0].record()
+    for i in range(args.prefill_iters):
         call()
-    t1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.prefill_iters
+    ms = ev[0].elapsed_time(ev[-1]) / args.prefill_iters
+    per_call = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.prefill_iters)])
     # algorithmic work of each prefill kernel (rows t < M take every key and are not scored)
     r0 = min(M, n)
     scored_pairs = (n * (n + 1) - r0 * (r0 + 1)) // 2
@@ -553,6 +553,9 @@ def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
     torch.cuda.empty_cache()
     dropout = None if args.no_kl else bench_dropout(torch, Lb, cfg, sh, t, w_idx, n, M)
     res = {"prefill_workload": cfg.name, "prefill_ms": round(ms, 3),
+           "prefill_ms_median_p10_p90": [round(float(np.median(per_call)), 3),
+                                         round(float(np.percentile(per_call, 10)), 3),
+                                         round(float(np.percentile(per_call, 90)), 3)],
            "dense_causal_prefill_attention_ms": dense, "window_prefill": window,
            "prefill_tok_s": round(n / (ms * 1e-3), 1), "prefill_kernel_us": kern,
            "prefill_kernel_roofline": proofs, "indexer_kl": indexer_kl, "candidate_dropout": dropout}
