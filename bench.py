@@ -54,6 +54,7 @@ def parse():
                    help="run only the prefill leg (for kernel profiling; prints the prefill numbers)")
     p.add_argument("--prefill-iters", type=int, default=20)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-all", action="store_true", help="also time the oracle on a 16K prefill row (~30 s)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run four 256 MiB device copies (a counter-scaling reference)")
     return p.parse_args()
@@ -821,7 +822,49 @@ def cpu_baseline(args, inp, M):
         res["single_thread"] = {"value": round(n1 * B / d1, 3), "unit": "tok/s", "sample": f"{n1} steps, {d1:.1f} s"}
     except Exception as e:  # threadpoolctl missing: report without it
         res["single_thread"] = {"value": None, "error": str(e)[:200]}
+    res["per_config"] = cpu_per_config(args)
     return res
+
+
+def cpu_per_config(args):
+    """The oracle on bounded samples of the other timed workloads (input
+    generation excluded): 4 sequences of the ragged batch, one sequence of
+    the 32K / 40-head decode at M = 2048 and, with --cpu-all, one row of the
+    16K prefill."""
+    import oracle
+    from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs
+    budget = max(1.0, args.cpu_seconds / 3)
+    out = {}
+
+    def loop(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            if time.perf_counter() - t0 > budget:
+                return n, time.perf_counter() - t0
+
+    c2 = CONFIGS[2].replace(B=4)
+    inp2 = decode_inputs(c2, 2)
+    n, dt = loop(lambda: oracle.decode_step(inp2, c2.M))
+    out[CONFIGS[2].name] = {"value": round(n * c2.B / dt, 3), "unit": "tok/s",
+                            "sample": f"{n} steps of 4 sequences, lengths {inp2['seq_lens'].tolist()}, {dt:.1f} s"}
+    del inp2
+    if args.cpu_all:  # about half a minute: the oracle's prefill builds the whole sequence's linear state
+        c3 = CONFIGS[3]
+        inp3 = prefill_inputs(c3, 3)
+        rows = [8191]
+        n, dt = loop(lambda: oracle.prefill_rows(inp3, c3.M, rows))
+        out[c3.name] = {"value": round(n * len(rows) / dt, 4), "unit": "rows/s",
+                        "sample": f"{n} call(s) of the output of prefill row {rows[0]}, which includes the linear "
+                                  f"state over the whole 16384-token sequence, {dt:.1f} s"}
+        del inp3
+    c4 = CONFIGS[4].replace(B=1)
+    inp4 = decode_inputs(c4, 4)
+    n, dt = loop(lambda: oracle.decode_step(inp4, 2048))
+    out[CONFIGS[4].name] = {"value": round(n / dt, 3), "unit": "tok/s",
+                            "sample": f"{n} steps of one 32768-token sequence, M = 2048, {dt:.1f} s"}
+    return out
 
 
 if __name__ == "__main__":
