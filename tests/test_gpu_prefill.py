@@ -56,7 +56,7 @@ def test_prefill_c0_selection_bit_exact_on_oracle_scores():
         assert got[t, : len(exp)].tolist() == exp.tolist() and np.all(got[t, len(exp):] == -1), t
 
 
-@pytest.mark.parametrize("n,M,B", [(700, 128, 2), (129, 128, 1), (64, 256, 1), (333, 1, 1)])
+@pytest.mark.parametrize("n,M,B", [(700, 128, 2), (129, 128, 1), (64, 256, 1), (333, 1, 1), (1, 32, 1), (2, 1, 2)])
 def test_prefill_small_bf16(n, M, B):
     cfg = CONFIGS[3].replace(B=B, n=n, cap=n + 5)
     _full_parity(cfg, prefill_inputs(cfg, 3, n=n, salt=n), M, f"bf16 n={n} M={M}")
