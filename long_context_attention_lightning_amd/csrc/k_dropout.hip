@@ -18,8 +18,23 @@ __device__ __forceinline__ int dropout_row_len(const DropoutArgs& a, int r) {
   return a.prefill ? r % a.rows_per_seq + 1 : a.seq_lens[r];
 }
 
-// One block per row; thread k takes a contiguous run of mask words, so the
-// survivors come out in position order after one block scan of the counts.
+// One block per row; thread k takes a contiguous run of mask words (at most
+// DR_MAXW), so the survivors come out in position order after one block scan
+// of the counts.  A word's 32 uniforms and, if any candidate survives, its
+// 32 scores are read as independent 16-byte vectors, and the survivor bits
+// stay in registers between the counting and the writing pass.
+constexpr int DR_MAXW = 8;  // 2048 words of the longest row (65536) over 256 threads
+
+// 32 floats of a row from position 32 w, the part at or past ld read as 0
+__device__ __forceinline__ void load_word(const float* row, int64_t ld, int w, float (&v)[32]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int64_t p = 32 * (int64_t)w + 4 * k;
+    const float4 x = p < ld ? *reinterpret_cast<const float4*>(row + p) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[4 * k] = x.x; v[4 * k + 1] = x.y; v[4 * k + 2] = x.z; v[4 * k + 3] = x.w;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_dropout_compact(DropoutArgs a) {
   __shared__ uint32_t wsum[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
@@ -28,18 +43,22 @@ __global__ __launch_bounds__(256) void k_dropout_compact(DropoutArgs a) {
   const int per = (words + 255) / 256, w0 = min(tid * per, words), w1 = min(w0 + per, words);
   const uint32_t* mrow = a.mask + (size_t)r * a.mask_ld;
   const float* urow = a.u + (size_t)r * a.ld;
-  auto survivors = [&](int w) {  // survivor bits of word w
-    uint32_t m = mrow[w];
-    if (32 * w + 32 > len) m &= (len - 32 * w >= 32) ? ~0u : ((1u << (len - 32 * w)) - 1u);
-    uint32_t keep = 0;
-    for (uint32_t x = m; x; x &= x - 1) {
-      const int bit = __builtin_ctz(x);
-      if (urow[32 * w + bit] >= a.p) keep |= 1u << bit;
-    }
-    return keep;
-  };
+  uint32_t keep[DR_MAXW];
   uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += (uint32_t)__builtin_popcount(survivors(w));
+#pragma unroll
+  for (int i = 0; i < DR_MAXW; ++i) {
+    keep[i] = 0u;
+    const int w = w0 + i;
+    if (w >= w1) continue;
+    uint32_t m = mrow[w];
+    if (32 * w + 32 > len) m &= (1u << (len - 32 * w)) - 1u;  // len - 32 w < 32 here
+    if (!m) continue;
+    float u[32];
+    load_word(urow, a.ld, w, u);
+#pragma unroll
+    for (int b = 0; b < 32; ++b) keep[i] |= (((m >> b) & 1u) && u[b] >= a.p) ? (1u << b) : 0u;
+    cnt += (uint32_t)__builtin_popcount(keep[i]);
+  }
   const uint32_t incl = wave_incl_scan_u32(cnt);
   if (lane == WAVE - 1) wsum[wave] = incl;
   __syncthreads();
@@ -52,12 +71,19 @@ __global__ __launch_bounds__(256) void k_dropout_compact(DropoutArgs a) {
   const float* srow = a.scores + (size_t)r * a.ld;
   float* cs = a.cscore + (size_t)r * a.cld;
   int32_t* cp = a.cpos + (size_t)r * a.cld;
-  for (int w = w0; w < w1; ++w) {
-    for (uint32_t x = survivors(w); x; x &= x - 1) {
-      const int p = 32 * w + __builtin_ctz(x);
-      cs[o] = srow[p];
-      cp[o] = p;
-      ++o;
+#pragma unroll
+  for (int i = 0; i < DR_MAXW; ++i) {
+    if (!keep[i]) continue;
+    const int w = w0 + i;
+    float sv[32];
+    load_word(srow, a.ld, w, sv);
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+      if ((keep[i] >> b) & 1u) {
+        cs[o] = sv[b];
+        cp[o] = 32 * w + b;
+        ++o;
+      }
     }
   }
   if (tid == 0) a.cnt[r] = (int32_t)total;
