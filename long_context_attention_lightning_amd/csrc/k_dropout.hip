@@ -91,12 +91,20 @@ __global__ __launch_bounds__(256) void k_dropout_compact(DropoutArgs a) {
 
 __global__ __launch_bounds__(256) void k_dropout_gather(DropoutArgs a) {
   const int r = blockIdx.x;
-  const int32_t* in = a.idx2 + (size_t)r * a.M;
-  const int32_t* cp = a.cpos + (size_t)r * a.cld;
-  int32_t* out = a.idx_out + (size_t)r * a.M;
-  for (int k = threadIdx.x; k < a.M; k += 256) {
-    const int e = in[k];
-    out[k] = e >= 0 ? cp[e] : -1;
+  const int32_t* __restrict__ in = a.idx2 + (size_t)r * a.M;
+  const int32_t* __restrict__ cp = a.cpos + (size_t)r * a.cld;
+  int32_t* __restrict__ out = a.idx_out + (size_t)r * a.M;
+  constexpr int U = 8;  // entries per thread in flight
+  for (int k0 = threadIdx.x; k0 < a.M; k0 += 256 * U) {
+    int e[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) e[u] = k0 + 256 * u < a.M ? in[k0 + 256 * u] : -1;
+    int p[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) p[u] = e[u] >= 0 ? cp[e[u]] : -1;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (k0 + 256 * u < a.M) out[k0 + 256 * u] = p[u];
   }
 }
 
