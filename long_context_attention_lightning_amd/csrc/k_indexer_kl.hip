@@ -258,13 +258,26 @@ __global__ __launch_bounds__(256) void k_kl_valu(KlArgs a) {
   if (tid == 0) a.kl[((size_t)b * n + t) * sh.H_I + j] = acc_tl - acc_ts + lse_s * acc_t;
 }
 
-// Loss of Eq. 2: the mean of every KL value (one block, fixed order).
-__global__ __launch_bounds__(256) void k_kl_loss(KlArgs a, int count) {
-  __shared__ float red[4];
+// Loss of Eq. 2: the mean of every KL value (one block of 1024 threads,
+// four values in flight per thread, a fixed summation order).
+__global__ __launch_bounds__(1024) void k_kl_loss(KlArgs a, int count) {
+  __shared__ float red[16];
   float s = 0.f;
-  for (int i = threadIdx.x; i < count; i += 256) s += a.kl[i];
-  s = block_sum256(s, red);
-  if (threadIdx.x == 0) a.loss[0] = s / (float)count;
+  for (int i0 = threadIdx.x; i0 < count; i0 += 4096) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i0 + 1024 * u < count ? a.kl[i0 + 1024 * u] : 0.f;
+    s += (v[0] + v[1]) + (v[2] + v[3]);
+  }
+  s = group_sum(s, WAVE);
+  if ((threadIdx.x & (WAVE - 1)) == 0) red[threadIdx.x / WAVE] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) t += red[w];
+    a.loss[0] = t / (float)count;
+  }
 }
 
 bool kl_mfma_supported(const Shape& sh) {
@@ -295,7 +308,7 @@ hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_indexer_kl_loss(const KlArgs& a, hipStream_t st) {
-  klaunch(k_kl_loss, dim3(1), dim3(256), 0, st, a, a.sh.B * a.n * a.sh.H_I);
+  klaunch(k_kl_loss, dim3(1), dim3(1024), 0, st, a, a.sh.B * a.n * a.sh.H_I);
   return hipGetLastError();
 }
 
