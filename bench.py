@@ -70,7 +70,8 @@ def _lens(L, B):
 
 def decode_bytes(cfg, L, M, B, indexer=True):
     """Per-step bytes of the whole decode step (all sequences); without the
-    indexer (sliding window) the index keys are not read."""
+    indexer (sliding window, or a budget M that covers every position) the
+    index keys are not read."""
     tot = 0
     for l in _lens(L, B):
         m = min(M, int(l))
@@ -260,7 +261,9 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
                               inp["seq_lens"].astype(np.int64), traffic_prefix)
 
     lens = inp["seq_lens"].astype(np.int64)
-    indexer = not (flags & Lb.LISA_SLIDING_WINDOW)
+    # no index-key stream in window mode, nor when the budget covers every
+    # position (the library then skips scoring and selection)
+    indexer = not (flags & Lb.LISA_SLIDING_WINDOW) and M < Lctx
     work = {0: (phase_a_bytes(cfg, lens, B, indexer), "hbm"),
             1: (SELECT_OPS_PER_KEY * int(lens.sum()), "alu"),
             12: (attention_bytes(cfg, lens, M, B) + 4 * int(lens.sum()), "hbm"),

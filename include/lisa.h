@@ -138,6 +138,10 @@ size_t lisa_workspace_bytes(const lisa_shape* shape, int op, int32_t n);
  * out       [B, H_q, d] T.
  * idx_out   nullable [B, M] int32: ascending selected positions, -1 padded.
  * ws        workspace of lisa_workspace_bytes(shape, LISA_OP_DECODE, 0) bytes.
+ * With M >= max_len every position is selected whatever the scores, so the
+ * step appends k_idx_new but reads neither q_idx, w_idx nor the cached index
+ * keys (they must still be valid pointers); the results are those of the
+ * full selection.
  */
 int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens,
                      const void* q, const void* k_new, const void* v_new,

@@ -11,9 +11,10 @@
 //   * gate chunks: partial dot products x . W_g[:, h] over 64 hidden rows
 //     (Section 3.3 Eq. 5); the attention epilogue sums them.
 // Attention: gathered GQA softmax attention over the selected rows, split
-//   over the selected set, with an in-kernel combine by the last split block
-//   and the gate epilogue out = g*O_s + (1-g)*O_L (Section 3.2 Eq. 1, with
-//   the gate on the sparse branch).
+//   over the selected set; each split writes its (max, sum, accumulator)
+//   partial, and a separate merge launch combines the splits and applies the
+//   gate epilogue out = g*O_s + (1-g)*O_L (Section 3.2 Eq. 1, with the gate
+//   on the sparse branch).
 #include <type_traits>
 
 #include "lisa_common.h"

@@ -399,6 +399,11 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   if (rc) return rc;
   if ((rc = check_decode_len(sh))) return rc;
   const bool window = sh.flags & LISA_SLIDING_WINDOW;  // no indexer: its arguments are not used
+  // A budget of at least max_len keeps every position of every sequence, so
+  // the scores cannot change the selection: the step appends the index key
+  // but neither scores nor selects, and attends to positions 0 .. L-1 as the
+  // window path does (a window of M >= L is the whole prefix).
+  const bool take_all = !window && sh.M >= sh.max_len;
   REQUIRE_PTR(seq_lens); REQUIRE_PTR(q); REQUIRE_PTR(k_new); REQUIRE_PTR(v_new);
   REQUIRE_PTR(q_lin); REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(x);
   REQUIRE_PTR(w_gate); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
@@ -421,12 +426,12 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   pa.o_lin = at<float>(ws, w.o_lin); pa.lin_den = at<float>(ws, w.lin_den);
   pa.gate_part = at<float>(ws, w.gate); pa.gate_chunks = decode_gate_chunks(sh);
   pa.append = 1; pa.do_scores = 1; pa.do_linear = 1; pa.do_gate = 1; pa.linear_output = 1;
-  if (window) {  // append without scoring; the window's index list if asked for
-    pa.q_idx = nullptr; pa.k_idx_new = nullptr; pa.k_idx_cache = nullptr; pa.w_idx = nullptr;
+  if (window || take_all) {  // append without scoring; the window's index list if asked for
+    if (window) { pa.q_idx = nullptr; pa.k_idx_new = nullptr; pa.k_idx_cache = nullptr; pa.w_idx = nullptr; }
     pa.do_scores = 0; pa.window_idx = idx_out; pa.M = sh.M;
   }
   LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
-  if (window) {
+  if (window || take_all) {
     AttnArgs aa{};
     aa.sh = sh; aa.n_rows = sh.B; aa.rows_per_seq = 1; aa.prefill = 0; aa.dense = 0; aa.window = 1;
     aa.seq_lens = seq_lens; aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = nullptr; aa.idx_ld = 0;

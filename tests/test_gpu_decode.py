@@ -77,6 +77,10 @@ SMALL = [
      [3, 255, 256, 257, 1024], 256),
     ("fp32 G7 d128", dict(dtype="f32"), [1, 100, 600], 64),
     ("bf16 M=1", dict(), [1, 2, 50], 1),
+    # budgets that cover every position: no scoring or selection, the index key still appended
+    ("bf16 M > every length", dict(), [1, 2, 100, 700], 1000),
+    ("fp32 M = longest", dict(dtype="f32", H_q=2, H_kv=1, d=32, H_I=1, H_Ik=1, d_I=16, H_L=2, hidden=64),
+     [1, 33, 300], 300),
 ]
 
 

@@ -73,6 +73,22 @@ def test_kl_mfma_teacher_group_sizes(gt, H_q, H_kv, n):
     _check(cfg, inp, n, list(range(n)), f"mfma G_T={gt}")
 
 
+def test_kl_mfma_teacher_logits_growing_along_keys():
+    """Teacher logits that grow along the keys (every query 1, key j = j/8 in
+    every dimension: logit sqrt(d) j / 8, about 2 j in base 2), so a row's
+    logits span several hundred in base 2 and its later keys dominate.  The
+    running maximum of the first pass must rescale its sums all along the
+    row; an offset fixed by a row's first keys would leave the fp32 range."""
+    n = 200
+    cfg = CONFIGS[3].replace(n=n, cap=n)
+    inp = prefill_inputs(cfg, 3, n=n, salt=43)
+    q = np.ones_like(inp["q"])
+    k = np.empty_like(inp["k"])
+    k[:] = (np.arange(n, dtype=np.float32) / 8.0)[None, :, None, None]  # exact in bf16 for j < 256
+    inp["q"], inp["k"] = q, k
+    _check(cfg, inp, n, list(range(n)), "mfma growing logits")
+
+
 @pytest.mark.parametrize("label,cid,over,n", [
     ("valu fp32 C0", 0, {}, 256),
     ("valu bf16 d64 shared key", 3, dict(H_q=6, H_kv=2, H_L=6, d=64, H_I=2, H_Ik=1, d_I=32, hidden=96), 150),
