@@ -6,8 +6,10 @@ import torch
 
 import oracle
 from lisa_inputs import CONFIGS, decode_inputs
-from gpu_helpers import (RECALL_MIN, assert_out_close, assert_state_close, check_idx_format,
-                         gpu_decode, gpu_dense_decode, out_errors, recall, host, saturate_gate)
+import long_context_attention_lightning_amd as L
+from gpu_helpers import (RECALL_MIN, assert_out_close, assert_state_close, check_idx_format, dev,
+                         gpu_decode, gpu_dense_decode, out_errors, recall, host, saturate_gate, shape_of,
+                         tdtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +132,60 @@ def test_decode_is_deterministic():
     a, b = gpu_decode(cfg, inp, repeat=2)
     assert torch.equal(a["out_t"], b["out_t"])
     assert np.array_equal(a["S"], b["S"]) and np.array_equal(a["idx"], b["idx"])
+
+
+@pytest.mark.parametrize("M", [512, 2048, 6000], ids=["fused select", "separate select", "every position"])
+def test_decode_graph_replays_match_eager(M):
+    """A decode step of eight sequences captured in a graph: every replay must
+    reproduce the eager step bit for bit (output, index list, state, caches),
+    with eager work (state resets) between the replays.  M = 512 takes the
+    fused select + attention, 2048 the separate select and gather, 6000
+    (>= every length) the path without scoring."""
+    cfg = CONFIGS[2].replace(B=8, L_lo=1000, L_hi=5000, cap=5000)
+    inp = decode_inputs(cfg, 2, salt=78)
+    seq = inp["seq_lens"]
+    T = tdtype(cfg)
+    sh = shape_of(cfg, M=M, max_len=int(seq.max()), cap=cfg.cap, B=cfg.B)
+    t = {k: dev(inp[k], T) for k in ("q", "k_new", "v_new", "q_idx", "k_idx_new", "q_lin", "k_lin", "v_lin",
+                                     "x", "w_gate")}
+    w_idx = dev(inp["w_idx"], torch.float32)
+    seq_t = torch.from_numpy(seq.astype(np.int32)).cuda()
+    S0, z0 = dev(inp["S0"], torch.float32), dev(inp["z0"], torch.float32)
+    caches = [dev(inp[k], T) for k in ("k_cache", "v_cache", "k_idx_cache")]
+    ws = L.workspace(sh, L.LISA_OP_DECODE)
+
+    def bufs():
+        return dict(S=S0.clone(), z=z0.clone(), kc=[c.clone() for c in caches],
+                    out=torch.empty((cfg.B, cfg.H_q, cfg.d), dtype=T, device="cuda"),
+                    idx=torch.full((cfg.B, M), -7, dtype=torch.int32, device="cuda"))
+
+    def run(b):
+        L.lisa_decode_step(sh, seq_t, t["q"], t["k_new"], t["v_new"], t["q_idx"], t["k_idx_new"], t["q_lin"],
+                           t["k_lin"], t["v_lin"], t["x"], t["w_gate"], w_idx, *b["kc"], b["S"], b["z"], b["out"],
+                           b["idx"], ws)
+
+    s = torch.cuda.Stream()
+    e = bufs()
+    with torch.cuda.stream(s):  # eager, on the stream the graph is captured on
+        run(e)
+    torch.cuda.synchronize()
+    gb = bufs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run(gb)
+    for rep in range(3):
+        gb["S"].copy_(S0)
+        gb["z"].copy_(z0)
+        gb["out"].zero_()
+        gb["idx"].fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(gb["out"], e["out"]) and torch.equal(gb["idx"], e["idx"]), rep
+        assert torch.equal(gb["S"], e["S"]) and torch.equal(gb["z"], e["z"]), rep
+        for c_g, c_e in zip(gb["kc"], e["kc"]):
+            assert torch.equal(c_g, c_e), rep
+    ref = oracle.decode_step(inp, M)
+    assert recall(host(e["idx"]), ref["idx"]) >= RECALL_MIN
+    assert_out_close(cfg, host(e["out"]), ref["out"], f"eager decode M={M}")
+    assert_state_close(host(e["S"]), host(e["z"]), ref["S"], ref["z"], f"eager decode M={M}")
