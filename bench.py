@@ -133,7 +133,7 @@ def kernel_roofline(name, avg_ms, work, bound, traffic_key=None):
             "algorithmic_work_per_launch": work, "avg_launch_us": round(avg_ms * 1e3, 3)}
 
 
-def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, traffic_prefix="", flags=0,
+def bench_decode(args, torch, Lb, cfg, nbuf, steps, warmup, with_dense, traffic_prefix="", flags=0,
                  with_mass=False):
     """Graph-replayed decode steps of one workload over nbuf buffer sets:
     step time, per-kernel durations and rooflines, the dense baseline, and
@@ -142,7 +142,7 @@ def bench_decode(args, torch, Lb, cfg, cid, nbuf, steps, warmup, with_dense, tra
     B, Lctx, M = cfg.B, (cfg.L or cfg.L_hi), cfg.M
     T = torch.bfloat16
     print(f"# decode: {cfg.name} B={B} L={Lctx} M={M} nbuf={nbuf}", file=sys.stderr, flush=True)
-    inp = decode_inputs(cfg, cid)
+    inp = decode_inputs(cfg)
 
     def up(a, dt=T):
         return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt).contiguous()
@@ -356,13 +356,12 @@ def main():
 
     import torch
     import long_context_attention_lightning_amd as Lb
-    from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs
+    from lisa_inputs import QWEN7B_DECODE_16K, QWEN7B_RAGGED_DECODE, QWEN14B_DECODE_32K, prefill_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     Lb.library()
-    cid = 1
-    cfg = CONFIGS[cid]
+    cfg = QWEN7B_DECODE_16K
     B, Lctx, M = cfg.B, cfg.L, cfg.M
     T = torch.bfloat16
     print(f"# bench: {cfg.name} B={B} L={Lctx} M={M} nbuf={args.nbuf}", file=sys.stderr, flush=True)
@@ -375,24 +374,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.prefill_only:
-        print(json.dumps(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs)), flush=True)
+        print(json.dumps(bench_prefill(args, torch, Lb, prefill_inputs)), flush=True)
         return
     if args.batched_only:
-        cb = CONFIGS[2]
-        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense, "batched:",
+        cb = QWEN7B_RAGGED_DECODE
+        db = bench_decode(args, torch, Lb, cb, 2, args.batched_steps, 8, not args.no_dense, "batched:",
                           with_mass=True)
         db.pop("inp")
         print(json.dumps({k: v for k, v in db.items()}), flush=True)
         return
-    d = bench_decode(args, torch, Lb, cfg, cid, args.nbuf, args.steps, args.warmup, not args.no_dense)
+    d = bench_decode(args, torch, Lb, cfg, args.nbuf, args.steps, args.warmup, not args.no_dense)
     inp = d.pop("inp")
     ms_step, done, roof = d.pop("ms_step"), d.pop("steps"), d.pop("roofline")
     tok_s = B / (ms_step * 1e-3)
     extra = d
     extra["pages_context"] = "about 50% end-to-end inference speedup at 16K context (other hardware, whole model)"
     if not args.no_batched:
-        cb = CONFIGS[2]
-        db = bench_decode(args, torch, Lb, cb, 2, 2, args.batched_steps, 8, not args.no_dense, "batched:",
+        cb = QWEN7B_RAGGED_DECODE
+        db = bench_decode(args, torch, Lb, cb, 2, args.batched_steps, 8, not args.no_dense, "batched:",
                           with_mass=True)
         db.pop("inp")
         bms = db.pop("ms_step")
@@ -402,7 +401,7 @@ def main():
         del db
         torch.cuda.empty_cache()
     if not args.no_window:
-        dw = bench_decode(args, torch, Lb, cfg, cid, 8, 160, 16, False, "window:", flags=Lb.LISA_SLIDING_WINDOW)
+        dw = bench_decode(args, torch, Lb, cfg, 8, 160, 16, False, "window:", flags=Lb.LISA_SLIDING_WINDOW)
         dw.pop("inp")
         wms = dw.pop("ms_step")
         dw.pop("steps")
@@ -411,11 +410,11 @@ def main():
                                       kernel_us=dw["kernel_us"], step_hbm_roofline_frac=dw["step_hbm_roofline_frac"])
         torch.cuda.empty_cache()
     if not args.no_sweep:
-        c4 = CONFIGS[4]
+        c4 = QWEN14B_DECODE_32K
         sweep = {}
         for Mv in c4.M_sweep:
             cm = c4.replace(M=Mv)
-            dm = bench_decode(args, torch, Lb, cm, 4, 2, 32, 4, Mv == c4.M_sweep[0] and not args.no_dense,
+            dm = bench_decode(args, torch, Lb, cm, 2, 32, 4, Mv == c4.M_sweep[0] and not args.no_dense,
                               f"sweep{Mv}:")
             dm.pop("inp")
             mms = dm.pop("ms_step")
@@ -432,9 +431,9 @@ def main():
                                        **sweep)
 
     if not args.no_kl:
-        extra["segment_correct"] = bench_segment(torch, Lb, CONFIGS[2])
+        extra["segment_correct"] = bench_segment(torch, Lb, QWEN7B_RAGGED_DECODE)
     if not args.no_prefill:
-        extra.update(bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs))
+        extra.update(bench_prefill(args, torch, Lb, prefill_inputs))
 
     cpu = None if args.no_cpu else cpu_baseline(args, inp, M)
     if not args.no_dense:
@@ -483,13 +482,13 @@ def source_hash(files):
     return h.hexdigest()
 
 
-def bench_prefill(args, torch, Lb, CONFIGS, prefill_inputs):
-    cid = 3
-    cfg = CONFIGS[cid]
+def bench_prefill(args, torch, Lb, prefill_inputs):
+    from lisa_inputs import QWEN7B_PREFILL_16K
+    cfg = QWEN7B_PREFILL_16K
     n, M = cfg.n, cfg.M
     T = torch.bfloat16
     print(f"# prefill: {cfg.name} n={n}", file=sys.stderr, flush=True)
-    inp = prefill_inputs(cfg, cid)
+    inp = prefill_inputs(cfg)
 
     def up(a, dt=T):
         return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt).contiguous()
@@ -835,7 +834,7 @@ def cpu_per_config(args):
     the 32K / 40-head decode at M = 2048 and, with --cpu-all, one row of the
     16K prefill."""
     import oracle
-    from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs
+    from lisa_inputs import QWEN7B_RAGGED_DECODE, QWEN7B_PREFILL_16K, QWEN14B_DECODE_32K, decode_inputs, prefill_inputs
     budget = max(1.0, args.cpu_seconds / 3)
     out = {}
 
@@ -847,26 +846,26 @@ def cpu_per_config(args):
             if time.perf_counter() - t0 > budget:
                 return n, time.perf_counter() - t0
 
-    c2 = CONFIGS[2].replace(B=4)
-    inp2 = decode_inputs(c2, 2)
+    c2 = QWEN7B_RAGGED_DECODE.replace(B=4)
+    inp2 = decode_inputs(c2)
     n, dt = loop(lambda: oracle.decode_step(inp2, c2.M))
-    out[CONFIGS[2].name] = {"value": round(n * c2.B / dt, 3), "unit": "tok/s",
-                            "sample": f"{n} steps of 4 sequences, lengths {inp2['seq_lens'].tolist()}, {dt:.1f} s"}
+    out[c2.name] = {"value": round(n * c2.B / dt, 3), "unit": "tok/s",
+                    "sample": f"{n} steps of 4 sequences, lengths {inp2['seq_lens'].tolist()}, {dt:.1f} s"}
     del inp2
     if args.cpu_all:  # about half a minute: the oracle's prefill builds the whole sequence's linear state
-        c3 = CONFIGS[3]
-        inp3 = prefill_inputs(c3, 3)
+        c3 = QWEN7B_PREFILL_16K
+        inp3 = prefill_inputs(c3)
         rows = [8191]
         n, dt = loop(lambda: oracle.prefill_rows(inp3, c3.M, rows))
         out[c3.name] = {"value": round(n * len(rows) / dt, 4), "unit": "rows/s",
                         "sample": f"{n} call(s) of the output of prefill row {rows[0]}, which includes the linear "
                                   f"state over the whole 16384-token sequence, {dt:.1f} s"}
         del inp3
-    c4 = CONFIGS[4].replace(B=1)
-    inp4 = decode_inputs(c4, 4)
+    c4 = QWEN14B_DECODE_32K.replace(B=1)
+    inp4 = decode_inputs(c4)
     n, dt = loop(lambda: oracle.decode_step(inp4, 2048))
-    out[CONFIGS[4].name] = {"value": round(n / dt, 3), "unit": "tok/s",
-                            "sample": f"{n} steps of one 32768-token sequence, M = 2048, {dt:.1f} s"}
+    out[c4.name] = {"value": round(n / dt, 3), "unit": "tok/s",
+                    "sample": f"{n} steps of one 32768-token sequence, M = 2048, {dt:.1f} s"}
     return out
 
 

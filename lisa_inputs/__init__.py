@@ -6,14 +6,16 @@ precision; it holds none of the method's arithmetic (no scores, no selection,
 no attention, no feature map, no gate).
 
 Every tensor comes from its own stream,
-``numpy.random.default_rng([20260723, config_id, tensor_id])``, drawn in
+``numpy.random.default_rng([20260723, seed_id, tensor_id])``, drawn in
 float32 and then rounded to bfloat16 (round to nearest even) for the bf16
-configurations.  Arrays are returned as float32 numpy arrays whose values are
+configurations; ``seed_id`` is the workload's ``sid`` unless a caller passes
+its own.  Arrays are returned as float32 numpy arrays whose values are
 exactly representable in the storage dtype, so that torch can upload them to
 bf16 without a second rounding and the oracle can upcast them to float64
 exactly.
 
-Shapes follow the configurations the layer is measured on:
+Shapes follow the workloads the layer is measured on (module constants of
+the same names in capitals):
 
 * ``tiny_fp32_prefill``   one sequence of 256 tokens, 2/1 heads, head dim 32
 * ``qwen7b_decode_16k``   Qwen-7B-shaped decode step at 16384 cached tokens
@@ -54,6 +56,7 @@ T_Z0 = 16
 @dataclasses.dataclass(frozen=True)
 class LayerConfig:
     name: str
+    sid: int             # seed stream id of the workload's inputs
     mode: str            # "prefill" | "decode"
     dtype: str           # "f32" | "bf16"
     B: int
@@ -78,24 +81,31 @@ class LayerConfig:
         return dataclasses.replace(self, **kw)
 
 
-CONFIGS: Dict[int, LayerConfig] = {
-    0: LayerConfig(name="tiny_fp32_prefill", mode="prefill", dtype="f32", B=1,
-                   H_q=2, H_kv=1, d=32, H_I=1, H_Ik=1, d_I=16, H_L=2, hidden=64,
-                   M=32, n=256, cap=256, chunk=64),
-    1: LayerConfig(name="qwen7b_decode_16k", mode="decode", dtype="bf16", B=1,
-                   H_q=28, H_kv=4, d=128, H_I=4, H_Ik=4, d_I=64, H_L=28,
-                   hidden=3584, M=2048, L=16384, cap=16384),
-    2: LayerConfig(name="qwen7b_ragged_decode", mode="decode", dtype="bf16", B=32,
-                   H_q=28, H_kv=4, d=128, H_I=4, H_Ik=4, d_I=64, H_L=28,
-                   hidden=3584, M=2048, L_lo=4096, L_hi=16384, cap=16384),
-    3: LayerConfig(name="qwen7b_prefill_16k", mode="prefill", dtype="bf16", B=1,
-                   H_q=28, H_kv=4, d=128, H_I=4, H_Ik=4, d_I=64, H_L=28,
-                   hidden=3584, M=2048, n=16384, cap=16384, chunk=64),
-    4: LayerConfig(name="qwen14b_decode_32k", mode="decode", dtype="bf16", B=8,
-                   H_q=40, H_kv=8, d=128, H_I=4, H_Ik=4, d_I=64, H_L=40,
-                   hidden=5120, M=2048, L=32768, cap=32768,
-                   M_sweep=(512, 2048, 8192, 32768)),
-}
+TINY_FP32_PREFILL = LayerConfig(
+    name="tiny_fp32_prefill", sid=0, mode="prefill", dtype="f32", B=1,
+    H_q=2, H_kv=1, d=32, H_I=1, H_Ik=1, d_I=16, H_L=2, hidden=64,
+    M=32, n=256, cap=256, chunk=64)
+QWEN7B_DECODE_16K = LayerConfig(
+    name="qwen7b_decode_16k", sid=1, mode="decode", dtype="bf16", B=1,
+    H_q=28, H_kv=4, d=128, H_I=4, H_Ik=4, d_I=64, H_L=28,
+    hidden=3584, M=2048, L=16384, cap=16384)
+QWEN7B_RAGGED_DECODE = LayerConfig(
+    name="qwen7b_ragged_decode", sid=2, mode="decode", dtype="bf16", B=32,
+    H_q=28, H_kv=4, d=128, H_I=4, H_Ik=4, d_I=64, H_L=28,
+    hidden=3584, M=2048, L_lo=4096, L_hi=16384, cap=16384)
+QWEN7B_PREFILL_16K = LayerConfig(
+    name="qwen7b_prefill_16k", sid=3, mode="prefill", dtype="bf16", B=1,
+    H_q=28, H_kv=4, d=128, H_I=4, H_Ik=4, d_I=64, H_L=28,
+    hidden=3584, M=2048, n=16384, cap=16384, chunk=64)
+QWEN14B_DECODE_32K = LayerConfig(
+    name="qwen14b_decode_32k", sid=4, mode="decode", dtype="bf16", B=8,
+    H_q=40, H_kv=8, d=128, H_I=4, H_Ik=4, d_I=64, H_L=40,
+    hidden=5120, M=2048, L=32768, cap=32768,
+    M_sweep=(512, 2048, 8192, 32768))
+
+WORKLOADS: Dict[str, LayerConfig] = {
+    c.name: c for c in (TINY_FP32_PREFILL, QWEN7B_DECODE_16K, QWEN7B_RAGGED_DECODE,
+                        QWEN7B_PREFILL_16K, QWEN14B_DECODE_32K)}
 
 
 # ----------------------------------------------------------------------------
@@ -119,16 +129,16 @@ def to_storage(a: np.ndarray, dtype: str) -> np.ndarray:
     return round_bf16(a) if dtype == "bf16" else np.ascontiguousarray(a)
 
 
-def rng(config_id: int, tensor_id: int, salt: int = 0) -> np.random.Generator:
-    key = [SEED_BASE, int(config_id), int(tensor_id)]
+def rng(seed_id: int, tensor_id: int, salt: int = 0) -> np.random.Generator:
+    key = [SEED_BASE, int(seed_id), int(tensor_id)]
     if salt:
         key.append(int(salt))
     return np.random.default_rng(key)
 
 
-def normal(config_id: int, tensor_id: int, shape, dtype: str, std: float = 1.0,
+def normal(seed_id: int, tensor_id: int, shape, dtype: str, std: float = 1.0,
            salt: int = 0) -> np.ndarray:
-    g = rng(config_id, tensor_id, salt)
+    g = rng(seed_id, tensor_id, salt)
     a = g.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
         a *= np.float32(std)
@@ -138,8 +148,8 @@ def normal(config_id: int, tensor_id: int, shape, dtype: str, std: float = 1.0,
 # ----------------------------------------------------------------------------
 # input sets
 # ----------------------------------------------------------------------------
-def prefill_inputs(cfg: LayerConfig, config_id: int, n: Optional[int] = None,
-                   salt: int = 0) -> Dict[str, np.ndarray]:
+def prefill_inputs(cfg: LayerConfig, n: Optional[int] = None, salt: int = 0,
+                   seed_id: Optional[int] = None) -> Dict[str, np.ndarray]:
     """All inputs of a causal prefill of ``n`` tokens per sequence.
 
     Activations are N(0,1); the gate weight is N(0, 1/hidden); the indexer
@@ -147,7 +157,7 @@ def prefill_inputs(cfg: LayerConfig, config_id: int, n: Optional[int] = None,
     """
     n = cfg.n if n is None else n
     B, dt = cfg.B, cfg.dtype
-    c = config_id
+    c = cfg.sid if seed_id is None else seed_id
     return {
         "q": normal(c, T_Q, (B, n, cfg.H_q, cfg.d), dt, salt=salt),
         "k": normal(c, T_K, (B, n, cfg.H_kv, cfg.d), dt, salt=salt),
@@ -166,15 +176,15 @@ def prefill_inputs(cfg: LayerConfig, config_id: int, n: Optional[int] = None,
     }
 
 
-def ragged_lengths(cfg: LayerConfig, config_id: int) -> np.ndarray:
+def ragged_lengths(cfg: LayerConfig, seed_id: Optional[int] = None) -> np.ndarray:
     if cfg.L:
         return np.full((cfg.B,), cfg.L, dtype=np.int32)
-    g = rng(config_id, T_SEQ_LENS)
+    g = rng(cfg.sid if seed_id is None else seed_id, T_SEQ_LENS)
     return g.integers(cfg.L_lo, cfg.L_hi + 1, size=cfg.B, dtype=np.int64).astype(np.int32)
 
 
-def decode_inputs(cfg: LayerConfig, config_id: int, seq_lens: Optional[np.ndarray] = None,
-                  salt: int = 0) -> Dict[str, np.ndarray]:
+def decode_inputs(cfg: LayerConfig, seq_lens: Optional[np.ndarray] = None, salt: int = 0,
+                  seed_id: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Inputs of one decode step.
 
     ``seq_lens[b]`` counts the new token: the caches hold rows
@@ -188,9 +198,10 @@ def decode_inputs(cfg: LayerConfig, config_id: int, seq_lens: Optional[np.ndarra
     deviation sqrt(0.62(L-1)) and clipped below at 1.  (These are the first
     two moments of such a sum; only their order of magnitude matters.)
     """
-    B, dt, c = cfg.B, cfg.dtype, config_id
+    B, dt = cfg.B, cfg.dtype
+    c = cfg.sid if seed_id is None else seed_id
     if seq_lens is None:
-        seq_lens = ragged_lengths(cfg, config_id)
+        seq_lens = ragged_lengths(cfg, c)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     cap = cfg.cap if cfg.cap else int(seq_lens.max())
     hist = np.maximum(seq_lens.astype(np.float64) - 1.0, 0.0)
@@ -222,9 +233,9 @@ def decode_inputs(cfg: LayerConfig, config_id: int, seq_lens: Optional[np.ndarra
     }
 
 
-def signed_head_weights(H_I: int, config_id: int = 99) -> np.ndarray:
+def signed_head_weights(H_I: int, seed_id: int = 99) -> np.ndarray:
     """Seeded signed indexer head weights (exercise negative and -0.0 scores)."""
-    w = rng(config_id, T_W_IDX).standard_normal((H_I,), dtype=np.float32)
+    w = rng(seed_id, T_W_IDX).standard_normal((H_I,), dtype=np.float32)
     return w
 
 

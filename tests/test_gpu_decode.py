@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import oracle
-from lisa_inputs import CONFIGS, decode_inputs
+from lisa_inputs import QWEN7B_DECODE_16K, QWEN7B_RAGGED_DECODE, QWEN14B_DECODE_32K, decode_inputs
 import long_context_attention_lightning_amd as L
 from gpu_helpers import (RECALL_MIN, assert_out_close, assert_state_close, check_idx_format, dev,
                          gpu_decode, gpu_dense_decode, out_errors, recall, host, saturate_gate, shape_of,
@@ -41,31 +41,31 @@ def _branches(cfg, inp, M, label):
         assert_out_close(cfg, g["out"], ref[key], f"{label} {key}")
 
 
-def test_decode_c1_qwen7b_16k():
-    cfg = CONFIGS[1]
-    inp = decode_inputs(cfg, 1)
-    _parity(cfg, inp, cfg.M, "C1")
-    _branches(cfg, inp, cfg.M, "C1")
+def test_decode_qwen7b_16k():
+    cfg = QWEN7B_DECODE_16K
+    inp = decode_inputs(cfg)
+    _parity(cfg, inp, cfg.M, "qwen7b 16K")
+    _branches(cfg, inp, cfg.M, "qwen7b 16K")
 
 
-def test_decode_c2_ragged_batch32():
-    cfg = CONFIGS[2]
-    inp = decode_inputs(cfg, 2)
+def test_decode_qwen7b_ragged_batch32():
+    cfg = QWEN7B_RAGGED_DECODE
+    inp = decode_inputs(cfg)
     assert inp["seq_lens"].min() >= 4096 and inp["seq_lens"].max() <= 16384
-    _parity(cfg, inp, cfg.M, "C2")
-    _branches(cfg, inp, cfg.M, "C2")
+    _parity(cfg, inp, cfg.M, "qwen7b ragged B=32")
+    _branches(cfg, inp, cfg.M, "qwen7b ragged B=32")
 
 
 @pytest.mark.slow
-def test_decode_c4_qwen14b_m_sweep_and_dense():
-    cfg = CONFIGS[4]
-    inp = decode_inputs(cfg, 4)
+def test_decode_qwen14b_32k_m_sweep_and_dense():
+    cfg = QWEN14B_DECODE_32K
+    inp = decode_inputs(cfg)
     for M in cfg.M_sweep:
-        g, ref = _parity(cfg, inp, M, f"C4 M={M}")
+        g, ref = _parity(cfg, inp, M, f"qwen14b 32K M={M}")
     # M = L: the sparse branch is full causal attention; compare the dense kernel
     dense_gpu = gpu_dense_decode(cfg, inp, g["k_cache"], g["v_cache"])
     dense_ref = oracle.dense_decode(inp)
-    assert_out_close(cfg, dense_gpu, dense_ref, "C4 dense kernel")
+    assert_out_close(cfg, dense_gpu, dense_ref, "qwen14b 32K dense kernel")
     np.testing.assert_allclose(ref["o_sparse"], dense_ref, rtol=1e-10, atol=1e-12)
 
 
@@ -88,22 +88,22 @@ SMALL = [
 
 @pytest.mark.parametrize("label,over,lens,M", SMALL, ids=[s[0] for s in SMALL])
 def test_decode_small_shapes(label, over, lens, M):
-    base = CONFIGS[1].replace(B=len(lens), L=0, cap=max(lens) + 3, **over)
-    inp = decode_inputs(base, 11, seq_lens=np.array(lens, np.int32))
+    base = QWEN7B_DECODE_16K.replace(B=len(lens), L=0, cap=max(lens) + 3, **over)
+    inp = decode_inputs(base, seed_id=11, seq_lens=np.array(lens, np.int32))
     _parity(base, inp, M, label)
     _branches(base, inp, M, label)
 
 
 def test_decode_signed_head_weights():
-    cfg = CONFIGS[1].replace(B=3, L=0, cap=3000)
-    inp = decode_inputs(cfg, 12, seq_lens=np.array([100, 2048, 2999], np.int32))
+    cfg = QWEN7B_DECODE_16K.replace(B=3, L=0, cap=3000)
+    inp = decode_inputs(cfg, seed_id=12, seq_lens=np.array([100, 2048, 2999], np.int32))
     inp["w_idx"] = np.array([1.0, -0.5, 0.0, 2.0], np.float32)
     _parity(cfg, inp, 256, "signed w")
 
 
 def test_decode_unnormalized_linear():
-    cfg = CONFIGS[1].replace(B=2, L=0, cap=600, hidden=64)
-    inp = decode_inputs(cfg, 13, seq_lens=np.array([10, 500], np.int32))
+    cfg = QWEN7B_DECODE_16K.replace(B=2, L=0, cap=600, hidden=64)
+    inp = decode_inputs(cfg, seed_id=13, seq_lens=np.array([10, 500], np.int32))
     inp["S0"] = inp["S0"] * 0.01
     g = gpu_decode(cfg, inp, M=64, flags=1)
     ref = oracle.decode_step(inp, 64, normalized=False)
@@ -113,8 +113,8 @@ def test_decode_unnormalized_linear():
 
 
 def test_decode_gate_saturated_equals_dense_at_full_budget():
-    cfg = CONFIGS[1].replace(B=3, L=0, cap=5000)
-    inp = decode_inputs(cfg, 14, seq_lens=np.array([1, 777, 4999], np.int32))
+    cfg = QWEN7B_DECODE_16K.replace(B=3, L=0, cap=5000)
+    inp = decode_inputs(cfg, seed_id=14, seq_lens=np.array([1, 777, 4999], np.int32))
     inp["x"] = np.zeros_like(inp["x"])
     inp["x"][:, 0] = 1.0
     inp["w_gate"] = np.zeros_like(inp["w_gate"])
@@ -127,8 +127,8 @@ def test_decode_gate_saturated_equals_dense_at_full_budget():
 
 
 def test_decode_is_deterministic():
-    cfg = CONFIGS[2].replace(B=4, L_lo=2000, L_hi=9000, cap=9000)
-    inp = decode_inputs(cfg, 15)
+    cfg = QWEN7B_RAGGED_DECODE.replace(B=4, L_lo=2000, L_hi=9000, cap=9000)
+    inp = decode_inputs(cfg, seed_id=15)
     a, b = gpu_decode(cfg, inp, repeat=2)
     assert torch.equal(a["out_t"], b["out_t"])
     assert np.array_equal(a["S"], b["S"]) and np.array_equal(a["idx"], b["idx"])
@@ -141,8 +141,8 @@ def test_decode_graph_replays_match_eager(M):
     with eager work (state resets) between the replays.  M = 512 takes the
     fused select + attention, 2048 the separate select and gather, 6000
     (>= every length) the path without scoring."""
-    cfg = CONFIGS[2].replace(B=8, L_lo=1000, L_hi=5000, cap=5000)
-    inp = decode_inputs(cfg, 2, salt=78)
+    cfg = QWEN7B_RAGGED_DECODE.replace(B=8, L_lo=1000, L_hi=5000, cap=5000)
+    inp = decode_inputs(cfg, salt=78)
     seq = inp["seq_lens"]
     T = tdtype(cfg)
     sh = shape_of(cfg, M=M, max_len=int(seq.max()), cap=cfg.cap, B=cfg.B)

@@ -15,7 +15,7 @@ import torch
 
 import long_context_attention_lightning_amd as L
 import oracle
-from lisa_inputs import CONFIGS, prefill_inputs
+from lisa_inputs import TINY_FP32_PREFILL, QWEN7B_PREFILL_16K, prefill_inputs
 from gpu_helpers import dev, host, shape_of, tdtype
 
 pytestmark = pytest.mark.gpu
@@ -47,29 +47,29 @@ def _check(cfg, inp, n, rows, label):
     return kl
 
 
-def test_kl_mfma_grouped_teacher_c3_heads():
+def test_kl_mfma_grouped_teacher_qwen7b_heads():
     """28 query heads as 4 teacher groups of 7, one per indexer head (the
     matrix-core path); 300 rows span five 64-row blocks with a ragged tail."""
     n = 300
-    cfg = CONFIGS[3].replace(n=n, cap=n)
-    inp = prefill_inputs(cfg, 3, n=n, salt=33)
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n)
+    inp = prefill_inputs(cfg, n=n, salt=33)
     kl = _check(cfg, inp, n, list(range(n)), "mfma G_T=7")
     assert abs(kl[0, 0, 0]) < 1e-4  # one key: T = Q
 
 
 def test_kl_mfma_two_teacher_heads_batch2():
     n = 200
-    cfg = CONFIGS[3].replace(B=2, n=n, cap=n, H_q=8, H_kv=2, H_L=8, H_I=4, H_Ik=4)
-    inp = prefill_inputs(cfg, 3, n=n, salt=34)
+    cfg = QWEN7B_PREFILL_16K.replace(B=2, n=n, cap=n, H_q=8, H_kv=2, H_L=8, H_I=4, H_Ik=4)
+    inp = prefill_inputs(cfg, n=n, salt=34)
     _check(cfg, inp, n, list(range(n)), "mfma G_T=2 B=2")
 
 
 @pytest.mark.parametrize("gt,H_q,H_kv,n", [(1, 4, 2, 150), (4, 16, 4, 131), (8, 32, 4, 140)])
 def test_kl_mfma_teacher_group_sizes(gt, H_q, H_kv, n):
     """Matrix-core path for other teacher-group sizes (4 indexer heads)."""
-    cfg = CONFIGS[3].replace(n=n, cap=n, H_q=H_q, H_kv=H_kv, H_L=H_q, H_I=4, H_Ik=4)
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n, H_q=H_q, H_kv=H_kv, H_L=H_q, H_I=4, H_Ik=4)
     assert H_q // 4 == gt
-    inp = prefill_inputs(cfg, 3, n=n, salt=36 + gt)
+    inp = prefill_inputs(cfg, n=n, salt=36 + gt)
     _check(cfg, inp, n, list(range(n)), f"mfma G_T={gt}")
 
 
@@ -80,8 +80,8 @@ def test_kl_mfma_teacher_logits_growing_along_keys():
     running maximum of the first pass must rescale its sums all along the
     row; an offset fixed by a row's first keys would leave the fp32 range."""
     n = 200
-    cfg = CONFIGS[3].replace(n=n, cap=n)
-    inp = prefill_inputs(cfg, 3, n=n, salt=43)
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n)
+    inp = prefill_inputs(cfg, n=n, salt=43)
     q = np.ones_like(inp["q"])
     k = np.empty_like(inp["k"])
     k[:] = (np.arange(n, dtype=np.float32) / 8.0)[None, :, None, None]  # exact in bf16 for j < 256
@@ -89,21 +89,21 @@ def test_kl_mfma_teacher_logits_growing_along_keys():
     _check(cfg, inp, n, list(range(n)), "mfma growing logits")
 
 
-@pytest.mark.parametrize("label,cid,over,n", [
-    ("valu fp32 C0", 0, {}, 256),
-    ("valu bf16 d64 shared key", 3, dict(H_q=6, H_kv=2, H_L=6, d=64, H_I=2, H_Ik=1, d_I=32, hidden=96), 150),
+@pytest.mark.parametrize("label,base,over,n", [
+    ("valu fp32 tiny prefill", TINY_FP32_PREFILL, {}, 256),
+    ("valu bf16 d64 shared key", QWEN7B_PREFILL_16K, dict(H_q=6, H_kv=2, H_L=6, d=64, H_I=2, H_Ik=1, d_I=32, hidden=96), 150),
 ])
-def test_kl_vector_path(label, cid, over, n):
-    cfg = CONFIGS[cid].replace(n=n, cap=n, **over)
-    inp = prefill_inputs(cfg, cid, n=n, salt=35)
+def test_kl_vector_path(label, base, over, n):
+    cfg = base.replace(n=n, cap=n, **over)
+    inp = prefill_inputs(cfg, n=n, salt=35)
     _check(cfg, inp, n, list(range(n)), label)
 
 
 @pytest.mark.slow
-def test_kl_c3_16k_sampled_rows():
-    cfg = CONFIGS[3]
-    inp = prefill_inputs(cfg, 3)
+def test_kl_qwen7b_prefill_16k_sampled_rows():
+    cfg = QWEN7B_PREFILL_16K
+    inp = prefill_inputs(cfg)
     n = cfg.n
     rows = sorted(set(range(0, n, 509)) | {1, 63, 64, 2047, 2048, n - 65, n - 64, n - 1})
-    _check(cfg, inp, n, rows, "C3 16K")
+    _check(cfg, inp, n, rows, "qwen7b prefill 16K")
 

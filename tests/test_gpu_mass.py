@@ -15,7 +15,7 @@ import torch
 
 import long_context_attention_lightning_amd as L
 import oracle
-from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs
+from lisa_inputs import QWEN7B_DECODE_16K, QWEN7B_PREFILL_16K, decode_inputs, prefill_inputs
 from gpu_helpers import dev, gpu_decode, gpu_prefill, host, shape_of, tdtype
 
 pytestmark = pytest.mark.gpu
@@ -54,9 +54,9 @@ def _check(got_mass, got_bound, q_rows, K_rows, idx_rows, lens, M, label):
 def test_mass_after_decode_step_on_its_selection():
     """Decode rows (row_seq NULL): the coverage of the step's own index sets,
     with the caches as the step left them (the new key appended)."""
-    cfg = CONFIGS[1].replace(B=3, L=0, L_lo=500, L_hi=3000, cap=3072)
+    cfg = QWEN7B_DECODE_16K.replace(B=3, L=0, L_lo=500, L_hi=3000, cap=3072)
     M = 256
-    inp = decode_inputs(cfg, 1, salt=21)
+    inp = decode_inputs(cfg, salt=21)
     g = gpu_decode(cfg, inp, M=M)
     lens = inp["seq_lens"]
     K_rows = []
@@ -72,8 +72,8 @@ def test_mass_prefill_rows_share_one_sequence():
     """Sampled prefill rows of one sequence (row_seq all 0, row_len t+1) with
     the prefill's index lists, rows at and around M included."""
     n, M = 700, 100
-    cfg = CONFIGS[3].replace(n=n, cap=n)
-    inp = prefill_inputs(cfg, 3, n=n, salt=12)
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n)
+    inp = prefill_inputs(cfg, n=n, salt=12)
     g = gpu_prefill(cfg, inp, M=M)
     rows = [0, 1, 2, 98, 99, 100, 101, 257, 512, 698, 699]
     T = tdtype(cfg)
@@ -94,9 +94,9 @@ def test_mass_shapes_and_degenerate_sets(label, over, dtype):
     """Several rows per sequence, in any order; sets with -1 padding and with
     entries past the row (skipped), empty sets (mass 0), a one-key row and a
     budget that covers the whole row (mass = bound = 1)."""
-    cfg = CONFIGS[1].replace(dtype=dtype, B=2, L=0, cap=1500, H_L=over["H_q"], **over)
+    cfg = QWEN7B_DECODE_16K.replace(dtype=dtype, B=2, L=0, cap=1500, H_L=over["H_q"], **over)
     r = np.random.default_rng(8)
-    inp = decode_inputs(cfg, 1, seq_lens=np.array([1400, 1500]), salt=3)
+    inp = decode_inputs(cfg, seq_lens=np.array([1400, 1500]), salt=3)
     K_all = inp["k_cache"]
     M = 300
     specs = [(1, 1500), (0, 1400), (1, 1), (0, 250), (1, 777), (0, 1024)]
@@ -121,14 +121,14 @@ def test_mass_shapes_and_degenerate_sets(label, over, dtype):
 
 
 @pytest.mark.slow
-def test_mass_c1_full_context():
+def test_mass_qwen7b_16k_full_context():
     """One 16384-position decode row at the 28/4-head, d = 128 shape with
     M = 2048 (a random selected set and the per-head bound)."""
-    cfg = CONFIGS[1]
-    inp = decode_inputs(cfg, 1, salt=4)
+    cfg = QWEN7B_DECODE_16K
+    inp = decode_inputs(cfg, salt=4)
     n = int(inp["seq_lens"][0])
     r = np.random.default_rng(9)
     idx = np.sort(r.choice(n, cfg.M, replace=False))[None, :]
     T = tdtype(cfg)
     mass, bound = _gpu_mass(cfg, inp["q"], dev(inp["k_cache"], T), idx, [n], cfg.M)
-    _check(mass, bound, inp["q"], [inp["k_cache"][0]], idx, [n], cfg.M, "C1 16K")
+    _check(mass, bound, inp["q"], [inp["k_cache"][0]], idx, [n], cfg.M, "qwen7b decode 16K")

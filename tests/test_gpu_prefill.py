@@ -6,7 +6,7 @@ import torch
 
 import long_context_attention_lightning_amd as L
 import oracle
-from lisa_inputs import CONFIGS, prefill_inputs, decode_inputs, row_sample
+from lisa_inputs import TINY_FP32_PREFILL, QWEN7B_PREFILL_16K, prefill_inputs, decode_inputs, row_sample
 from gpu_helpers import (RECALL_MIN, assert_out_close, assert_state_close, check_idx_format,
                          dev, gpu_decode, gpu_prefill, host, recall, saturate_gate, shape_of, tdtype)
 
@@ -31,14 +31,14 @@ def _full_parity(cfg, inp, M, label):
     return g, ref
 
 
-def test_prefill_c0_tiny_fp32():
-    cfg = CONFIGS[0]
-    _full_parity(cfg, prefill_inputs(cfg, 0), cfg.M, "C0")
+def test_prefill_tiny_fp32():
+    cfg = TINY_FP32_PREFILL
+    _full_parity(cfg, prefill_inputs(cfg), cfg.M, "tiny fp32")
 
 
-def test_prefill_c0_selection_bit_exact_on_oracle_scores():
-    cfg = CONFIGS[0]
-    inp = prefill_inputs(cfg, 0)
+def test_prefill_tiny_fp32_selection_bit_exact_on_oracle_scores():
+    cfg = TINY_FP32_PREFILL
+    inp = prefill_inputs(cfg)
     n = cfg.n
     res = oracle.prefill_rows(inp, cfg.M, range(n))
     ld = n
@@ -58,8 +58,8 @@ def test_prefill_c0_selection_bit_exact_on_oracle_scores():
 
 @pytest.mark.parametrize("n,M,B", [(700, 128, 2), (129, 128, 1), (64, 256, 1), (333, 1, 1), (1, 32, 1), (2, 1, 2)])
 def test_prefill_small_bf16(n, M, B):
-    cfg = CONFIGS[3].replace(B=B, n=n, cap=n + 5)
-    _full_parity(cfg, prefill_inputs(cfg, 3, n=n, salt=n), M, f"bf16 n={n} M={M}")
+    cfg = QWEN7B_PREFILL_16K.replace(B=B, n=n, cap=n + 5)
+    _full_parity(cfg, prefill_inputs(cfg, n=n, salt=n), M, f"bf16 n={n} M={M}")
 
 
 PREFILL_SHAPES = [
@@ -71,8 +71,8 @@ PREFILL_SHAPES = [
 
 @pytest.mark.parametrize("label,over,n,M", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
 def test_prefill_bf16_shapes(label, over, n, M):
-    cfg = CONFIGS[3].replace(n=n, cap=n + 1, **over)
-    inp = prefill_inputs(cfg, 3, n=n, salt=31)
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n + 1, **over)
+    inp = prefill_inputs(cfg, n=n, salt=31)
     # start from a state carried over from an earlier part of the sequence
     r = np.random.default_rng(17)
     inp["S0"] = (r.standard_normal(inp["S0"].shape) * 30).astype(np.float32)
@@ -85,9 +85,9 @@ def test_prefill_bf16_offset_fallback():
     softmax offset taken from the first tile leaves every selected
     probability below 2^-126, so the attention must recompute with the exact
     maximum over the selected keys, and still match."""
-    cfg = CONFIGS[3].replace(n=300, cap=300)
+    cfg = QWEN7B_PREFILL_16K.replace(n=300, cap=300)
     n, M = 300, 64
-    inp = prefill_inputs(cfg, 3, n=n, salt=41)
+    inp = prefill_inputs(cfg, n=n, salt=41)
     from lisa_inputs import round_bf16
     u = np.ones(cfg.d) / np.sqrt(cfg.d)
     q = inp["q"].astype(np.float64) + 10.0 * u          # every query shares a direction
@@ -104,14 +104,14 @@ def test_prefill_bf16_offset_fallback():
 
 
 def test_prefill_fp32_shared_key_small_heads():
-    cfg = CONFIGS[0].replace(H_q=6, H_kv=2, H_L=6, H_I=2, H_Ik=1, n=300, cap=300, d=64, d_I=16)
-    _full_parity(cfg, prefill_inputs(cfg, 0, n=300, salt=5), 40, "fp32 shared key")
+    cfg = TINY_FP32_PREFILL.replace(H_q=6, H_kv=2, H_L=6, H_I=2, H_Ik=1, n=300, cap=300, d=64, d_I=16)
+    _full_parity(cfg, prefill_inputs(cfg, n=300, salt=5), 40, "fp32 shared key")
 
 
 def test_prefill_scores_out_and_topk_match_oracle():
-    cfg = CONFIGS[3].replace(n=600, cap=600)
+    cfg = QWEN7B_PREFILL_16K.replace(n=600, cap=600)
     n, M = 600, 100
-    inp = prefill_inputs(cfg, 3, n=n, salt=2)
+    inp = prefill_inputs(cfg, n=n, salt=2)
     sh = shape_of(cfg, M=M, cap=n)
     T = tdtype(cfg)
     kic = dev(inp["k_idx"], T)
@@ -135,9 +135,9 @@ def test_prefill_scores_out_and_topk_match_oracle():
 
 
 def test_linear_state_update_matches_oracle():
-    cfg = CONFIGS[3].replace(B=2)
+    cfg = QWEN7B_PREFILL_16K.replace(B=2)
     n = 333
-    inp = prefill_inputs(cfg, 3, n=n, salt=9)
+    inp = prefill_inputs(cfg, n=n, salt=9)
     r = np.random.default_rng(4)
     S0 = (r.standard_normal(inp["S0"].shape) * 30).astype(np.float32)
     z0 = (np.abs(r.standard_normal(inp["z0"].shape)) * 100 + 1).astype(np.float32)
@@ -152,9 +152,9 @@ def test_linear_state_update_matches_oracle():
 
 
 def test_prefill_then_decode_continues_the_sequence():
-    cfg = CONFIGS[3].replace(n=401, cap=410)
+    cfg = QWEN7B_PREFILL_16K.replace(n=401, cap=410)
     n, M = 400, 64
-    full = prefill_inputs(cfg, 3, n=n + 1, salt=7)
+    full = prefill_inputs(cfg, n=n + 1, salt=7)
     part = {k: (v[:, :n] if v.ndim >= 3 and v.shape[1] == n + 1 else v) for k, v in full.items()}
     g = gpu_prefill(cfg, part, M=M)
     ref_full = oracle.prefill(full, M)
@@ -181,20 +181,20 @@ def test_prefill_then_decode_continues_the_sequence():
 
 
 @pytest.mark.slow
-def test_prefill_c3_qwen7b_16k_sampled_rows():
-    cfg = CONFIGS[3]
-    inp = prefill_inputs(cfg, 3)
+def test_prefill_qwen7b_16k_sampled_rows():
+    cfg = QWEN7B_PREFILL_16K
+    inp = prefill_inputs(cfg)
     g = gpu_prefill(cfg, inp)
     rows = row_sample(cfg.n, cfg.M, stride=256)
     ref = oracle.prefill_rows(inp, cfg.M, rows)
     got = np.stack([g["out"][0, t] for t in rows])
     exp = np.stack([ref["out"][t] for t in rows])
-    assert_out_close(cfg, got, exp, f"C3 {len(rows)} rows")
+    assert_out_close(cfg, got, exp, f"qwen7b prefill 16K, {len(rows)} rows")
     check_idx_format(g["idx"][0][rows], np.array(rows) + 1, cfg.M)
     rc = recall(g["idx"][0][rows], [ref["idx"][t] for t in rows])
-    print(f"[C3] recall={rc:.6f}")
+    print(f"[qwen7b prefill 16K] recall={rc:.6f}")
     assert rc >= RECALL_MIN
-    assert_state_close(g["S"][0], g["z"][0], ref["S"], ref["z"], "C3 state")
+    assert_state_close(g["S"][0], g["z"][0], ref["S"], ref["z"], "qwen7b prefill 16K state")
 
 
 def test_prefill_graph_replays_match_eager():
@@ -203,8 +203,8 @@ def test_prefill_graph_replays_match_eager():
     graph edges), every replay must reproduce the eager result bit for bit,
     with eager work (state resets) between the replays."""
     n = 700
-    cfg = CONFIGS[3].replace(n=n, cap=n)
-    inp = prefill_inputs(cfg, 3, n=n, salt=77)
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n)
+    inp = prefill_inputs(cfg, n=n, salt=77)
     T = tdtype(cfg)
     sh = shape_of(cfg, cap=n)
     t = {k: dev(inp[k], T) for k in ("q", "k", "v", "k_idx", "q_idx", "q_lin", "k_lin", "v_lin", "x", "w_gate")}

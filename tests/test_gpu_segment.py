@@ -7,7 +7,7 @@ import torch
 
 import long_context_attention_lightning_amd as L
 import oracle
-from lisa_inputs import CONFIGS, prefill_inputs
+from lisa_inputs import QWEN7B_PREFILL_16K, prefill_inputs
 from gpu_helpers import dev, host, shape_of
 
 pytestmark = pytest.mark.gpu
@@ -18,8 +18,8 @@ def test_segment_correction_run_matches_oracle(alpha):
     """Six segments of 64 tokens: each segment's tokens enter the state
     (lisa_linear_state_update), then the segment is corrected; the GPU state,
     start state and mean direction track the oracle's."""
-    cfg = CONFIGS[3].replace(B=2, n=384, cap=384, H_q=4, H_kv=1, H_L=4, d=128, hidden=64)
-    inp = prefill_inputs(cfg, 3, n=384, salt=11)
+    cfg = QWEN7B_PREFILL_16K.replace(B=2, n=384, cap=384, H_q=4, H_kv=1, H_L=4, d=128, hidden=64)
+    inp = prefill_inputs(cfg, n=384, salt=11)
     sh = shape_of(cfg, M=64, cap=384, B=2)
     T = torch.bfloat16
     S = dev(inp["S0"], torch.float32)

@@ -7,7 +7,8 @@ import torch
 
 import long_context_attention_lightning_amd as L
 import oracle
-from lisa_inputs import CONFIGS, decode_inputs, prefill_inputs, row_sample
+from lisa_inputs import (TINY_FP32_PREFILL, QWEN7B_DECODE_16K, QWEN7B_RAGGED_DECODE, QWEN7B_PREFILL_16K,
+                         QWEN14B_DECODE_32K, decode_inputs, prefill_inputs, row_sample)
 from gpu_helpers import dev, gpu_select_rows, host, padded
 
 pytestmark = pytest.mark.gpu
@@ -48,35 +49,35 @@ def test_select_mixed_lengths_one_launch():
     _check(rows, 2048, "mixed")
 
 
-@pytest.mark.parametrize("cid", [1, 2, 4])
-def test_select_on_oracle_decode_scores(cid):
-    cfg = CONFIGS[cid]
-    inp = decode_inputs(cfg, cid)
+@pytest.mark.parametrize("cfg", [QWEN7B_DECODE_16K, QWEN7B_RAGGED_DECODE, QWEN14B_DECODE_32K],
+                         ids=lambda c: c.name)
+def test_select_on_oracle_decode_scores(cfg):
+    inp = decode_inputs(cfg)
     Ms = cfg.M_sweep or (cfg.M,)
     for M in Ms:
         ref = oracle.decode_step(inp, M)
         rows = [s.astype(np.float32) for s in ref["scores"]]
-        _check(rows, M, f"C{cid} M={M}")
+        _check(rows, M, f"{cfg.name} M={M}")
 
 
-def test_select_on_oracle_prefill_scores_c0():
-    cfg = CONFIGS[0]
-    inp = prefill_inputs(cfg, 0)
+def test_select_on_oracle_prefill_scores_tiny_fp32():
+    cfg = TINY_FP32_PREFILL
+    inp = prefill_inputs(cfg)
     res = oracle.prefill_rows(inp, cfg.M, range(cfg.n))
     rows = [res["scores"][t].astype(np.float32) for t in range(cfg.n)]
-    _check(rows, cfg.M, "C0 all rows")
+    _check(rows, cfg.M, "tiny fp32 prefill, all rows")
 
 
 @pytest.mark.slow
-def test_select_on_oracle_prefill_scores_c3_rows():
-    cfg = CONFIGS[3]
-    inp = prefill_inputs(cfg, 3)
+def test_select_on_oracle_prefill_scores_qwen7b_16k_rows():
+    cfg = QWEN7B_PREFILL_16K
+    inp = prefill_inputs(cfg)
     rows_t = row_sample(cfg.n, cfg.M, stride=16)
     rows = []
     for t in rows_t:
         s = oracle.index_scores(inp["q_idx"][0, t], inp["k_idx"][0, : t + 1], inp["w_idx"])
         rows.append(s.astype(np.float32))
-    _check(rows, cfg.M, f"C3 {len(rows)} rows")
+    _check(rows, cfg.M, f"qwen7b prefill 16K, {len(rows)} rows")
 
 
 def test_select_prefill_rows_all_item_bands():

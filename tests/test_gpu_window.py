@@ -7,7 +7,7 @@ import torch
 
 import long_context_attention_lightning_amd as L
 import oracle
-from lisa_inputs import CONFIGS, prefill_inputs, decode_inputs
+from lisa_inputs import TINY_FP32_PREFILL, QWEN7B_DECODE_16K, QWEN7B_PREFILL_16K, prefill_inputs, decode_inputs
 from gpu_helpers import (assert_out_close, assert_state_close, dev, gpu_decode, gpu_prefill, host,
                          saturate_gate, shape_of, tdtype)
 
@@ -34,33 +34,33 @@ def _check_prefill(cfg, inp, M, label):
     assert_out_close(cfg, gs["out"], ref["o_sparse"], f"{label} o_sparse")
 
 
-def test_window_prefill_c0_fp32():
-    cfg = CONFIGS[0]
-    _check_prefill(cfg, prefill_inputs(cfg, 0), cfg.M, "window C0 fp32")
+def test_window_prefill_tiny_fp32():
+    cfg = TINY_FP32_PREFILL
+    _check_prefill(cfg, prefill_inputs(cfg), cfg.M, "window tiny fp32 prefill")
 
 
 @pytest.mark.parametrize("n,M,B", [(700, 128, 2), (333, 64, 1), (129, 200, 1), (300, 1, 1)])
 def test_window_prefill_bf16(n, M, B):
     """MFMA path: the band mask is formed from positions, and key tiles that
     lie before every row's window are skipped."""
-    cfg = CONFIGS[3].replace(B=B, n=n, cap=n + 3)
-    _check_prefill(cfg, prefill_inputs(cfg, 3, n=n, salt=n + 7), M, f"window bf16 n={n} M={M}")
+    cfg = QWEN7B_PREFILL_16K.replace(B=B, n=n, cap=n + 3)
+    _check_prefill(cfg, prefill_inputs(cfg, n=n, salt=n + 7), M, f"window bf16 n={n} M={M}")
 
 
 def test_window_prefill_bf16_g7_long_band():
-    cfg = CONFIGS[3].replace(n=1100, cap=1100)
-    _check_prefill(cfg, prefill_inputs(cfg, 3, n=1100, salt=5), 200, "window bf16 G7 n=1100 M=200")
+    cfg = QWEN7B_PREFILL_16K.replace(n=1100, cap=1100)
+    _check_prefill(cfg, prefill_inputs(cfg, n=1100, salt=5), 200, "window bf16 G7 n=1100 M=200")
 
 
-@pytest.mark.parametrize("cid,M", [(1, 64), (1, 2048), (0, 8)])
-def test_window_decode(cid, M):
-    base = CONFIGS[cid]
-    if cid == 1:
-        cfg = base.replace(B=3, L=0, L_lo=40, L_hi=3000, cap=3072)
+@pytest.mark.parametrize("small,M", [(False, 64), (False, 2048), (True, 8)],
+                         ids=["bf16 qwen7b heads M=64", "bf16 qwen7b heads M=2048", "fp32 small heads M=8"])
+def test_window_decode(small, M):
+    if not small:
+        cfg = QWEN7B_DECODE_16K.replace(B=3, L=0, L_lo=40, L_hi=3000, cap=3072)
     else:  # fp32, small heads
-        cfg = CONFIGS[1].replace(dtype="f32", B=2, L=0, L_lo=5, L_hi=60, cap=64, H_q=2, H_kv=1, H_L=2, d=32,
+        cfg = QWEN7B_DECODE_16K.replace(dtype="f32", B=2, L=0, L_lo=5, L_hi=60, cap=64, H_q=2, H_kv=1, H_L=2, d=32,
                                  H_I=1, H_Ik=1, d_I=16, hidden=64)
-    inp = decode_inputs(cfg, 1, salt=M)
+    inp = decode_inputs(cfg, salt=M)
     T = tdtype(cfg)
     seq = inp["seq_lens"]
     cap = inp["k_cache"].shape[1]
@@ -78,7 +78,7 @@ def test_window_decode(cid, M):
                        t["k_cache"], t["v_cache"], None, S, z, out, idx, ws)
     torch.cuda.synchronize()
     ref = oracle.decode_step(inp, M, window=True)
-    label = f"window decode C{cid} M={M}"
+    label = f"window decode {'fp32 small heads' if small else 'bf16 qwen7b heads'} M={M}"
     for b in range(len(seq)):
         P = ref["idx"][b]
         row = host(idx)[b]
@@ -93,8 +93,8 @@ def test_window_decode(cid, M):
 def test_window_matches_indexed_path_with_tied_scores():
     """All indexer weights zero: every score ties and top-M keeps the most
     recent positions, so the indexed path selects exactly the window."""
-    cfg = CONFIGS[1].replace(B=2, L=0, L_lo=100, L_hi=900, cap=1024)
-    inp = decode_inputs(cfg, 1, salt=3)
+    cfg = QWEN7B_DECODE_16K.replace(B=2, L=0, L_lo=100, L_hi=900, cap=1024)
+    inp = decode_inputs(cfg, salt=3)
     inp["w_idx"] = np.zeros_like(inp["w_idx"])
     for M in (50, 512):
         a = gpu_decode(cfg, inp, M=M, flags=W)
@@ -104,7 +104,7 @@ def test_window_matches_indexed_path_with_tied_scores():
 
 
 def test_window_flag_rejected_by_indexer_topk():
-    cfg = CONFIGS[1]
+    cfg = QWEN7B_DECODE_16K
     sh = shape_of(cfg, max_len=cfg.L, flags=W)
     idx = torch.zeros((1, cfg.M), dtype=torch.int32, device="cuda")
     with pytest.raises(Exception):

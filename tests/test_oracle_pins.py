@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from lisa_inputs import CONFIGS, prefill_inputs, decode_inputs, round_bf16
+from lisa_inputs import TINY_FP32_PREFILL, QWEN7B_DECODE_16K, QWEN7B_RAGGED_DECODE, prefill_inputs, decode_inputs, round_bf16
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -328,8 +328,8 @@ def _layer_brute(inp, M, t):
 
 
 def test_prefill_against_scalar_brute_force():
-    cfg = CONFIGS[0].replace(d=4, d_I=3, hidden=5, H_q=4, H_kv=2, H_L=4, M=3, H_I=2, H_Ik=2)
-    inp = prefill_inputs(cfg, 0, n=9, salt=1)
+    cfg = TINY_FP32_PREFILL.replace(d=4, d_I=3, hidden=5, H_q=4, H_kv=2, H_L=4, M=3, H_I=2, H_Ik=2)
+    inp = prefill_inputs(cfg, n=9, salt=1)
     r = np.random.default_rng(13)
     inp["S0"] = r.standard_normal(inp["S0"].shape).astype(np.float32)
     inp["z0"] = (np.abs(r.standard_normal(inp["z0"].shape)) + 1).astype(np.float32)
@@ -345,8 +345,8 @@ def test_prefill_against_scalar_brute_force():
 
 
 def test_gate_saturation_selects_one_branch():
-    cfg = CONFIGS[0]
-    inp = prefill_inputs(cfg, 0, n=40)
+    cfg = TINY_FP32_PREFILL
+    inp = prefill_inputs(cfg, n=40)
     inp["x"] = np.zeros_like(inp["x"])
     inp["x"][..., 0] = 1.0
     for sign, key in [(1.0, "o_sparse"), (-1.0, "o_linear")]:
@@ -361,9 +361,9 @@ def test_gate_saturation_selects_one_branch():
 
 def test_decode_continues_prefill():
     """prefill(n) followed by one decode step equals the last row of prefill(n+1)."""
-    cfg = CONFIGS[0].replace(H_q=4, H_kv=2, H_L=4, H_I=2, H_Ik=2, M=16)
+    cfg = TINY_FP32_PREFILL.replace(H_q=4, H_kv=2, H_L=4, H_I=2, H_Ik=2, M=16)
     n = 50
-    full = prefill_inputs(cfg, 0, n=n + 1, salt=3)
+    full = prefill_inputs(cfg, n=n + 1, salt=3)
     part = {k: (v[:, :n] if k in ("q", "k", "v", "q_idx", "k_idx", "q_lin", "k_lin", "v_lin", "x") else v)
             for k, v in full.items()}
     ref_full = oracle.prefill(full, cfg.M)
@@ -393,9 +393,9 @@ def test_decode_continues_prefill():
 
 
 def test_decode_full_budget_equals_dense():
-    cfg = CONFIGS[1].replace(B=3, L=0, L_lo=20, L_hi=90, cap=96, H_q=8, H_kv=2, H_L=8, d=16,
+    cfg = QWEN7B_DECODE_16K.replace(B=3, L=0, L_lo=20, L_hi=90, cap=96, H_q=8, H_kv=2, H_L=8, d=16,
                              d_I=8, hidden=32)
-    inp = decode_inputs(cfg, 1)
+    inp = decode_inputs(cfg)
     inp["w_gate"] = np.zeros_like(inp["w_gate"])
     inp["x"] = np.ones_like(inp["x"])
     inp["w_gate"][0, :] = 300.0                   # g = 1: output is the sparse branch
@@ -420,8 +420,8 @@ def test_window_prefill_equals_topm_with_tied_scores(M):
     """With every indexer score equal, top-M keeps the largest positions (the
     tie rule), which is the sliding window: the windowed layer must equal the
     indexed layer with all head weights zero."""
-    cfg = CONFIGS[0].replace(n=129, cap=129, M=M)
-    inp = prefill_inputs(cfg, 0)
+    cfg = TINY_FP32_PREFILL.replace(n=129, cap=129, M=M)
+    inp = prefill_inputs(cfg)
     tied = dict(inp, w_idx=np.zeros_like(inp["w_idx"]))
     a = oracle.prefill(inp, M, window=True)
     b = oracle.prefill(tied, M)
@@ -432,8 +432,8 @@ def test_window_prefill_equals_topm_with_tied_scores(M):
 
 def test_window_prefill_full_window_equals_torch_sdpa_causal():
     """A window at least as long as the sequence is full causal attention."""
-    cfg = CONFIGS[0].replace(n=96, cap=96, M=96)
-    inp = prefill_inputs(cfg, 0)
+    cfg = TINY_FP32_PREFILL.replace(n=96, cap=96, M=96)
+    inp = prefill_inputs(cfg)
     inp["w_gate"] = np.zeros_like(inp["w_gate"])
     inp["x"] = np.ones_like(inp["x"])
     inp["w_gate"][0, :] = 300.0                   # g = 1: the sparse branch alone
@@ -447,9 +447,9 @@ def test_window_prefill_full_window_equals_torch_sdpa_causal():
 
 
 def test_window_decode_equals_tied_topm_and_dense_when_wide():
-    cfg = CONFIGS[1].replace(B=3, L=0, L_lo=20, L_hi=90, cap=96, H_q=8, H_kv=2, H_L=8, d=16,
+    cfg = QWEN7B_DECODE_16K.replace(B=3, L=0, L_lo=20, L_hi=90, cap=96, H_q=8, H_kv=2, H_L=8, d=16,
                              d_I=8, hidden=32)
-    inp = decode_inputs(cfg, 1)
+    inp = decode_inputs(cfg)
     tied = dict(inp, w_idx=np.zeros_like(inp["w_idx"]))
     for M in (1, 16, 50):
         a = oracle.decode_step(inp, M, window=True)
@@ -525,9 +525,9 @@ def test_round_bf16_matches_torch():
 
 
 def test_generator_is_seeded_and_shaped():
-    cfg = CONFIGS[2].replace(B=4, cap=64, L_lo=5, L_hi=60)
-    a = decode_inputs(cfg, 2)
-    b = decode_inputs(cfg, 2)
+    cfg = QWEN7B_RAGGED_DECODE.replace(B=4, cap=64, L_lo=5, L_hi=60)
+    a = decode_inputs(cfg)
+    b = decode_inputs(cfg)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
     assert a["k_cache"].shape == (4, 64, 4, 128)
