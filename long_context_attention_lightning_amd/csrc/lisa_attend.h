@@ -216,16 +216,16 @@ __device__ __forceinline__ void attend_split(const AttnArgs& a, int r, int g, in
 }
 
 // ---------------------------------------------------------------------------
-// The same split on bf16 MFMA.  Waves 0 and 1 take 32 entries each of every
-// 64-entry chunk of the split: S^T = K Q^T (gathered K rows as the A operand,
-// the G query heads of the KV group as the 16 columns, rows past G zero),
-// online softmax per head along the accumulator rows, then O = P V with P
-// taken from the accumulators (contraction order permuted alike in P and in
-// V) and V transposed through LDS as packed position pairs.  The other waves
-// only join the block's barriers.
+// The same split on bf16 MFMA.  The block's first NWA waves take 32 entries
+// each of every (32 NWA)-entry chunk of the split: S^T = K Q^T (gathered K
+// rows as the A operand, the G query heads of the KV group as the 16 columns,
+// rows past G zero), online softmax per head along the accumulator rows, then
+// O = P V with P taken from the accumulators (contraction order permuted
+// alike in P and in V) and V transposed through LDS as packed position pairs.
+// Each attending wave keeps its own online-softmax state and the epilogue
+// merges them; waves past NWA (the fused select kernel has eight waves, two
+// of which attend) only join the block's barriers.
 // ---------------------------------------------------------------------------
-// NWA waves of the block gather and attend, 32 selected entries each per
-// round, with their own online-softmax state; the epilogue merges them.
 template <int D, int GT, int NWA>
 struct AttnMfmaShared {
   union {  // the merge state is written once no wave reads its V tile any more
