@@ -189,3 +189,37 @@ def test_decode_graph_replays_match_eager(M):
     assert recall(host(e["idx"]), ref["idx"]) >= RECALL_MIN
     assert_out_close(cfg, host(e["out"]), ref["out"], f"eager decode M={M}")
     assert_state_close(host(e["S"]), host(e["z"]), ref["S"], ref["z"], f"eager decode M={M}")
+
+
+@pytest.mark.parametrize("M", [512, 2048, 6000], ids=["fused select", "separate select", "every position"])
+def test_decode_without_index_list_matches(M):
+    """idx_out is optional: without it the step must produce the same output,
+    state and caches bit for bit (the fused kernel then keeps the selection in
+    LDS, the separate select writes it to the workspace, and the path without
+    scoring writes none)."""
+    cfg = QWEN7B_RAGGED_DECODE.replace(B=8, L_lo=1000, L_hi=5000, cap=5000)
+    inp = decode_inputs(cfg, salt=79)
+    seq = inp["seq_lens"]
+    T = tdtype(cfg)
+    sh = shape_of(cfg, M=M, max_len=int(seq.max()), cap=cfg.cap, B=cfg.B)
+    t = {k: dev(inp[k], T) for k in ("q", "k_new", "v_new", "q_idx", "k_idx_new", "q_lin", "k_lin", "v_lin",
+                                     "x", "w_gate")}
+    w_idx = dev(inp["w_idx"], torch.float32)
+    seq_t = torch.from_numpy(seq.astype(np.int32)).cuda()
+    caches = [dev(inp[k], T) for k in ("k_cache", "v_cache", "k_idx_cache")]
+    ws = L.workspace(sh, L.LISA_OP_DECODE)
+    res = []
+    for with_idx in (True, False):
+        S, z = dev(inp["S0"], torch.float32), dev(inp["z0"], torch.float32)
+        kc = [c.clone() for c in caches]
+        out = torch.empty((cfg.B, cfg.H_q, cfg.d), dtype=T, device="cuda")
+        idx = torch.full((cfg.B, M), -7, dtype=torch.int32, device="cuda") if with_idx else None
+        L.lisa_decode_step(sh, seq_t, t["q"], t["k_new"], t["v_new"], t["q_idx"], t["k_idx_new"], t["q_lin"],
+                           t["k_lin"], t["v_lin"], t["x"], t["w_gate"], w_idx, *kc, S, z, out, idx, ws)
+        torch.cuda.synchronize()
+        res.append((out, S, z, kc))
+    (o1, S1, z1, k1), (o2, S2, z2, k2) = res
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(z1, z2)
+    for a, b in zip(k1, k2):
+        assert torch.equal(a, b)
+    assert_out_close(cfg, host(o2), oracle.decode_step(inp, M)["out"], f"no index list M={M}")
