@@ -349,10 +349,11 @@ __global__ __launch_bounds__(AT_THREADS) void k_attention(AttnArgs a) {
 // Merge the split partials of one (row, query head) and apply the epilogue.
 // Lane sp of every wave loads split sp's max and sum (vector loads; the
 // values are block-uniform and would otherwise become serialized scalar
-// loads); every thread loads its dimension of all split accumulators at once.
-template <typename T>
+// loads); every thread loads its dimension of all split accumulators at once,
+// NS of them, the launch's split count rounded up to 8, 16 or 32.
+template <typename T, int NS>
 __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
-  static_assert(AT_MAX_SPLITS <= WAVE, "one lane per split");
+  static_assert(NS <= AT_MAX_SPLITS && AT_MAX_SPLITS <= WAVE, "one lane per split");
   const Shape& sh = a.sh;
   const int D = sh.d;
   const int G = sh.H_q / sh.H_kv;
@@ -369,9 +370,9 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
   // gate partials and the linear output.
   const int len = a.prefill ? t + 1 : a.seq_lens[b];
   const float* p0 = a.part + ((size_t)r * sh.H_kv + g) * a.nsplit * PS;
-  float ov[AT_MAX_SPLITS];
+  float ov[NS];
 #pragma unroll
-  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) ov[sp] = p0[(size_t)min(sp, a.nsplit - 1) * PS + hh * D + dim];
+  for (int sp = 0; sp < NS; ++sp) ov[sp] = p0[(size_t)min(sp, a.nsplit - 1) * PS + hh * D + dim];
   const int ls = min(lane, a.nsplit - 1);
   const float m_raw = p0[(size_t)ls * PS + GD + hh];
   const float l_raw = p0[(size_t)ls * PS + GD + G + hh];
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
   const float l = group_sum(live ? l_raw * f_l : 0.f, WAVE);
   float o = 0.f;
 #pragma unroll
-  for (int sp = 0; sp < AT_MAX_SPLITS; ++sp) {
+  for (int sp = 0; sp < NS; ++sp) {
     const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_l), sp));
     o = fmaf(sp < nvalid ? ov[sp] : 0.f, f, o);  // stale partials past the row never enter
   }
@@ -434,7 +435,9 @@ template <typename T>
 static hipError_t launch_combine_t(const AttnArgs& a, hipStream_t st) {
   if (a.nsplit == 1) return hipSuccess;
   const dim3 grid((unsigned)((size_t)a.n_rows * a.sh.H_q));
-  klaunch((k_attn_combine<T>), grid, dim3(128), 0, st, a);
+  if (a.nsplit <= 8) klaunch((k_attn_combine<T, 8>), grid, dim3(128), 0, st, a);
+  else if (a.nsplit <= 16) klaunch((k_attn_combine<T, 16>), grid, dim3(128), 0, st, a);
+  else klaunch((k_attn_combine<T, AT_MAX_SPLITS>), grid, dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
