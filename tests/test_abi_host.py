@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(L.EXPORTED_SYMBOLS)
 
 
-def _c1(**kw):
+def _qwen7b_decode_shape(**kw):
     base = dict(B=1, H_q=28, H_kv=4, d=128, H_I=4, H_Ik=4, d_I=64, hidden=3584, M=2048,
                 cap=16384, max_len=16384)
     base.update(kw)
@@ -46,12 +46,12 @@ def _c1(**kw):
 
 
 def test_workspace_sizes(lib):
-    sh = _c1()
+    sh = _qwen7b_decode_shape()
     dec = L.lisa_workspace_bytes(sh, L.LISA_OP_DECODE)
     assert dec > 16384 * 4          # holds at least one score row
     pre = L.lisa_workspace_bytes(sh, L.LISA_OP_PREFILL, 16384)
     assert pre > (16384 - 2048) * 16384 * 4
-    assert L.lisa_workspace_bytes(_c1(B=32), L.LISA_OP_DECODE) > 30 * dec // 2
+    assert L.lisa_workspace_bytes(_qwen7b_decode_shape(B=32), L.LISA_OP_DECODE) > 30 * dec // 2
     assert L.lisa_workspace_bytes(sh, L.LISA_OP_DENSE_DECODE) > 0
     assert L.lisa_workspace_bytes(sh, L.LISA_OP_TOPK_PREFILL, 4096) > 0
     assert L.lisa_workspace_bytes(sh, 99) == 0
@@ -62,13 +62,16 @@ def test_workspace_sizes(lib):
     (dict(H_kv=5), L.LisaError),
     (dict(H_L=27), L.LisaError),
     (dict(M=0), L.LisaError),
+    (dict(B=0), L.LisaError),
+    (dict(hidden=0), L.LisaError),
+    (dict(chunk=32), L.LisaError),
     (dict(d=96), L.LisaError),
     (dict(max_len=20000), L.LisaError),
     (dict(H_Ik=3), L.LisaError),
     (dict(dtype=7), L.LisaError),
 ])
 def test_bad_shapes_are_rejected(lib, kw, code):
-    sh = _c1(**{k: v for k, v in kw.items() if k != "dtype"})
+    sh = _qwen7b_decode_shape(**{k: v for k, v in kw.items() if k != "dtype"})
     if "dtype" in kw:
         sh.dtype = kw["dtype"]
     assert L.lisa_workspace_bytes(sh, L.LISA_OP_DECODE) == 0
@@ -77,7 +80,7 @@ def test_bad_shapes_are_rejected(lib, kw, code):
 
 def test_unsupported_vs_invalid_codes(lib):
     f = lib.lisa_workspace_bytes
-    sh = _c1(d=96)
+    sh = _qwen7b_decode_shape(d=96)
     assert f(ctypes.byref(sh), 0, 0) == 0
     assert "head dim" in L.lisa_last_error()
     assert L.lisa_status_string(-2) == "unsupported configuration"
@@ -96,18 +99,18 @@ def _call_decode(sh, ptr=16, ws_bytes=1 << 40, **over):
 
 
 def test_decode_rejects_null_misaligned_and_small_workspace(lib):
-    sh = _c1()
+    sh = _qwen7b_decode_shape()
     assert _call_decode(sh, q=None) == -1
     assert "q is NULL" in L.lisa_last_error()
     assert _call_decode(sh, k_cache=24) == -1
     assert "aligned" in L.lisa_last_error()
     assert _call_decode(sh, ws_bytes=100) == -3
-    assert _call_decode(_c1(H_q=27, H_kv=4)) == -1
-    assert _call_decode(_c1(H_q=72, H_kv=8)) == -2
+    assert _call_decode(_qwen7b_decode_shape(H_q=27, H_kv=4)) == -1
+    assert _call_decode(_qwen7b_decode_shape(H_q=72, H_kv=8)) == -2
 
 
 def test_prefill_and_topk_reject_bad_lengths(lib):
-    sh = _c1()
+    sh = _qwen7b_decode_shape()
     p = 16
     rc = lib.lisa_prefill(ctypes.byref(sh), 0, *([p] * 16), 1 << 40, None)
     assert rc == -1 and "n 0" in L.lisa_last_error()
@@ -129,7 +132,7 @@ def test_kernel_names(lib):
 
 
 def test_segment_correct_rejects_bad_args(lib):
-    sh = _c1()
+    sh = _qwen7b_decode_shape()
     buf = (ctypes.c_float * 64)()
     p = ctypes.cast(buf, ctypes.c_void_p)
     rc = lib.lisa_segment_correct(ctypes.byref(sh), p, p, p, p, p, p, 0, 0.5, None)
@@ -141,7 +144,7 @@ def test_segment_correct_rejects_bad_args(lib):
 
 
 def test_attention_mass_workspace_and_rejections(lib):
-    sh = _c1()
+    sh = _qwen7b_decode_shape()
     ws = L.lisa_workspace_bytes(sh, L.LISA_OP_MASS, 3)
     assert ws >= 3 * 28 * 16384 * 4 + 3 * 28 * 2048 * 4  # logits and the bound's index sets
     assert L.lisa_workspace_bytes(sh, L.LISA_OP_MASS, 0) == 0
@@ -155,7 +158,7 @@ def test_attention_mass_workspace_and_rejections(lib):
     assert rc == -3
     assert lib.lisa_attention_mass(ctypes.byref(sh), 0, None, None, None, None, None, None, None, None, 0,
                                    None) == 0  # no rows: nothing to do
-    bad = _c1(max_len=0)
+    bad = _qwen7b_decode_shape(max_len=0)
     rc = lib.lisa_attention_mass(ctypes.byref(bad), 3, None, p, p, p, p, p, None, p, 1 << 40, None)
     assert rc == -1 and "max_len" in L.lisa_last_error()
 
@@ -163,15 +166,15 @@ def test_attention_mass_workspace_and_rejections(lib):
 def test_indexer_kl_rejections(lib):
     buf = (ctypes.c_float * 64)()
     p = ctypes.cast(buf, ctypes.c_void_p)
-    sh = _c1(H_I=8, H_Ik=8)  # 28 teacher heads do not split over 8 indexer heads
+    sh = _qwen7b_decode_shape(H_I=8, H_Ik=8)  # 28 teacher heads do not split over 8 indexer heads
     rc = lib.lisa_indexer_kl(ctypes.byref(sh), 64, p, p, p, p, p, None, None)
     assert rc == -2 and "H_I" in L.lisa_last_error()
-    sh = _c1()
+    sh = _qwen7b_decode_shape()
     rc = lib.lisa_indexer_kl(ctypes.byref(sh), 64, p, p, p, p, None, None, None)
     assert rc == -1 and "kl_out" in L.lisa_last_error()
     rc = lib.lisa_indexer_kl(ctypes.byref(sh), 0, p, p, p, p, p, None, None)
     assert rc == -1
-    win = _c1(flags=L.LISA_SLIDING_WINDOW)
+    win = _qwen7b_decode_shape(flags=L.LISA_SLIDING_WINDOW)
     rc = lib.lisa_indexer_kl(ctypes.byref(win), 64, p, p, p, p, p, None, None)
     assert rc == -1 and "sliding-window" in L.lisa_last_error()
 
@@ -179,7 +182,7 @@ def test_indexer_kl_rejections(lib):
 def test_candidate_dropout_rejections(lib):
     buf = (ctypes.c_float * 64)()
     p = ctypes.cast(buf, ctypes.c_void_p)
-    sh = _c1()
+    sh = _qwen7b_decode_shape()
     ws = L.lisa_workspace_bytes(sh, L.LISA_OP_DROPOUT_DECODE)
     assert ws >= 16384 * 4 + 2048 * 4
     assert L.lisa_workspace_bytes(sh, L.LISA_OP_DROPOUT_PREFILL, 4096) > 4096 * 4096 * 4
