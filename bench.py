@@ -410,11 +410,11 @@ def main():
                                       kernel_us=dw["kernel_us"], step_hbm_roofline_frac=dw["step_hbm_roofline_frac"])
         torch.cuda.empty_cache()
     if not args.no_sweep:
-        c4 = QWEN14B_DECODE_32K
+        q14 = QWEN14B_DECODE_32K
         sweep = {}
-        for Mv in c4.M_sweep:
-            cm = c4.replace(M=Mv)
-            dm = bench_decode(args, torch, Lb, cm, 2, 32, 4, Mv == c4.M_sweep[0] and not args.no_dense,
+        for Mv in q14.M_sweep:
+            cm = q14.replace(M=Mv)
+            dm = bench_decode(args, torch, Lb, cm, 2, 32, 4, Mv == q14.M_sweep[0] and not args.no_dense,
                               f"sweep{Mv}:")
             dm.pop("inp")
             mms = dm.pop("ms_step")
@@ -423,11 +423,11 @@ def main():
                     "step_hbm_roofline_frac", "dense_decode_us_per_step", "speedup_vs_dense_decode")
             sweep[str(Mv)] = dict(tok_s=round(cm.B / (mms * 1e-3), 1), **{k: v for k, v in dm.items() if k in keep})
             torch.cuda.empty_cache()
-        dense_us = sweep[str(c4.M_sweep[0])].get("dense_decode_us_per_step")
+        dense_us = sweep[str(q14.M_sweep[0])].get("dense_decode_us_per_step")
         if dense_us:
             for v in sweep.values():
                 v["speedup_vs_dense_decode"] = round(dense_us / v["us_per_step"], 3)
-        extra["m_sweep_decode"] = dict(workload=c4.name, batch=c4.B, context=c4.L, dense_decode_us_per_step=dense_us,
+        extra["m_sweep_decode"] = dict(workload=q14.name, batch=q14.B, context=q14.L, dense_decode_us_per_step=dense_us,
                                        **sweep)
 
     if not args.no_kl:
@@ -846,25 +846,25 @@ def cpu_per_config(args):
             if time.perf_counter() - t0 > budget:
                 return n, time.perf_counter() - t0
 
-    c2 = QWEN7B_RAGGED_DECODE.replace(B=4)
-    inp2 = decode_inputs(c2)
-    n, dt = loop(lambda: oracle.decode_step(inp2, c2.M))
-    out[c2.name] = {"value": round(n * c2.B / dt, 3), "unit": "tok/s",
-                    "sample": f"{n} steps of 4 sequences, lengths {inp2['seq_lens'].tolist()}, {dt:.1f} s"}
-    del inp2
+    ragged = QWEN7B_RAGGED_DECODE.replace(B=4)
+    inp_ragged = decode_inputs(ragged)
+    n, dt = loop(lambda: oracle.decode_step(inp_ragged, ragged.M))
+    out[ragged.name] = {"value": round(n * ragged.B / dt, 3), "unit": "tok/s",
+                        "sample": f"{n} steps of 4 sequences, lengths {inp_ragged['seq_lens'].tolist()}, {dt:.1f} s"}
+    del inp_ragged
     if args.cpu_all:  # about half a minute: the oracle's prefill builds the whole sequence's linear state
-        c3 = QWEN7B_PREFILL_16K
-        inp3 = prefill_inputs(c3)
+        pre = QWEN7B_PREFILL_16K
+        inp_pre = prefill_inputs(pre)
         rows = [8191]
-        n, dt = loop(lambda: oracle.prefill_rows(inp3, c3.M, rows))
-        out[c3.name] = {"value": round(n * len(rows) / dt, 4), "unit": "rows/s",
-                        "sample": f"{n} call(s) of the output of prefill row {rows[0]}, which includes the linear "
-                                  f"state over the whole 16384-token sequence, {dt:.1f} s"}
-        del inp3
-    c4 = QWEN14B_DECODE_32K.replace(B=1)
-    inp4 = decode_inputs(c4)
-    n, dt = loop(lambda: oracle.decode_step(inp4, 2048))
-    out[c4.name] = {"value": round(n / dt, 3), "unit": "tok/s",
+        n, dt = loop(lambda: oracle.prefill_rows(inp_pre, pre.M, rows))
+        out[pre.name] = {"value": round(n * len(rows) / dt, 4), "unit": "rows/s",
+                         "sample": f"{n} call(s) of the output of prefill row {rows[0]}, which includes the linear "
+                                   f"state over the whole 16384-token sequence, {dt:.1f} s"}
+        del inp_pre
+    q14 = QWEN14B_DECODE_32K.replace(B=1)
+    inp_q14 = decode_inputs(q14)
+    n, dt = loop(lambda: oracle.decode_step(inp_q14, 2048))
+    out[q14.name] = {"value": round(n / dt, 3), "unit": "tok/s",
                     "sample": f"{n} steps of one 32768-token sequence, M = 2048, {dt:.1f} s"}
     return out
 
