@@ -18,75 +18,55 @@ __device__ __forceinline__ int dropout_row_len(const DropoutArgs& a, int r) {
   return a.prefill ? r % a.rows_per_seq + 1 : a.seq_lens[r];
 }
 
-// One block per row; thread k takes a contiguous run of mask words (at most
-// DR_MAXW), so the survivors come out in position order after one block scan
-// of the counts.  A word's 32 uniforms and, if any candidate survives, its
-// 32 scores are read as independent 16-byte vectors, and the survivor bits
-// stay in registers between the counting and the writing pass.
-constexpr int DR_MAXW = 8;  // 2048 words of the longest row (65536) over 256 threads
-
-// 32 floats of a row from position 32 w, the part at or past ld read as 0
-__device__ __forceinline__ void load_word(const float* row, int64_t ld, int w, float (&v)[32]) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int64_t p = 32 * (int64_t)w + 4 * k;
-    const float4 x = p < ld ? *reinterpret_cast<const float4*>(row + p) : make_float4(0.f, 0.f, 0.f, 0.f);
-    v[4 * k] = x.x; v[4 * k + 1] = x.y; v[4 * k + 2] = x.z; v[4 * k + 3] = x.w;
-  }
-}
-
+// One block per row, in rounds of 1024 positions: thread t takes positions
+// 1024 i + 4 t .. + 3, so every wave reads 256 consecutive uniforms and
+// scores (two 16-byte vectors per lane, issued with the mask word before any
+// of them is used).  A block scan of the survivor counts of the round, added
+// to the survivors of the earlier rounds, gives each thread its output
+// offset, so the survivors come out in position order and each wave's writes
+// fill one consecutive range.  One barrier per round: the scan's wave totals
+// alternate between two slots.
 __global__ __launch_bounds__(256) void k_dropout_compact(DropoutArgs a) {
-  __shared__ uint32_t wsum[4];
+  __shared__ uint32_t wsum[2][4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   const int len = dropout_row_len(a, r);
-  const int words = (len + 31) / 32;
-  const int per = (words + 255) / 256, w0 = min(tid * per, words), w1 = min(w0 + per, words);
   const uint32_t* mrow = a.mask + (size_t)r * a.mask_ld;
   const float* urow = a.u + (size_t)r * a.ld;
-  uint32_t keep[DR_MAXW];
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int i = 0; i < DR_MAXW; ++i) {
-    keep[i] = 0u;
-    const int w = w0 + i;
-    if (w >= w1) continue;
-    uint32_t m = mrow[w];
-    if (32 * w + 32 > len) m &= (1u << (len - 32 * w)) - 1u;  // len - 32 w < 32 here
-    if (!m) continue;
-    float u[32];
-    load_word(urow, a.ld, w, u);
-#pragma unroll
-    for (int b = 0; b < 32; ++b) keep[i] |= (((m >> b) & 1u) && u[b] >= a.p) ? (1u << b) : 0u;
-    cnt += (uint32_t)__builtin_popcount(keep[i]);
-  }
-  const uint32_t incl = wave_incl_scan_u32(cnt);
-  if (lane == WAVE - 1) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t o = incl - cnt, total = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) o += wsum[w];
-    total += wsum[w];
-  }
   const float* srow = a.scores + (size_t)r * a.ld;
   float* cs = a.cscore + (size_t)r * a.cld;
   int32_t* cp = a.cpos + (size_t)r * a.cld;
-#pragma unroll
-  for (int i = 0; i < DR_MAXW; ++i) {
-    if (!keep[i]) continue;
-    const int w = w0 + i;
-    float sv[32];
-    load_word(srow, a.ld, w, sv);
-#pragma unroll
-    for (int b = 0; b < 32; ++b) {
-      if ((keep[i] >> b) & 1u) {
-        cs[o] = sv[b];
-        cp[o] = 32 * w + b;
-        ++o;
-      }
+  uint32_t base = 0;  // survivors of the earlier rounds
+  const int rounds = (len + 1023) / 1024;
+  for (int i = 0; i < rounds; ++i) {
+    const int p = 1024 * i + 4 * tid;  // 4-aligned; p < len implies p + 3 < ld
+    uint32_t m4 = 0;
+    float4 u = make_float4(0.f, 0.f, 0.f, 0.f), sc = u;
+    if (p < len) {
+      m4 = (mrow[p >> 5] >> (p & 31)) & 0xfu;
+      u = *reinterpret_cast<const float4*>(urow + p);
+      sc = *reinterpret_cast<const float4*>(srow + p);
+      if (len - p < 4) m4 &= (1u << (len - p)) - 1u;  // positions past the row
     }
+    const uint32_t keep = ((m4 & 1u) && u.x >= a.p ? 1u : 0u) | ((m4 & 2u) && u.y >= a.p ? 2u : 0u) |
+                          ((m4 & 4u) && u.z >= a.p ? 4u : 0u) | ((m4 & 8u) && u.w >= a.p ? 8u : 0u);
+    const uint32_t c = (uint32_t)__builtin_popcount(keep);
+    const uint32_t incl = wave_incl_scan_u32(c);
+    if (lane == WAVE - 1) wsum[i & 1][wave] = incl;
+    __syncthreads();
+    uint32_t o = base + incl - c, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t t = wsum[i & 1][w];
+      if (w < wave) o += t;
+      tot += t;
+    }
+    base += tot;
+    if (keep & 1u) { cs[o] = sc.x; cp[o] = p; ++o; }
+    if (keep & 2u) { cs[o] = sc.y; cp[o] = p + 1; ++o; }
+    if (keep & 4u) { cs[o] = sc.z; cp[o] = p + 2; ++o; }
+    if (keep & 8u) { cs[o] = sc.w; cp[o] = p + 3; }
   }
-  if (tid == 0) a.cnt[r] = (int32_t)total;
+  if (tid == 0) a.cnt[r] = (int32_t)base;
 }
 
 __global__ __launch_bounds__(256) void k_dropout_gather(DropoutArgs a) {
