@@ -351,7 +351,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer runs on a single "
-              "MI355X and this build has no multi-GPU path.", file=sys.stderr)
+              "MI355X and the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -785,7 +785,7 @@ def dense_prefill_baseline(torch, q, k, v, cfg, n, iters):
             torch.cuda.synchronize()
         return {"ms": round(t0.elapsed_time(t1) / iters, 3), "what": "torch SDPA (flash/efficient backend), causal, "
                 "K/V repeated to the query heads, attention only (no indexer, select, linear branch or gate)"}
-    except Exception as e:  # no fused backend on this build: not reported
+    except Exception as e:  # no fused backend in this torch: not reported
         return {"ms": None, "error": str(e)[:200]}
 
 
