@@ -11,7 +11,8 @@
 // selection is exact and deterministic, so all blocks of a row agree.  Each
 // block keeps the positions of its own split of the ascending selection in
 // LDS and gathers them right away; the blocks of a row read the same score
-// row concurrently from the shared caches.
+// row concurrently from the shared caches.  Each block writes its own slice of
+// the index list (KV head 0), so no block writes the whole list.
 #include <type_traits>
 
 #include "lisa_attend.h"
@@ -27,13 +28,15 @@ constexpr int FS_MAX_SPLIT = 64;  // positions per split
 template <typename T, int D, int GT, int ITEMS>
 __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, SelectArgs sa) {
   constexpr int NW = FS_THREADS / WAVE;
+  constexpr bool MF = sizeof(T) == 2;  // bf16: MFMA split attention
+  // splits of at most FS_MAX_SPLIT entries: two attending waves of 32
+  using AttT = typename std::conditional<MF, AttnMfmaShared<D, GT, FS_MAX_SPLIT / 32>, AttnMergeShared<NW, GT, D>>::type;
   struct SelPart {
     SelShared<NW> sm;
     KeyStore<FS_THREADS, ITEMS, true> ks;
   };
-  constexpr bool MF = sizeof(T) == 2;  // bf16: MFMA split attention
-  // splits of at most FS_MAX_SPLIT entries: two attending waves of 32
-  using AttT = typename std::conditional<MF, AttnMfmaShared<D, GT, FS_MAX_SPLIT / 32>, AttnMergeShared<NW, GT, D>>::type;
+  // the key store takes more than half of a CU's 160 KB for rows of 16K or
+  // more, so the few blocks of a launch spread one per CU
   union Shared {
     SelPart sel;
     AttT att;  // used only after the selection is complete
@@ -48,14 +51,14 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, Select
   const int g = blk % sh.H_kv;
   const int b = blk / sh.H_kv;  // decode: one row per sequence
   // the score row is read up to max_len while the sequence length loads
+  const float* srow = sa.scores + (size_t)b * sa.ld;
   RunLoad<ITEMS> ld;
-  run_load<FS_THREADS, ITEMS>(sa.scores + (size_t)b * sa.ld, sa.max_len, ld);
+  run_load<FS_THREADS, ITEMS>(srow, sa.max_len, ld);
   const int len = a.seq_lens[b];
   const int M = sh.M;
   const int m = min(M, len);
   const int i0 = s * a.split_len;
-  const bool want_idx = sa.idx && g == 0 && s == 0;
-  if (i0 >= m && !want_idx) return;  // empty split: the combine skips it
+  if (i0 >= m) return;  // empty split: the combine skips it (the split-0 block pads the index list)
   const int i1 = min(m, i0 + a.split_len);
 
   // thread-contiguous runs: their compaction is one scan, which is what a
@@ -63,24 +66,21 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, Select
   uint64_t selbits;
   uint32_t o;
   int p0;
-  select_row_runs<FS_THREADS, ITEMS, true>(sa.scores + (size_t)b * sa.ld, len, M, u.sel.sm, u.sel.ks, ld, selbits, o,
-                                           p0);
+  select_row_runs<FS_THREADS, ITEMS, true>(srow, len, M, u.sel.sm, u.sel.ks, ld, selbits, o, p0);
 
-  if (want_idx) {  // the index list, written once per sequence
-    int32_t* orow = sa.idx + (size_t)b * sa.idx_ld;
-    uint32_t oo = o;
-    for (uint64_t mm = selbits; mm; mm &= mm - 1) {
-      if (oo < (uint32_t)M) orow[oo] = p0 + __builtin_ctzll(mm);
-      ++oo;
-    }
-    for (int k = m + (int)threadIdx.x; k < M; k += FS_THREADS) orow[k] = -1;
-    if (i0 >= m) return;
-  }
+  // this split's positions, and its slice of the index list (KV head 0)
+  int32_t* orow = (sa.idx && g == 0) ? sa.idx + (size_t)b * sa.idx_ld : nullptr;
   for (uint64_t mm = selbits; mm; mm &= mm - 1) {
     const int rank = (int)o++;
     if (rank >= i1) break;
-    if (rank >= i0) plist[rank - i0] = p0 + __builtin_ctzll(mm);
+    if (rank >= i0) {
+      const int pos = p0 + __builtin_ctzll(mm);
+      plist[rank - i0] = pos;
+      if (orow) orow[rank] = pos;
+    }
   }
+  if (orow && s == 0)
+    for (int k = m + (int)threadIdx.x; k < M; k += FS_THREADS) orow[k] = -1;
   __syncthreads();
   auto pos_of = [&](int i) { return plist[i - i0]; };
   if constexpr (MF) attend_split_mfma<D, GT, FS_THREADS, FS_MAX_SPLIT / 32>(a, b, g, s, len, i0, i1, pos_of, u.att);
@@ -113,6 +113,43 @@ static hipError_t launch_fs_t(const AttnArgs& a, const SelectArgs& sa, hipStream
     case 128: return launch_fs_td<T, 128>(a, sa, grid, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Selection alone with the same core as k_select_attend, one block per
+// decode row, writing the whole index list.
+template <int ITEMS>
+__global__ __launch_bounds__(FS_THREADS) void k_select_runs(SelectArgs sa) {
+  struct Shared {
+    SelShared<FS_THREADS / WAVE> sm;
+    KeyStore<FS_THREADS, ITEMS, true> ks;
+  };
+  __shared__ Shared u;
+  const int b = blockIdx.x;
+  const float* srow = sa.scores + (size_t)b * sa.ld;
+  RunLoad<ITEMS> ld;
+  run_load<FS_THREADS, ITEMS>(srow, sa.max_len, ld);
+  const int len = sa.seq_lens[b];
+  const int M = sa.M;
+  uint64_t selbits;
+  uint32_t o;
+  int p0;
+  select_row_runs<FS_THREADS, ITEMS, true>(srow, len, M, u.sm, u.ks, ld, selbits, o, p0);
+  int32_t* orow = sa.idx + (size_t)b * sa.idx_ld;
+  for (uint64_t mm = selbits; mm; mm &= mm - 1) {
+    if (o < (uint32_t)M) orow[o] = p0 + __builtin_ctzll(mm);
+    ++o;
+  }
+  for (int k = min(M, len) + (int)threadIdx.x; k < M; k += FS_THREADS) orow[k] = -1;
+}
+
+hipError_t launch_select_runs(const SelectArgs& sa, hipStream_t st) {
+  if (sa.n_rows <= 0) return hipSuccess;
+  if (sa.prefill || !sa.idx) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)sa.n_rows);
+  if (sa.max_len <= FS_THREADS * 32) klaunch(k_select_runs<32>, grid, dim3(FS_THREADS), 0, st, sa);
+  else if (sa.max_len <= FS_THREADS * 64) klaunch(k_select_runs<64>, grid, dim3(FS_THREADS), 0, st, sa);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 bool select_attend_supported(const Shape& sh, int nsplit, int split_len) {

@@ -126,6 +126,15 @@ struct DecodeWs {
   int nsplit, split_len;
 };
 
+// A decode step of few sequences selects inside its attention launch (every
+// attention block selects the whole row, then attends to its split); larger
+// batches run a separate select launch.  lisa_indexer_topk routes decode rows
+// the same way, so it selects with the core the decode step of that shape
+// uses.
+bool decode_fused(const Shape& sh, int nsplit, int split_len) {
+  return select_attend_supported(sh, nsplit, split_len);
+}
+
 DecodeWs decode_ws(const Shape& sh) {
   DecodeWs w;
   Layout L;
@@ -430,8 +439,8 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
     if (window) { pa.q_idx = nullptr; pa.k_idx_new = nullptr; pa.k_idx_cache = nullptr; pa.w_idx = nullptr; }
     pa.do_scores = 0; pa.window_idx = idx_out; pa.M = sh.M;
   }
-  LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
   if (window || take_all) {
+    LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
     AttnArgs aa{};
     aa.sh = sh; aa.n_rows = sh.B; aa.rows_per_seq = 1; aa.prefill = 0; aa.dense = 0; aa.window = 1;
     aa.seq_lens = seq_lens; aa.q = q; aa.k_cache = k_cache; aa.v_cache = v_cache; aa.idx = nullptr; aa.idx_ld = 0;
@@ -443,7 +452,8 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
     return LISA_OK;
   }
 
-  const bool fused = select_attend_supported(sh, w.nsplit, w.split_len);
+  LAUNCH(KID_DECODE_PHASE_A, st, launch_decode_phase_a(pa, st));
+  const bool fused = decode_fused(sh, w.nsplit, w.split_len);
   int32_t* idx = idx_out ? idx_out : (fused ? nullptr : at<int32_t>(ws, w.idx));
   SelectArgs sa{};
   sa.n_rows = sh.B; sa.rows_per_seq = 1; sa.prefill = 0; sa.seq_lens = seq_lens;
@@ -555,6 +565,15 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n, const i
       LAUNCH(KID_PREFILL_INDEX, st, index_mfma_supported(sh) ? launch_index_scores_mfma(ia, st)
                                                              : launch_index_scores(ia, st));
       sa.scores = ia.scores; sa.ld = ia.ld; sa.first_row = ia.row0; sa.stored_rows = ia.stored_rows;
+    }
+  }
+  if (dec) {
+    // the core the decode step of this shape selects with
+    int nsplit, split_len;
+    decode_split(sh, sh.M < sh.max_len ? sh.M : sh.max_len, nsplit, split_len);
+    if (decode_fused(sh, nsplit, split_len)) {
+      LAUNCH(KID_SELECT, st, launch_select_runs(sa, st));
+      return LISA_OK;
     }
   }
   LAUNCH(KID_SELECT, st, launch_select(sa, st));

@@ -211,6 +211,8 @@ size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit);
 // (every split block selects the whole row; split partials as above).
 bool select_attend_supported(const Shape& sh, int nsplit, int split_len);
 hipError_t launch_select_attend(const AttnArgs& a, const SelectArgs& sa, hipStream_t st);
+// the selection core of launch_select_attend alone (decode rows, full index lists)
+hipError_t launch_select_runs(const SelectArgs& sa, hipStream_t st);
 
 
 }  // namespace lisa

@@ -102,14 +102,38 @@ def gpu_prefill(cfg: LayerConfig, inp, M=None, flags=0, want_idx=True, S0=None, 
     return {"out": host(out), "idx": None if idx is None else host(idx), "S": host(S), "z": host(z)}
 
 
-def gpu_select_rows(rows, M, scores_ld=None, dtype="bf16"):
-    """lisa_indexer_topk in decode-row mode over given fp32 score rows."""
+def decode_split(P, B, H_kv):
+    """Split length and count of the decode attention over P selected entries
+    (the library's rule, mirrored to name the select core a shape uses)."""
+    sl = 64
+    while -(-P // sl) > 32:
+        sl *= 2
+    if B * H_kv * -(-P // sl) > 1024 and sl < 128:
+        sl = 128
+    while B * H_kv * -(-P // sl) > 4096 and sl < P:
+        sl *= 2
+    return sl, -(-P // sl)
+
+
+def decode_select_core(B, H_kv, d, M, max_len):
+    """Which select core the decode step of this shape runs: 'runs' (inside
+    the fused select + attention launch, few sequences with rows of up to
+    32K) or 'general' (the separate select launch)."""
+    sl, ns = decode_split(min(M, max_len), B, H_kv)
+    if max_len <= 32768 and sl <= 64 and ns <= 32 and B * H_kv * ns <= 512:
+        return "runs"
+    return "general"
+
+
+def gpu_select_rows(rows, M, scores_ld=None, dtype="bf16", H_q=1, H_kv=1, d=32):
+    """lisa_indexer_topk in decode-row mode over given fp32 score rows; the
+    shape's heads and head dim pick the select core (decode_select_core)."""
     lens = np.array([len(r) for r in rows], dtype=np.int32)
     ld = int(scores_ld or max(4, int(np.ceil(lens.max() / 4) * 4)))
     buf = np.zeros((len(rows), ld), dtype=np.float32)
     for i, r in enumerate(rows):
         buf[i, :len(r)] = r
-    sh = L.make_shape(B=len(rows), H_q=1, H_kv=1, d=32, H_I=1, H_Ik=1, d_I=16, hidden=1, M=M,
+    sh = L.make_shape(B=len(rows), H_q=H_q, H_kv=H_kv, d=d, H_I=1, H_Ik=1, d_I=16, hidden=1, M=M,
                       cap=int(lens.max()), max_len=int(lens.max()), dtype=dtype)
     idx = torch.full((len(rows), M), -7, dtype=torch.int32, device="cuda")
     L.lisa_indexer_topk(sh, L.LISA_ROWS_DECODE, 0, torch.from_numpy(lens).cuda(), None, None, None,
