@@ -153,6 +153,29 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens,
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same decode step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): its workspace is a static device array of
+ * LISA_DECODE_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  The call allocates nothing and frees nothing.  Arguments and
+ * results are those of lisa_decode_step without ws/ws_bytes; a shape whose
+ * lisa_workspace_bytes(shape, LISA_OP_DECODE, 0) exceeds
+ * LISA_DECODE_SCRATCH_BYTES is rejected with LISA_ERR_WORKSPACE (4 MiB
+ * covers batch 1 at contexts up to 16K with M = 2048 for a 28/4-head,
+ * d = 128 layer).  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents (nothing in it has to start at zero): calls that
+ * overlap on one GPU, e.g. on two streams, race and must not be made.
+ */
+#define LISA_DECODE_SCRATCH_BYTES ((size_t)4 << 20)
+int lisa_decode_step_noalloc(const lisa_shape* shape, const int32_t* seq_lens,
+                             const void* q, const void* k_new, const void* v_new,
+                             const void* q_idx, const void* k_idx_new,
+                             const void* q_lin, const void* k_lin, const void* v_lin,
+                             const void* x, const void* w_gate, const float* w_idx,
+                             void* k_cache, void* v_cache, void* k_idx_cache,
+                             float* S, float* z, void* out, int32_t* idx_out, void* stream);
+
+/*
  * Causal prefill of n tokens in every sequence (positions 0..n-1).
  *
  * q         [B, n, H_q, d] T

@@ -19,10 +19,11 @@ import torch
 
 __all__ = [
     "LisaError", "LisaLibraryMissing", "lisa_shape", "make_shape", "library",
-    "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
+    "lisa_workspace_bytes", "lisa_decode_step", "lisa_decode_step_noalloc", "lisa_prefill", "lisa_indexer_topk",
     "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_attention_mass",
     "lisa_indexer_kl", "lisa_candidate_dropout", "lisa_status_string", "lisa_last_error", "lisa_timing_enable",
     "lisa_timing_count", "lisa_kernel_name",
+    "LISA_DECODE_SCRATCH_BYTES",
     "workspace", "LISA_F32", "LISA_BF16", "LISA_LINEAR_UNNORMALIZED", "LISA_SLIDING_WINDOW",
     "LISA_OP_DECODE", "LISA_OP_PREFILL", "LISA_OP_TOPK_DECODE", "LISA_OP_TOPK_PREFILL",
     "LISA_OP_LINEAR_UPDATE", "LISA_OP_DENSE_DECODE", "LISA_OP_MASS",
@@ -40,9 +41,10 @@ LISA_SLIDING_WINDOW = 2
  LISA_OP_LINEAR_UPDATE, LISA_OP_DENSE_DECODE, LISA_OP_MASS, LISA_OP_DROPOUT_DECODE,
  LISA_OP_DROPOUT_PREFILL) = range(9)
 LISA_ROWS_DECODE, LISA_ROWS_PREFILL = 0, 1
+LISA_DECODE_SCRATCH_BYTES = 4 << 20
 
 EXPORTED_SYMBOLS = (
-    "lisa_workspace_bytes", "lisa_decode_step", "lisa_prefill", "lisa_indexer_topk",
+    "lisa_workspace_bytes", "lisa_decode_step", "lisa_decode_step_noalloc", "lisa_prefill", "lisa_indexer_topk",
     "lisa_linear_state_update", "lisa_segment_correct", "lisa_dense_decode", "lisa_attention_mass",
     "lisa_indexer_kl", "lisa_candidate_dropout", "lisa_status_string", "lisa_last_error", "lisa_timing_enable",
     "lisa_timing_count", "lisa_kernel_name",
@@ -95,6 +97,7 @@ def library() -> ctypes.CDLL:
     lib.lisa_workspace_bytes.argtypes = [sp, ctypes.c_int, _I32]
     lib.lisa_workspace_bytes.restype = ctypes.c_size_t
     lib.lisa_decode_step.argtypes = [sp] + [_P] * 20 + [ctypes.c_size_t, _P]
+    lib.lisa_decode_step_noalloc.argtypes = [sp] + [_P] * 19 + [_P]
     lib.lisa_decode_step.restype = ctypes.c_int
     lib.lisa_prefill.argtypes = [sp, _I32] + [_P] * 16 + [ctypes.c_size_t, _P]
     lib.lisa_prefill.restype = ctypes.c_int
@@ -194,6 +197,21 @@ def lisa_decode_step(shape, seq_lens, q, k_new, v_new, q_idx, k_idx_new, q_lin, 
         _ptr(idx_out, "idx_out", torch.int32), _ptr(ws, "ws"), 0 if ws is None else ws.numel(),
         _stream(stream))
     _check(rc, "lisa_decode_step")
+
+
+def lisa_decode_step_noalloc(shape, seq_lens, q, k_new, v_new, q_idx, k_idx_new, q_lin, k_lin, v_lin,
+                             x, w_gate, w_idx, k_cache, v_cache, k_idx_cache, S, z, out, idx_out, stream=None):
+    T = _act(shape)
+    rc = library().lisa_decode_step_noalloc(
+        ctypes.byref(shape), _ptr(seq_lens, "seq_lens", torch.int32),
+        _ptr(q, "q", T), _ptr(k_new, "k_new", T), _ptr(v_new, "v_new", T),
+        _ptr(q_idx, "q_idx", T), _ptr(k_idx_new, "k_idx_new", T),
+        _ptr(q_lin, "q_lin", T), _ptr(k_lin, "k_lin", T), _ptr(v_lin, "v_lin", T),
+        _ptr(x, "x", T), _ptr(w_gate, "w_gate", T), _ptr(w_idx, "w_idx", torch.float32),
+        _ptr(k_cache, "k_cache", T), _ptr(v_cache, "v_cache", T), _ptr(k_idx_cache, "k_idx_cache", T),
+        _ptr(S, "S", torch.float32), _ptr(z, "z", torch.float32), _ptr(out, "out", T),
+        _ptr(idx_out, "idx_out", torch.int32), _stream(stream))
+    _check(rc, "lisa_decode_step_noalloc")
 
 
 def lisa_prefill(shape, n, q, k_cache, v_cache, k_idx_cache, q_idx, q_lin, k_lin, v_lin, x,

@@ -17,6 +17,9 @@
 
 using namespace lisa;
 
+// Workspace of lisa_decode_step_noalloc (see decode_scratch below).
+static __device__ __align__(256) unsigned char scratch[LISA_DECODE_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
@@ -318,6 +321,37 @@ bool timing_armed() { return g_timing.kid >= 0 && g_timing.count < g_timing.n; }
     if (e_ != hipSuccess) return fail_hip(e_, kKernelNames[kid]);                   \
   } while (0)
 
+// ---------------------------------------------------------------------------
+// static scratch of the allocation-free decode step: one copy per GPU, held
+// until the process ends.  Host code reaches it only through the device
+// address that hipGetSymbolAddress returns on each device.
+// ---------------------------------------------------------------------------
+constexpr int MAX_DEVICES = 64;
+
+int decode_scratch(void*& ptr) {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "decode scratch: hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(LISA_ERR_UNSUPPORTED, "device %d beyond %d", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail_hip(e != hipSuccess ? e : hipErrorInvalidSymbol, "decode scratch address");
+    addr[dev] = p;
+  }
+  ptr = addr[dev];
+  return LISA_OK;
+}
+
+int decode_step(const Shape& sh, const int32_t* seq_lens, const void* q, const void* k_new, const void* v_new,
+                const void* q_idx, const void* k_idx_new, const void* q_lin, const void* k_lin, const void* v_lin,
+                const void* x, const void* w_gate, const float* w_idx, void* k_cache, void* v_cache,
+                void* k_idx_cache, float* S, float* z, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                void* stream);
+
 }  // namespace
 
 LaunchEvents& lisa::next_launch_events() { return g_next_launch; }
@@ -407,6 +441,42 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   int rc = check_shape(shape, sh);
   if (rc) return rc;
   if ((rc = check_decode_len(sh))) return rc;
+  return decode_step(sh, seq_lens, q, k_new, v_new, q_idx, k_idx_new, q_lin, k_lin, v_lin, x, w_gate, w_idx,
+                     k_cache, v_cache, k_idx_cache, S, z, out, idx_out, ws, ws_bytes, stream);
+}
+
+int lisa_decode_step_noalloc(const lisa_shape* shape, const int32_t* seq_lens, const void* q, const void* k_new,
+                             const void* v_new, const void* q_idx, const void* k_idx_new, const void* q_lin,
+                             const void* k_lin, const void* v_lin, const void* x, const void* w_gate,
+                             const float* w_idx, void* k_cache, void* v_cache, void* k_idx_cache, float* S,
+                             float* z, void* out, int32_t* idx_out, void* stream) {
+  Shape sh;
+  int rc = check_shape(shape, sh);
+  if (rc) return rc;
+  if ((rc = check_decode_len(sh))) return rc;
+  const size_t need = decode_ws(sh).total;
+  if (need > LISA_DECODE_SCRATCH_BYTES)
+    return fail(LISA_ERR_WORKSPACE,
+                "this shape needs %zu bytes of decode workspace; the allocation-free decode step holds %zu "
+                "(use lisa_decode_step with a caller workspace)",
+                need, (size_t)LISA_DECODE_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((rc = decode_scratch(ws))) return rc;
+  return decode_step(sh, seq_lens, q, k_new, v_new, q_idx, k_idx_new, q_lin, k_lin, v_lin, x, w_gate, w_idx,
+                     k_cache, v_cache, k_idx_cache, S, z, out, idx_out, ws, LISA_DECODE_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The decode step after shape validation: pointer checks, then the launches
+// on the workspace `ws` (caller-owned, or the static scratch).
+int decode_step(const Shape& sh, const int32_t* seq_lens, const void* q, const void* k_new, const void* v_new,
+                const void* q_idx, const void* k_idx_new, const void* q_lin, const void* k_lin, const void* v_lin,
+                const void* x, const void* w_gate, const float* w_idx, void* k_cache, void* v_cache,
+                void* k_idx_cache, float* S, float* z, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
+                void* stream) {
   const bool window = sh.flags & LISA_SLIDING_WINDOW;  // no indexer: its arguments are not used
   // A budget of at least max_len keeps every position of every sequence, so
   // the scores cannot change the selection: the step appends the index key
@@ -475,6 +545,10 @@ int lisa_decode_step(const lisa_shape* shape, const int32_t* seq_lens, const voi
   LAUNCH(KID_ATTN_COMBINE, st, launch_attention_combine(aa, st));
   return LISA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int lisa_dense_decode(const lisa_shape* shape, const int32_t* seq_lens, const void* q, const void* k_cache,
                       const void* v_cache, void* out, void* ws, size_t ws_bytes, void* stream) {
