@@ -11,7 +11,7 @@
  *        s[t,j] = sum_{h < H_I} w_idx[h] * max(0, q_idx[t,h] . k_idx[j, h*H_Ik/H_I])
  *   2. Top-M selection: the min(M, t+1) keys with the largest s[t,j]; equal
  *      scores go to the later position, -0.0 equals +0.0 ([LISA] Section 3.2
- *      Stage 2, "select the M positions with the largest values").
+ *      Stage 2, the top-M step that follows the summed indexer score).
  *   3. Sparse GQA softmax attention over the selected cached K/V rows, scale
  *      1/sqrt(d), query head h reading KV head h*H_kv/H_q ([LISA] Section
  *      3.1 Softmax Attention; Section 3.2 SA_M).
@@ -176,7 +176,10 @@ int lisa_decode_step_noalloc(const lisa_shape* shape, const int32_t* seq_lens,
                              float* S, float* z, void* out, int32_t* idx_out, void* stream);
 
 /*
- * Causal prefill of n tokens in every sequence (positions 0..n-1).
+ * Causal prefill of n tokens in every sequence (positions 0..n-1): steps 1-5
+ * above for every row t < n ([LISA] Section 3.2 Stages 1-2 for the indexer,
+ * the selection and SA_M; Section 3.3 Eqs. 3-5 for the linear branch as a
+ * chunked causal scan and the gate).  Rows with t + 1 <= M take every key.
  *
  * q         [B, n, H_q, d] T
  * k_cache, v_cache [B, cap, H_kv, d] T, k_idx_cache [B, cap, H_Ik, d_I] T:

@@ -12,12 +12,12 @@
 // the online softmax.
 //
 // Block = 4 waves of one KV head, each wave one (query head, 32 query
-// positions) unit; the K tile (row-major) and V tile (transposed) of 64
-// keys are staged in LDS for all four waves.  Per tile a wave computes
-// S^T = K Q^T (keys along the accumulator rows, so a lane holds four
-// consecutive keys of one query), masks and exponentiates it, and feeds the
-// probabilities straight from registers into O += P V, with the key order
-// of the contraction permuted the same way in P and in V.
+// positions) unit; the K and V tiles of 64 keys are staged row-major in LDS
+// for all four waves.  Per tile a wave computes S^T = K Q^T (keys along the
+// accumulator rows, so a lane holds four consecutive keys of one query),
+// masks and exponentiates it, and feeds the probabilities straight from
+// registers into O += P V; the V operands come from transposing LDS loads in
+// the key order of the P operand.
 #include "lisa_common.h"
 #include "lisa_kernels.h"
 #include "lisa_mfma.h"
@@ -29,34 +29,31 @@ constexpr int AK = 64;    // keys per tile
 constexpr int AP = 2;     // query tiles of 16 per wave
 constexpr int AQ = 16 * AP;
 
-// Row strides of 4 dwords modulo the 32 LDS banks keep every 16-byte
-// operand read free of bank conflicts.  The key columns of the V tile are
-// stored permuted within each 32-key half (vt_col), so that the eight keys
-// one lane contributes to a P V step are adjacent.
-// Two buffers: tile kt is read from buffer kt & 1 while tile kt + 1 is
-// staged into the other one.
+// K tile rows are D + 8 elements apart (4 dwords modulo the 64 LDS banks), so
+// the 16-byte K operand reads of 16 lanes (16 rows, one column block) hit
+// every bank once.  The V tile is stored row-major too, D + 16 elements
+// apart (8 dwords modulo 64): its operands are read with the transposing
+// 8-byte LDS load, and the two 16-lane groups served together read 8 rows x
+// 8 dwords, again every bank once.  Two buffers: tile kt is read from one
+// while tile kt + 1 is staged into the other.
 template <int D>
 struct AttnShared {
   bf16_t k[2][AK][D + 8];
-  bf16_t vt[2][D][AK + 8];
+  bf16_t v[2][AK][D + 16];
 };
-
-// Column of key j in the V tile: key 32 s + 16 h + 4 g + r sits at
-// 32 s + 8 g + 4 h + r, matching the P operand, whose lane group g holds keys
-// 32 s + 4 g + r and 32 s + 16 + 4 g + r of contraction step s.
-__device__ __forceinline__ int vt_col(int j) { return (j & 32) | ((j & 12) << 1) | ((j & 16) >> 2) | (j & 3); }
 
 template <int D>
 struct AttnRegs {
-  static constexpr int NK = AK * D / 8 / 256;   // K vectors per thread
-  static constexpr int NV = AK * D / 16 / 256;  // V token pairs per thread
-  uint4 k[NK], v[2 * NV];
+  static constexpr int NK = AK * D / 8 / 256;   // 16-byte K (and V) vectors per thread
+  uint4 k[NK], v[NK];
   uint2 mw[AP];                                 // mask words of the lane's query rows
 };
 
+// Thread tid stages vectors e = tid + 256 m: row e / (D / 8), columns
+// 8 (e % (D / 8)) .. + 7, of both tiles.
 template <int D>
 __device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& sm, int buf, bool with_v) {
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int m = 0; m < AttnRegs<D>::NK; ++m) {
     const int e = tid + 256 * m;
@@ -64,17 +61,24 @@ __device__ __forceinline__ void attn_stage(const AttnRegs<D>& r, AttnShared<D>& 
   }
   if (!with_v) return;
 #pragma unroll
-  for (int m = 0; m < AttnRegs<D>::NV; ++m) {
-    const int tau = lane & 31, c8 = 2 * (wave + 4 * m) + (lane >> 5);
-    const uint32_t a[4] = {r.v[2 * m].x, r.v[2 * m].y, r.v[2 * m].z, r.v[2 * m].w};
-    const uint32_t b[4] = {r.v[2 * m + 1].x, r.v[2 * m + 1].y, r.v[2 * m + 1].z, r.v[2 * m + 1].w};
-    const int col = vt_col(2 * tau);  // keys 2 tau and 2 tau + 1 stay adjacent
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * c8 + 2 * e][col]) = __builtin_amdgcn_perm(b[e], a[e], 0x05040100u);
-      *reinterpret_cast<uint32_t*>(&sm.vt[buf][8 * c8 + 2 * e + 1][col]) = __builtin_amdgcn_perm(b[e], a[e], 0x07060302u);
-    }
+  for (int m = 0; m < AttnRegs<D>::NK; ++m) {
+    const int e = tid + 256 * m;
+    *reinterpret_cast<uint4*>(&sm.v[buf][e / (D / 8)][8 * (e % (D / 8))]) = r.v[m];
   }
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// The transposing LDS load (ds_read_b64_tr_b16) works on groups of 16 lanes:
+// if lane j of a group points at 4 consecutive 16-bit elements X[j][0..3],
+// lane l receives X[4 e + l / 4][l % 4] for e = 0..3.  With lane j pointing
+// at row R0 + j / 4, columns C0 + 4 (j % 4) .. + 3 of a row-major tile, lane
+// l thus receives rows R0 .. R0 + 3 of column C0 + l: four consecutive keys
+// of one V column, the layout of an MFMA B fragment.
+__device__ __forceinline__ v4i16 lds_read_tr4(const bf16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
 
 template <int D>
@@ -83,7 +87,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   const Shape& sh = a.sh;
   const int n = a.n;
   const int G = sh.H_q / sh.H_kv;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);  // uniform: scalar unit bookkeeping
   const int r16 = lane & 15, g = lane >> 4;
   // Work units are (query tile of AQ rows, head of the KV group) pairs,
   // numbered head-fastest from the last query tile down; block k takes
@@ -124,17 +129,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   const __amdgpu_buffer_rsrc_t mres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.mask + (size_t)b * n * a.mask_ld), (short)0, (int)(n * a.mask_ld * 4), 0x00020000);
   const uint32_t tile_kv_bytes = (uint32_t)(AK * kv_stride * 2);
-  uint32_t koff[AttnRegs<D>::NK], voff[2 * AttnRegs<D>::NV], moff_b[AP];
+  // K and V share the cache layout, so one offset per staged vector serves both
+  uint32_t koff[AttnRegs<D>::NK], moff_b[AP];
 #pragma unroll
   for (int m = 0; m < AttnRegs<D>::NK; ++m) {
     const int e = tid + 256 * m;
     koff[m] = (uint32_t)(((e / (D / 8)) * kv_stride + (size_t)kvh * D + 8 * (e % (D / 8))) * 2);
-  }
-#pragma unroll
-  for (int m = 0; m < AttnRegs<D>::NV; ++m) {
-    const int tau = lane & 31, c8 = 2 * (wave + 4 * m) + (lane >> 5);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) voff[2 * m + u] = (uint32_t)(((2 * tau + u) * kv_stride + (size_t)kvh * D + 8 * c8) * 2);
   }
   // mask rows of the wave's queries (rows past n read row n - 1; never stored)
 #pragma unroll
@@ -148,12 +148,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   auto prefetch = [&](int kt, bool with_v) {
     const uint32_t tk = (uint32_t)kt * tile_kv_bytes;
 #pragma unroll
-    for (int m = 0; m < AttnRegs<D>::NK; ++m)
-      rg.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kres, koff[m] + tk, 0, 0));
-    if (with_v) {
-#pragma unroll
-      for (int m = 0; m < 2 * AttnRegs<D>::NV; ++m)
-        rg.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vres, voff[m] + tk, 0, 0));
+    for (int m = 0; m < AttnRegs<D>::NK; ++m) {
+      const uint32_t off = koff[m] + tk;
+      rg.k[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kres, off, 0, 0));
+      if (with_v) rg.v[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vres, off, 0, 0));
     }
     if (!a.window) {
 #pragma unroll
@@ -210,6 +208,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
 
   // the V operand of the row-sum block: every entry 1.0 (a constant, not an LDS read)
   const bf16x8 ones = as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  // V operand of output block q, contraction step s: keys 32 s + 4 g + 0..3
+  // and 32 s + 16 + 4 g + 0..3 (the key order of the P operand) of column
+  // 16 q + r16, as two transposing loads; lane r16 of group g points at row
+  // 4 g + r16 / 4 (plus 32 s, plus 16), columns 16 q + 4 (r16 % 4) .. + 3
+  const int vrow = 4 * g + (r16 >> 2), vcol = 4 * (r16 & 3);
+  auto v_operand = [&](int buf, int q, int s) -> bf16x8 {
+    const bf16_t* p = &sm.v[buf][32 * s + vrow][16 * q + vcol];
+    const v4i16 lo = lds_read_tr4(p);
+    const v4i16 hi = lds_read_tr4(p + 16 * (D + 16));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   // Walks the key tiles: body(kt, buf, mw) computes tile kt from LDS buffer
   // buf with the mask words mw of the wave's rows, while tile kt + 1 (loaded
@@ -239,8 +248,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   // Every row accumulates O = sum_k p_k v_k and l = sum_k p_k with
   // p_k = exp2(s_k scale - moff) for one fixed offset per row, so the
   // accumulators are never rescaled.  First attempt: the offset is the
-  // row's max over the whole first key tile (unmasked; any finite offset
-  // gives the same softmax in exact arithmetic).  The attempt is kept when l
+  // row's max over the whole first key tile the wave computes (unmasked; any
+  // finite offset gives the same softmax in exact arithmetic).  The attempt is kept when l
   // lies in [2^-60, inf) and O is finite for every row of the block, which
   // bounds both underflow of the leading terms and overflow; otherwise the
   // block recomputes with the exact max over the selected keys (a pass over
@@ -248,12 +257,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   f32x4 o[AP][NQ];
   float moff[AP];
   // O += P V over all key tiles with the offsets in moff; with set_offset the
-  // offsets are first taken from the first tile
+  // offsets are first taken from the first tile the wave computes
   auto accumulate = [&](bool set_offset) {
 #pragma unroll
     for (int i = 0; i < AP; ++i)
 #pragma unroll
       for (int q = 0; q < NQ; ++q) o[i][q] = zero4();
+    bool need_offset = set_offset;  // uniform over the wave
     walk(true, [&](int kt, int buf, const uint2 (&mw)[AP]) {
       const int J0 = kt * AK;
       uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
       __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int i = 0; i < AP; ++i) {
-        if (set_offset && kt == kt0) {  // the row's offset: max over the first tile
+        if (need_offset) {  // the row's offset: max over the first computed tile
           float m = -INFINITY;
 #pragma unroll
           for (int c = 0; c < 4; ++c) m = fmaxf(m, fmaxf(fmaxf(st[i][c][0], st[i][c][1]), fmaxf(st[i][c][2], st[i][c][3])));
@@ -294,14 +304,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
         for (int s = 0; s < 2; ++s) pf[i][s] = make_uint4(pk[2 * s][0], pk[2 * s][1], pk[2 * s + 1][0], pk[2 * s + 1][1]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      need_offset = false;
       __builtin_amdgcn_s_setprio(1);
-      // O += P V over the output blocks and the ones block: V operand of block
-      // q, step s: keys {32 s + 4 g .. +3, 32 s + 16 + 4 g .. +3}
+      // O += P V over the output blocks and the ones block
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const bf16x8 vf = q < NQ - 1 ? as_bf16x8(lds_read16(&sm.vt[buf][16 * q + r16][32 * s + 8 * g])) : ones;
+          const bf16x8 vf = q < NQ - 1 ? v_operand(buf, q, s) : ones;
 #pragma unroll
           for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf, o[i][q]);
         }
