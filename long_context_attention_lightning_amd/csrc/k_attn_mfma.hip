@@ -18,6 +18,8 @@
 // masks and exponentiates it, and feeds the probabilities straight from
 // registers into O += P V; the V operands come from transposing LDS loads in
 // the key order of the P operand.
+#include <type_traits>
+
 #include "lisa_common.h"
 #include "lisa_kernels.h"
 #include "lisa_mfma.h"
@@ -29,16 +31,17 @@ constexpr int AK = 64;    // keys per tile
 constexpr int AP = 2;     // query tiles of 16 per wave
 constexpr int AQ = 16 * AP;
 
-// K tile rows are D + 8 elements apart (4 dwords modulo the 64 LDS banks), so
-// the 16-byte K operand reads of 16 lanes (16 rows, one column block) hit
-// every bank once.  The V tile is stored row-major too, D + 16 elements
-// apart (8 dwords modulo 64): its operands are read with the transposing
-// 8-byte LDS load, and the two 16-lane groups served together read 8 rows x
-// 8 dwords, again every bank once.  Two buffers: tile kt is read from one
-// while tile kt + 1 is staged into the other.
+// Both tiles are stored row-major with rows D + 16 elements apart: 8 dwords
+// modulo the 64 LDS banks, and 16-byte aligned.  Measured on gfx950 with the
+// access patterns below (16-byte K operand reads of 16 rows per column
+// block, transposing 8-byte V reads): this stride runs conflict-free at 4
+// LDS cycles per wave-wide 16-byte read, while a stride of 4 dwords modulo
+// 64 takes 8 (half of them bank-conflict stalls) and an unaligned one also 8.
+// Two buffers: tile kt is read from one while tile kt + 1 is staged into
+// the other.
 template <int D>
 struct AttnShared {
-  bf16_t k[2][AK][D + 8];
+  bf16_t k[2][AK][D + 16];
   bf16_t v[2][AK][D + 16];
 };
 
@@ -84,6 +87,8 @@ __device__ __forceinline__ v4i16 lds_read_tr4(const bf16_t* p) {
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) {  // two blocks per CU
   __shared__ AttnShared<D> sm;
+  __shared__ uint16_t tiles[ATTN_MAX_TILES];  // the key tiles the block walks, ascending
+  __shared__ int tile_count[4];
   const Shape& sh = a.sh;
   const int n = a.n;
   const int G = sh.H_q / sh.H_kv;
@@ -118,6 +123,36 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
 
   const float scale = a.scale_log2e;
   const int nkt = tmax / AK + 1;
+
+  // The key tiles to walk: from kt0 in window mode; otherwise the tiles in
+  // which some row of the block's (at most two) query tiles selects a key,
+  // as the select kernel recorded them.  For spread-out selections that is
+  // every causal tile; clustered ones (recent keys, sinks) skip the rest.
+  int count = 0;
+  {
+    const uint32_t* occ_hi = nullptr;
+    const uint32_t* occ_lo = nullptr;
+    if (!a.window && a.occ) {
+      const size_t occ_rows = (size_t)(n + AQ - 1) / AQ;
+      const int T0_high = (nqt - 1 - (4 * kblk) / G) * AQ;
+      occ_hi = a.occ + ((size_t)b * occ_rows + T0_high / AQ) * a.occ_ld;
+      occ_lo = a.occ + ((size_t)b * occ_rows + T0_low / AQ) * a.occ_ld;
+    }
+    for (int base = 0; base < nkt; base += 256) {
+      const int tile = base + tid;
+      bool on = tile < nkt && tile >= kt0;
+      if (on && occ_hi) on = ((occ_hi[tile >> 5] | occ_lo[tile >> 5]) >> (tile & 31)) & 1u;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+      if (lane == 0) tile_count[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int pos = count;
+      for (int w = 0; w < wave; ++w) pos += tile_count[w];
+      pos += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (on) tiles[pos] = (uint16_t)tile;
+      count += tile_count[0] + tile_count[1] + tile_count[2] + tile_count[3];
+      __syncthreads();
+    }
+  }
 
   // K, V and mask rows of the sequence through buffer resources limited to
   // its n rows: loads past them return zeros.  Per-thread byte offsets start
@@ -173,16 +208,30 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   // on tiles that reach past the wave's first query
   // (every K operand read from LDS serves all AP query tiles)
   auto scores = [&](int buf, int J0, const uint2 (&mw)[AP], f32x4 (&st)[AP][4], uint32_t (&sel)[AP][4]) {
+    // K operands of key block c: key 16 c + r16, dims 32 s + 8 g .. + 7.  The
+    // reads of block c + 1 go out before the MFMAs of block c, so the LDS
+    // latency hides behind 2 D / 32 MFMAs instead of stalling each pair.
+    bf16x8 kf[2][D / 32];
+    auto load_k = [&](int c, bf16x8 (&dst)[D / 32]) {
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) dst[s] = as_bf16x8(lds_read16(&sm.k[buf][16 * c + r16][32 * s + 8 * g]));
+    };
+    load_k(0, kf[0]);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      if (c + 1 < 4) load_k(c + 1, kf[(c + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < AP; ++i) st[i][c] = zero4();
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {  // K operand: key 16 c + r16, dims 32 s + 8 g .. + 7
-        const bf16x8 kf = as_bf16x8(lds_read16(&sm.k[buf][16 * c + r16][32 * s + 8 * g]));
+      for (int s = 0; s < D / 32; ++s)
 #pragma unroll
-        for (int i = 0; i < AP; ++i) st[i][c] = mfma16(kf, qreg[i][s], st[i][c]);
-      }
+        for (int i = 0; i < AP; ++i) st[i][c] = mfma16(kf[c & 1][s], qreg[i][s], st[i][c]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);  // LDS reads of block 0
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (c + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, D / 32, 0);  // reads of block c + 1
+      __builtin_amdgcn_sched_group_barrier(0x008, AP * D / 32, 0);           // MFMAs of block c
     }
 #pragma unroll
     for (int i = 0; i < AP; ++i) {
@@ -220,150 +269,181 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // Walks the key tiles: body(kt, buf, mw) computes tile kt from LDS buffer
-  // buf with the mask words mw of the wave's rows, while tile kt + 1 (loaded
-  // into registers one tile earlier) is staged into the other buffer; one
-  // barrier per tile.
-  auto walk = [&](bool with_v, auto&& body) {
-    uint2 mw[AP];
-    prefetch(kt0, with_v);
-    attn_stage<D>(rg, sm, kt0 & 1, with_v);
-#pragma unroll
-    for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
-    __syncthreads();
-    if (kt0 + 1 < nkt) prefetch(kt0 + 1, with_v);
-    for (int kt = kt0; kt < nkt; ++kt) {
-      body(kt, kt & 1, mw);
-      if (kt + 1 < nkt) {
-        attn_stage<D>(rg, sm, (kt + 1) & 1, with_v);
-#pragma unroll
-        for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
-      }
-      __syncthreads();
-      if (kt + 2 < nkt) prefetch(kt + 2, with_v);
-    }
-  };
   constexpr int NQ = D / 16 + 1;  // output column blocks, the last one accumulates the row sums
-
-  // Every row accumulates O = sum_k p_k v_k and l = sum_k p_k with
-  // p_k = exp2(s_k scale - moff) for one fixed offset per row, so the
-  // accumulators are never rescaled.  First attempt: the offset is the
-  // row's max over the whole first key tile the wave computes (unmasked; any
-  // finite offset gives the same softmax in exact arithmetic).  The attempt is kept when l
-  // lies in [2^-60, inf) and O is finite for every row of the block, which
-  // bounds both underflow of the leading terms and overflow; otherwise the
-  // block recomputes with the exact max over the selected keys (a pass over
-  // the key tiles without V), for which every p <= 1.
   f32x4 o[AP][NQ];
   float moff[AP];
-  // O += P V over all key tiles with the offsets in moff; with set_offset the
-  // offsets are first taken from the first tile the wave computes
-  auto accumulate = [&](bool set_offset) {
-#pragma unroll
-    for (int i = 0; i < AP; ++i)
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) o[i][q] = zero4();
-    bool need_offset = set_offset;  // uniform over the wave
-    walk(true, [&](int kt, int buf, const uint2 (&mw)[AP]) {
-      const int J0 = kt * AK;
-      uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
-      f32x4 st[AP][4];
-      uint32_t sel[AP][4];
-      // MFMA phases at raised wave priority, so that the other wave on the
-      // SIMD fills the matrix-core time with its softmax arithmetic
-      __builtin_amdgcn_s_setprio(1);
-      scores(buf, J0, mw, st, sel);
-      __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-      for (int i = 0; i < AP; ++i) {
-        if (need_offset) {  // the row's offset: max over the first computed tile
-          float m = -INFINITY;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) m = fmaxf(m, fmaxf(fmaxf(st[i][c][0], st[i][c][1]), fmaxf(st[i][c][2], st[i][c][3])));
-          m = fmaxf(m, __shfl_xor(m, 16, WAVE));
-          m = fmaxf(m, __shfl_xor(m, 32, WAVE));
-          moff[i] = m * scale;
+  // Everything from here to the epilogue is compiled twice: for a block
+  // that walks every tile from kt0 (the tile index is the step count, no
+  // list lookups) and for one that walks a list.
+  auto run = [&](auto dense_c) {
+    constexpr bool dense = decltype(dense_c)::value;
+    auto kt_of = [&](int i) -> int {
+      if constexpr (dense) return kt0 + i;
+      else return __builtin_amdgcn_readfirstlane((int)tiles[i]);
+    };
+    // Walks the listed key tiles: body(kt, buf, mw) computes tile kt from LDS
+    // buffer buf with the mask words mw of the wave's rows, while the next
+    // listed tile (loaded into registers one tile earlier) is staged into the
+    // other buffer; one barrier per tile.
+    auto walk = [&](bool with_v, auto&& body) {
+      uint2 mw[AP];
+      prefetch(kt_of(0), with_v);
+      attn_stage<D>(rg, sm, 0, with_v);
+  #pragma unroll
+      for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
+      __syncthreads();
+      if (1 < count) prefetch(kt_of(1), with_v);
+      for (int it = 0; it < count; ++it) {
+        body(kt_of(it), it & 1, mw);
+        if (it + 1 < count) {
+          attn_stage<D>(rg, sm, (it + 1) & 1, with_v);
+  #pragma unroll
+          for (int i = 0; i < AP; ++i) mw[i] = rg.mw[i];
         }
-        // exponent s scale - offset, replaced by -inf (exp2 -> 0) where the
-        // key is not selected
-        uint32_t pk[4][2];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float x[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t m = bitmask(sel[i][c], r);
-            x[r] = __uint_as_float((__float_as_uint(fmaf(st[i][c][r], scale, -moff[i])) & m) | (0xff800000u & ~m));
-          }
-#pragma unroll
-          for (int r = 0; r < 4; r += 2)
-            pk[c][r / 2] = cvt_pk_bf16(__builtin_amdgcn_exp2f(x[r]), __builtin_amdgcn_exp2f(x[r + 1]));
-        }
-        // contraction step s covers key blocks 2 s and 2 s + 1
-#pragma unroll
-        for (int s = 0; s < 2; ++s) pf[i][s] = make_uint4(pk[2 * s][0], pk[2 * s][1], pk[2 * s + 1][0], pk[2 * s + 1][1]);
-        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        if (it + 2 < count) prefetch(kt_of(it + 2), with_v);
       }
-      need_offset = false;
-      __builtin_amdgcn_s_setprio(1);
-      // O += P V over the output blocks and the ones block
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8 vf = q < NQ - 1 ? v_operand(buf, q, s) : ones;
-#pragma unroll
-          for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf, o[i][q]);
-        }
-      __builtin_amdgcn_s_setprio(0);
-    });
-  };
+    };
 
-  accumulate(true);
-  // keep the result unless some row of the block is out of range
-  bool bad = false;
-#pragma unroll
-  for (int i = 0; i < AP; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float l = o[i][NQ - 1][r];
-      bad |= !(l >= 0x1p-60f && l < INFINITY);
-#pragma unroll
-      for (int q = 0; q < NQ - 1; ++q) bad |= !(fabsf(o[i][q][r]) < INFINITY);
-    }
-  if (__syncthreads_or(bad)) {
-    // exact maxima over the selected keys (a pass without V), then again
-    float mx[AP];
-#pragma unroll
-    for (int i = 0; i < AP; ++i) mx[i] = -INFINITY;
-    walk(false, [&](int kt, int buf, const uint2 (&mw)[AP]) {
-      f32x4 st[AP][4];
-      uint32_t sel[AP][4];
-      scores(buf, kt * AK, mw, st, sel);
-#pragma unroll
-      for (int i = 0; i < AP; ++i) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {  // the score where selected, -inf elsewhere
-            const uint32_t m = bitmask(sel[i][c], r);
-            v[r] = __uint_as_float((__float_as_uint(st[i][c][r]) & m) | (0xff800000u & ~m));
+    // Every row accumulates O = sum_k p_k v_k and l = sum_k p_k with
+    // p_k = exp2(s_k scale - moff) for one fixed offset per row, so the
+    // accumulators are never rescaled.  First attempt: the offset is the
+    // row's max over the whole first key tile the wave computes (unmasked; any
+    // finite offset gives the same softmax in exact arithmetic).  The attempt is kept when l
+    // lies in [2^-60, inf) and O is finite for every row of the block, which
+    // bounds both underflow of the leading terms and overflow; otherwise the
+    // block recomputes with the exact max over the selected keys (a pass over
+    // the key tiles without V), for which every p <= 1.
+    // O += P V over all key tiles with the offsets in moff; with set_offset the
+    // offsets are first taken from the first tile the wave computes
+    auto accumulate = [&](bool set_offset) {
+  #pragma unroll
+      for (int i = 0; i < AP; ++i)
+  #pragma unroll
+        for (int q = 0; q < NQ; ++q) o[i][q] = zero4();
+      bool need_offset = set_offset;  // uniform over the wave
+      walk(true, [&](int kt, int buf, const uint2 (&mw)[AP]) {
+        const int J0 = kt * AK;
+        uint4 pf[AP][2];  // probabilities as bf16, contraction order of the P V step
+        f32x4 st[AP][4];
+        uint32_t sel[AP][4];
+        // MFMA phases at raised wave priority, so that the other wave on the
+        // SIMD fills the matrix-core time with its softmax arithmetic
+        __builtin_amdgcn_s_setprio(1);
+        scores(buf, J0, mw, st, sel);
+        __builtin_amdgcn_s_setprio(0);
+        // V operands of output blocks 0 and 1, read while the softmax runs;
+        // each later block's operands are read two blocks ahead of its MFMAs
+        bf16x8 vf[3][2];
+  #pragma unroll
+        for (int q = 0; q < 2; ++q)
+  #pragma unroll
+          for (int s = 0; s < 2; ++s) vf[q][s] = v_operand(buf, q, s);
+  #pragma unroll
+        for (int i = 0; i < AP; ++i) {
+          if (need_offset) {  // the row's offset: max over the first computed tile
+            float m = -INFINITY;
+  #pragma unroll
+            for (int c = 0; c < 4; ++c) m = fmaxf(m, fmaxf(fmaxf(st[i][c][0], st[i][c][1]), fmaxf(st[i][c][2], st[i][c][3])));
+            m = fmaxf(m, __shfl_xor(m, 16, WAVE));
+            m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+            moff[i] = m * scale;
           }
-          mx[i] = fmaxf(mx[i], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+          // exponent s scale - offset, replaced by -inf (exp2 -> 0) where the
+          // key is not selected
+          uint32_t pk[4][2];
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float x[4];
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t m = bitmask(sel[i][c], r);
+              x[r] = __uint_as_float((__float_as_uint(fmaf(st[i][c][r], scale, -moff[i])) & m) | (0xff800000u & ~m));
+            }
+  #pragma unroll
+            for (int r = 0; r < 4; r += 2)
+              pk[c][r / 2] = cvt_pk_bf16(__builtin_amdgcn_exp2f(x[r]), __builtin_amdgcn_exp2f(x[r + 1]));
+          }
+          // contraction step s covers key blocks 2 s and 2 s + 1
+  #pragma unroll
+          for (int s = 0; s < 2; ++s) pf[i][s] = make_uint4(pk[2 * s][0], pk[2 * s][1], pk[2 * s + 1][0], pk[2 * s + 1][1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        need_offset = false;
+        __builtin_amdgcn_s_setprio(1);
+        // O += P V over the output blocks, then the ones block
+  #pragma unroll
+        for (int q = 0; q < NQ - 1; ++q) {
+          if (q + 2 < NQ - 1)
+  #pragma unroll
+            for (int s = 0; s < 2; ++s) vf[(q + 2) % 3][s] = v_operand(buf, q + 2, s);
+  #pragma unroll
+          for (int s = 0; s < 2; ++s)
+  #pragma unroll
+            for (int i = 0; i < AP; ++i) o[i][q] = mfma16(as_bf16x8(pf[i][s]), vf[q % 3][s], o[i][q]);
+        }
+  #pragma unroll
+        for (int s = 0; s < 2; ++s)
+  #pragma unroll
+          for (int i = 0; i < AP; ++i) o[i][NQ - 1] = mfma16(as_bf16x8(pf[i][s]), ones, o[i][NQ - 1]);
+  #pragma unroll
+        for (int q = 0; q < NQ - 1; ++q) {
+          if (q + 2 < NQ - 1) __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);  // reads of block q + 2
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * AP, 1);                // MFMAs of block q
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * AP, 1);  // the ones block
+        __builtin_amdgcn_s_setprio(0);
+      });
+    };
+
+    accumulate(true);
+    // keep the result unless some row of the block is out of range
+    bool bad = false;
+  #pragma unroll
+    for (int i = 0; i < AP; ++i)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float l = o[i][NQ - 1][r];
+        bad |= !(l >= 0x1p-60f && l < INFINITY);
+  #pragma unroll
+        for (int q = 0; q < NQ - 1; ++q) bad |= !(fabsf(o[i][q][r]) < INFINITY);
       }
-    });
-#pragma unroll
-    for (int i = 0; i < AP; ++i) {
-      float m = fmaxf(mx[i], __shfl_xor(mx[i], 16, WAVE));
-      m = fmaxf(m, __shfl_xor(m, 32, WAVE));
-      moff[i] = m == -INFINITY ? 0.f : m * scale;
+    if (__syncthreads_or(bad)) {
+      // exact maxima over the selected keys (a pass without V), then again
+      float mx[AP];
+  #pragma unroll
+      for (int i = 0; i < AP; ++i) mx[i] = -INFINITY;
+      walk(false, [&](int kt, int buf, const uint2 (&mw)[AP]) {
+        f32x4 st[AP][4];
+        uint32_t sel[AP][4];
+        scores(buf, kt * AK, mw, st, sel);
+  #pragma unroll
+        for (int i = 0; i < AP; ++i) {
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float v[4];
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {  // the score where selected, -inf elsewhere
+              const uint32_t m = bitmask(sel[i][c], r);
+              v[r] = __uint_as_float((__float_as_uint(st[i][c][r]) & m) | (0xff800000u & ~m));
+            }
+            mx[i] = fmaxf(mx[i], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+  #pragma unroll
+      for (int i = 0; i < AP; ++i) {
+        float m = fmaxf(mx[i], __shfl_xor(mx[i], 16, WAVE));
+        m = fmaxf(m, __shfl_xor(m, 32, WAVE));
+        moff[i] = m == -INFINITY ? 0.f : m * scale;
+      }
+      __syncthreads();
+      accumulate(false);
     }
-    __syncthreads();
-    accumulate(false);
-  }
+  };
+  if (count == nkt - kt0) run(std::true_type{});
+  else run(std::false_type{});
   if (!active) return;
 
   // epilogue: out = g O_s + (1 - g) O_L for rows t = T0 + 16 i + 4 g + r;

@@ -54,6 +54,12 @@ __device__ __forceinline__ void select_one(const SelectArgs& a, int b, int t, Se
   select_row<THREADS, ITEMS, LKEYS>(srow, len, M, sm, ks, ld, res);
   if (orow) for_each_selected<THREADS, ITEMS>(res, [&](uint32_t rank, int pos) { if (rank < (uint32_t)M) orow[rank] = pos; });
   if (mrow) {
+    // tiles of 64 keys that hold a selected key of this row (up to 1024 tiles)
+    __shared__ uint32_t occ_row[32];
+    if (a.occ) {
+      if (tid < 32) occ_row[tid] = 0u;
+      __syncthreads();
+    }
     // eight consecutive lanes hold the 32 positions of one mask word
     const int lane = tid & (WAVE - 1);
 #pragma unroll
@@ -63,7 +69,16 @@ __device__ __forceinline__ void select_one(const SelectArgs& a, int b, int t, Se
       word |= (uint32_t)__shfl_xor((int)word, 1, WAVE);
       word |= (uint32_t)__shfl_xor((int)word, 2, WAVE);
       word |= (uint32_t)__shfl_xor((int)word, 4, WAVE);
-      if ((lane & 7) == 0 && 4 * f < len) mrow[f >> 3] = word;
+      if ((lane & 7) == 0 && 4 * f < len) {
+        mrow[f >> 3] = word;
+        if (a.occ && word) atomicOr(&occ_row[f >> 9], 1u << ((f >> 4) & 31));  // tile f / 16
+      }
+    }
+    if (a.occ) {  // merge into the row group's occupancy (32 rows share a word)
+      __syncthreads();
+      uint32_t* orow_occ = a.occ + ((size_t)b * a.occ_rows + t / 32) * a.occ_ld;
+      const int words = (len + 2047) / 2048;
+      if (tid < words && occ_row[tid]) atomicOr(&orow_occ[tid], occ_row[tid]);
     }
   }
   const int m = M < len ? M : len;
@@ -119,6 +134,19 @@ __global__ __launch_bounds__(256) void k_window_index(int32_t* idx, int n, int M
 hipError_t launch_window_index(int32_t* idx, int B, int n, int M, hipStream_t st) {
   if (B <= 0 || n <= 0) return hipSuccess;
   klaunch(k_window_index, dim3((unsigned)((size_t)B * n)), dim3(256), 0, st, idx, n, M);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_zero_u32(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// A kernel rather than a memset, so that the clear is an ordinary kernel
+// node when the call is captured into a graph.
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  klaunch(k_zero_u32, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

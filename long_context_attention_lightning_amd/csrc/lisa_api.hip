@@ -169,8 +169,13 @@ DenseWs dense_ws(const Shape& sh) {
 int64_t prefill_scores_ld(int n) { return (int64_t)align_up((size_t)n, 64); }
 
 struct PrefillWs {
-  size_t scores, idx, mask, o_lin, gate, w_t, z_tmp, seg, total;
+  size_t scores, idx, mask, occ, o_lin, gate, w_t, z_tmp, seg, total;
 };
+
+// Key-tile occupancy of the prefill bitmask: one row of words per 32 query
+// rows, one bit per key tile of 64.
+int64_t prefill_occ_ld(int n) { return (int64_t)(((n + 63) / 64 + 31) / 32); }
+size_t prefill_occ_words(const Shape& sh, int n) { return (size_t)sh.B * ((n + 31) / 32) * prefill_occ_ld(n); }
 
 PrefillWs prefill_ws(const Shape& sh, int n) {
   PrefillWs w;
@@ -180,6 +185,7 @@ PrefillWs prefill_ws(const Shape& sh, int n) {
   w.scores = L.take((size_t)sh.B * srows * prefill_scores_ld(n) * 4);
   w.idx = L.take(mfma_attn ? 0 : (size_t)sh.B * n * sh.M * 4);  // the MFMA path reads the bitmask
   w.mask = L.take(mfma_attn ? (size_t)sh.B * n * attn_mask_ld(n) * 4 : 0);
+  w.occ = L.take(mfma_attn ? prefill_occ_words(sh, n) * 4 : 0);
   w.o_lin = L.take((size_t)sh.B * n * sh.H_L * sh.d * 4);
   w.gate = L.take((size_t)sh.B * n * sh.H_q * 4);
   w.w_t = L.take(gate_mfma_supported(sh) ? gate_transpose_elems(sh) * 2 : 0);
@@ -893,6 +899,10 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
   sa.scores = ia.scores; sa.ld = ia.ld; sa.first_row = ia.row0; sa.stored_rows = ia.stored_rows;
   sa.M = sh.M; sa.max_len = n; sa.idx = idx; sa.idx_ld = sh.M;
   sa.mask = mfma_attn ? at<uint32_t>(ws, w.mask) : nullptr; sa.mask_ld = attn_mask_ld(n);
+  if (mfma_attn) {
+    sa.occ = at<uint32_t>(ws, w.occ); sa.occ_ld = prefill_occ_ld(n); sa.occ_rows = (n + 31) / 32;
+    LAUNCH(KID_SELECT, st, launch_zero_u32(sa.occ, prefill_occ_words(sh, n), st));
+  }
   LAUNCH(KID_SELECT, st, launch_select(sa, st));
   if (side) {  // join: the attention reads the gate logits and the linear outputs
     hipError_t e = hipEventRecord(side->join, side->s);
@@ -904,7 +914,7 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
     AttnMaskArgs am{};
     am.sh = sh; am.n = n; am.q = q; am.k_cache = k_cache; am.v_cache = v_cache; am.mask = sa.mask;
     am.mask_ld = sa.mask_ld; am.scale_log2e = 1.4426950408889634f / sqrtf((float)sh.d);
-    am.gate_part = ga.gate_part; am.o_lin = o_lin; am.out = out;
+    am.gate_part = ga.gate_part; am.o_lin = o_lin; am.out = out; am.occ = sa.occ; am.occ_ld = sa.occ_ld;
     LAUNCH(KID_PREFILL_ATTN, st, launch_attn_prefill_mfma(am, st));
     return LISA_OK;
   }

@@ -96,8 +96,16 @@ struct SelectArgs {
   int64_t idx_ld;
   uint32_t* mask;           // nullable [n_rows, mask_ld] selection bitmask
   int64_t mask_ld;
+  // nullable (prefill with a bitmask): tile occupancy, one row per 32 query
+  // rows of a sequence ([B, occ_rows, occ_ld] words, zeroed beforehand); bit
+  // k of word w is set when some row of the group selects a key of key tile
+  // 32 w + k (64 keys per tile)
+  uint32_t* occ;
+  int64_t occ_ld;
+  int occ_rows;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // gathered GQA softmax attention over selected rows, split + combine + gate

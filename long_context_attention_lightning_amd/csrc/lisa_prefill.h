@@ -74,7 +74,11 @@ struct AttnMaskArgs {
   void* out;                // [B, n, H_q, d]
   int window;               // sliding window of sh.M positions: no mask rows are read, and key
                             // tiles before every row's window are skipped
+  const uint32_t* occ;      // nullable: tile occupancy per 32 query rows ([B, ceil(n/32), occ_ld],
+                            // see SelectArgs); a block skips the key tiles its rows never select
+  int64_t occ_ld;
 };
+constexpr int ATTN_MAX_TILES = 1024;  // key tiles of 64 a block can list (n <= 65536)
 bool attn_mfma_supported(const Shape& sh);
 int64_t attn_mask_ld(int n);
 hipError_t launch_attn_prefill_mfma(const AttnMaskArgs& a, hipStream_t st);

@@ -103,6 +103,44 @@ def test_prefill_bf16_offset_fallback():
     _full_parity(cfg, inp, M, "offset fallback")
 
 
+def test_prefill_clustered_selection():
+    """Selections clustered in a few key tiles: a sink tile [0, 64) and a band
+    [640, 704) score positive for every query, every other key scores 0, and
+    the select breaks the ties at 0 toward the larger position, so each row
+    takes the two clusters plus its most recent keys.  Most key tiles are
+    then selected by no row of a block; the attention skips them and must
+    still match the oracle on every sampled row."""
+    n, M = 2048, 256
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n, M=M)
+    inp = prefill_inputs(cfg, n=n, salt=58)
+    from lisa_inputs import round_bf16
+    q_idx = np.zeros_like(inp["q_idx"])
+    q_idx[..., 0] = 1.0
+    k_idx = np.zeros_like(inp["k_idx"])
+    for lo, hi in ((0, 64), (640, 704)):
+        j = np.arange(lo, hi)
+        k_idx[:, lo:hi, :, 0] = (1.0 + (j % 64) / 64.0)[None, :, None]  # distinct in bf16
+    inp["q_idx"], inp["k_idx"] = q_idx, round_bf16(k_idx)
+    inp["w_idx"] = np.full_like(inp["w_idx"], 0.5)
+    rows = [0, 63, 64, 255, 256, 300, 639, 640, 703, 704, 705, 831, 832, 1000, 1337, 1500, 2000, 2047]
+    ref = oracle.prefill_rows(inp, M, rows)
+    clusters = set(range(64)) | set(range(640, 704))
+    for t in (1000, 2047):  # construction holds: both clusters, then the most recent keys
+        want = clusters | set(range(t - (M - len(clusters)) + 1, t + 1))
+        assert set(int(v) for v in ref["idx"][t]) == want, t
+    g = gpu_prefill(cfg, inp, M=M)
+    for t in rows:
+        assert [int(v) for v in g["idx"][0][t] if v >= 0] == [int(v) for v in ref["idx"][t]], t
+    got = np.stack([g["out"][0, t] for t in rows])
+    exp = np.stack([ref["out"][t] for t in rows])
+    assert_out_close(cfg, got, exp, "clustered selection")
+    sat = saturate_gate(inp, 1.0)  # the sparse branch alone
+    gs = gpu_prefill(cfg, sat, M=M, want_idx=False)
+    ref_s = oracle.prefill_rows(sat, M, rows)
+    assert_out_close(cfg, np.stack([gs["out"][0, t] for t in rows]), np.stack([ref_s["out"][t] for t in rows]),
+                     "clustered selection, sparse branch")
+
+
 def test_prefill_fp32_shared_key_small_heads():
     cfg = TINY_FP32_PREFILL.replace(H_q=6, H_kv=2, H_L=6, H_I=2, H_Ik=1, n=300, cap=300, d=64, d_I=16)
     _full_parity(cfg, prefill_inputs(cfg, n=300, salt=5), 40, "fp32 shared key")
