@@ -57,6 +57,11 @@ def parse():
     p.add_argument("--cpu-all", action="store_true", help="also time the oracle on a 16K prefill row (~30 s)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run four 256 MiB device copies (a counter-scaling reference)")
+    p.add_argument("--write-traffic", nargs=3, metavar=("LEG", "FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU work: read two rocprofv3 --pmc counter CSVs (FETCH_SIZE, then WRITE_SIZE) of a "
+                        "--copy-calibration run of one leg (decode: the default decode leg; prefill: "
+                        "--prefill-only) and record each library kernel's HBM bytes per launch in "
+                        "profiles/traffic.json")
     return p.parse_args()
 
 
@@ -354,8 +359,89 @@ def bench_mass(torch, Lb, cfg, sh, seq, sets, capture, time_graph, kernel_times,
 
 
 # ----------------------------------------------------------------------------
+# Library kernels by symbol: (name the bench reports them under, source files
+# whose hash ties a traffic record to the code it was taken on).
+_COMMON = ["lisa_common.h", "lisa_kernels.h"]
+TRAFFIC_KERNELS = {
+    "decode": {
+        "k_decode_phase_a": ("decode_phase_a", ["k_decode.hip", "lisa_attend.h", "lisa_mfma.h"] + _COMMON),
+        "k_select_attend": ("select_attention", ["k_decode_fused.hip", "lisa_select.h", "lisa_attend.h",
+                                                 "lisa_mfma.h"] + _COMMON),
+        "k_attn_combine": ("attention_combine", ["k_decode.hip", "lisa_attend.h", "lisa_mfma.h"] + _COMMON),
+    },
+    "prefill": {
+        "k_gate_transpose": ("prefill_gate_transpose", ["k_prefill_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+        "k_gate_mfma": ("prefill_gate", ["k_prefill_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+        "k_lin_seg_sums": ("prefill_linear_sums", ["k_linear_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+        "k_lin_seg_prefix": ("prefill_linear_prefix", ["k_linear_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+        "k_lin_chunks": ("prefill_linear", ["k_linear_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+        "k_index_scores_mfma": ("prefill_index_scores", ["k_prefill_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+        "k_select_rows256": ("topm_select", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
+        "k_attn_prefill_mfma": ("prefill_attention", ["k_attn_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+    },
+}
+
+
+TRAFFIC_WORKLOAD = {
+    "decode": "decode step, Qwen-7B-shaped layer, batch 1, 16384 tokens, M = 2048",
+    "prefill": "causal prefill, Qwen-7B-shaped layer, 16384 tokens, M = 2048",
+}
+
+
+def write_traffic(leg, fetch_csv, write_csv):
+    """HBM bytes per launch of each library kernel of one leg from two
+    rocprofv3 counter runs.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are
+    scaled by what they read for the calibration copies (an elementwise
+    kernel that reads and writes 256 MiB), then averaged over the kernel's
+    dispatches; the record carries the hash of the kernel's sources."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+
+    want = 256 << 20
+    out = {}
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        vals = per_kernel(path, counter)
+        # the calibration copies: torch.mul(src, 1.0, out=dst) on 64 Mi floats
+        copies = [v for (d, k), v in vals.items() if "AUnaryFunctor<float, float, float" in k and v * 1024 > want / 4]
+        if not copies:
+            sys.exit(f"{path}: no calibration copy found (run with --copy-calibration)")
+        factor = want / (1024.0 * float(np.median(copies)))
+        for sym, (name, _) in TRAFFIC_KERNELS[leg].items():
+            got = [v for (d, k), v in vals.items() if re.search(r"lisa::%s\b" % sym, k)]
+            if got:
+                out.setdefault(name, {})[counter] = (float(np.mean(got)), factor, len(got))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    prefix = "" if leg == "decode" else leg + ":"
+    for sym, (name, sources) in TRAFFIC_KERNELS[leg].items():
+        c = out.get(name, {})
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        (f_kib, f_fac, _), (w_kib, w_fac, _) = c["FETCH_SIZE"], c["WRITE_SIZE"]
+        fb, wb = f_kib * 1024 * f_fac, w_kib * 1024 * w_fac
+        rec[prefix + name] = {"bytes_per_launch": int(round(fb + wb)), "fetch_bytes": int(round(fb)),
+                              "write_bytes": int(round(wb)), "fetch_kib_raw": round(f_kib, 2),
+                              "write_kib_raw": round(w_kib, 2), "sources": sources,
+                              "source_sha256": source_hash(sources), "workload": TRAFFIC_WORKLOAD[leg]}
+        print(f"{prefix + name}: read {fb / 1e6:.3f} MB, written {wb / 1e6:.3f} MB per launch "
+              f"(scale {f_fac:.3f} / {w_fac:.3f})")
+    json.dump(rec, open(path, "w"), indent=1, sort_keys=False)
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer runs on a single "
               "MI355X and the library has no multi-GPU path.", file=sys.stderr)
