@@ -377,6 +377,7 @@ TRAFFIC_KERNELS = {
         "k_lin_chunks": ("prefill_linear", ["k_linear_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
         "k_index_scores_mfma": ("prefill_index_scores", ["k_prefill_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
         "k_select_rows256": ("topm_select", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
+        "k_mask_occupancy": ("prefill_tile_occupancy", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
         "k_attn_prefill_mfma": ("prefill_attention", ["k_attn_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
     },
 }
@@ -640,7 +641,7 @@ def bench_prefill(args, torch, Lb, prefill_inputs):
     kern = {}
     call()
     torch.cuda.synchronize()
-    for kid in (4, 9, 10, 5, 3, 1, 6):  # one launch each per call
+    for kid in (4, 9, 10, 5, 3, 1, 19, 6):  # one launch each per call
         st = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         sp = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         for e in st + sp:
@@ -672,6 +673,8 @@ def bench_prefill(args, torch, Lb, prefill_inputs):
         "prefill_attention": (4 * cfg.H_q * cfg.d * attn_pairs, "mfma"),
         "prefill_gate": (n * cfg.hidden * 2 + cfg.hidden * cfg.H_q * 2 + n * cfg.H_q * 4, "hbm"),
         "topm_select": (SELECT_OPS_PER_KEY * scored_pairs, "alu"),
+        # the key-tile occupancy reads the selection bitmask once
+        "prefill_tile_occupancy": (cfg.B * n * (((n + 31) // 32 + 1) // 2 * 2) * 4, "hbm"),
     }
     proofs = {k: kernel_roofline(k, kern[k] * 1e-3, *pwork[k], traffic_key="prefill:" + k) for k in pwork if kern.get(k)}
     # the linear branch as a whole (segment sums + prefix + chunked outputs)

@@ -54,12 +54,6 @@ __device__ __forceinline__ void select_one(const SelectArgs& a, int b, int t, Se
   select_row<THREADS, ITEMS, LKEYS>(srow, len, M, sm, ks, ld, res);
   if (orow) for_each_selected<THREADS, ITEMS>(res, [&](uint32_t rank, int pos) { if (rank < (uint32_t)M) orow[rank] = pos; });
   if (mrow) {
-    // tiles of 64 keys that hold a selected key of this row (up to 1024 tiles)
-    __shared__ uint32_t occ_row[32];
-    if (a.occ) {
-      if (tid < 32) occ_row[tid] = 0u;
-      __syncthreads();
-    }
     // eight consecutive lanes hold the 32 positions of one mask word
     const int lane = tid & (WAVE - 1);
 #pragma unroll
@@ -69,16 +63,7 @@ __device__ __forceinline__ void select_one(const SelectArgs& a, int b, int t, Se
       word |= (uint32_t)__shfl_xor((int)word, 1, WAVE);
       word |= (uint32_t)__shfl_xor((int)word, 2, WAVE);
       word |= (uint32_t)__shfl_xor((int)word, 4, WAVE);
-      if ((lane & 7) == 0 && 4 * f < len) {
-        mrow[f >> 3] = word;
-        if (a.occ && word) atomicOr(&occ_row[f >> 9], 1u << ((f >> 4) & 31));  // tile f / 16
-      }
-    }
-    if (a.occ) {  // merge into the row group's occupancy (32 rows share a word)
-      __syncthreads();
-      uint32_t* orow_occ = a.occ + ((size_t)b * a.occ_rows + t / 32) * a.occ_ld;
-      const int words = (len + 2047) / 2048;
-      if (tid < words && occ_row[tid]) atomicOr(&orow_occ[tid], occ_row[tid]);
+      if ((lane & 7) == 0 && 4 * f < len) mrow[f >> 3] = word;
     }
   }
   const int m = M < len ? M : len;
@@ -137,16 +122,42 @@ hipError_t launch_window_index(int32_t* idx, int B, int n, int M, hipStream_t st
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_zero_u32(uint32_t* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+// Key-tile occupancy of a prefill selection bitmask: one block per group of
+// 32 query rows of a sequence.  Lane w of a wave ORs mask word w of the 32
+// rows (64 consecutive words = 32 tiles of 64 keys per wave pass); a ballot
+// turns that into one occupancy word, tile bit t set when word 2 t or
+// 2 t + 1 is non-zero in some row.  Rows past n and words past a row's
+// length are zero in the bitmask or never read.
+__global__ __launch_bounds__(256) void k_mask_occupancy(const uint32_t* mask, int64_t mask_ld, int n, uint32_t* occ,
+                                                        int64_t occ_ld) {
+  const int groups = (n + 31) / 32;
+  const int b = blockIdx.x / groups, grp = blockIdx.x % groups;
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
+  const int r0 = 32 * grp, r1 = min(n, r0 + 32);
+  const int words = (r1 + 31) / 32;  // mask words any row of the group can use
+  const uint32_t* mb = mask + ((size_t)b * n + r0) * mask_ld;
+  uint32_t* ob = occ + ((size_t)b * groups + grp) * occ_ld;
+  for (int ow = wave; ow < occ_ld; ow += 4) {
+    const int w = 64 * ow + lane;
+    uint32_t acc = 0;
+    if (w < words)
+      for (int r = 0; r < r1 - r0; ++r) acc |= mb[(size_t)r * mask_ld + w];
+    uint64_t nz = __builtin_amdgcn_ballot_w64(acc != 0u);
+    nz = (nz | (nz >> 1)) & 0x5555555555555555ull;  // bit 2t: tile t occupied; compact to bit t
+    nz = (nz | (nz >> 1)) & 0x3333333333333333ull;
+    nz = (nz | (nz >> 2)) & 0x0f0f0f0f0f0f0f0full;
+    nz = (nz | (nz >> 4)) & 0x00ff00ff00ff00ffull;
+    nz = (nz | (nz >> 8)) & 0x0000ffff0000ffffull;
+    nz = (nz | (nz >> 16)) & 0x00000000ffffffffull;
+    if (lane == 0) ob[ow] = (uint32_t)nz;
+  }
 }
 
-// A kernel rather than a memset, so that the clear is an ordinary kernel
-// node when the call is captured into a graph.
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  const size_t blocks = (n + 255) / 256;
-  klaunch(k_zero_u32, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, p, n);
+hipError_t launch_mask_occupancy(const uint32_t* mask, int64_t mask_ld, int B, int n, uint32_t* occ, int64_t occ_ld,
+                                 hipStream_t st) {
+  if (B <= 0 || n <= 0) return hipSuccess;
+  klaunch(k_mask_occupancy, dim3((unsigned)((size_t)B * ((n + 31) / 32))), dim3(256), 0, st, mask, mask_ld, n, occ,
+          occ_ld);
   return hipGetLastError();
 }
 

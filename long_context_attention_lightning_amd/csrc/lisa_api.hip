@@ -302,7 +302,8 @@ const char* const kKernelNames[KID_COUNT] = {
     "decode_phase_a", "topm_select", "gather_attention", "prefill_index_scores", "prefill_gate",
     "prefill_linear", "prefill_attention", "linear_state_update", "attention_combine",
     "prefill_linear_sums", "prefill_linear_prefix", "prefill_gate_transpose", "select_attention",
-    "segment_correct", "mass_logits", "mass_select", "mass_reduce", "indexer_kl", "candidate_dropout_compact"};
+    "segment_correct", "mass_logits", "mass_select", "mass_reduce", "indexer_kl", "candidate_dropout_compact",
+    "prefill_tile_occupancy"};
 
 thread_local LaunchEvents g_next_launch;
 
@@ -899,11 +900,9 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
   sa.scores = ia.scores; sa.ld = ia.ld; sa.first_row = ia.row0; sa.stored_rows = ia.stored_rows;
   sa.M = sh.M; sa.max_len = n; sa.idx = idx; sa.idx_ld = sh.M;
   sa.mask = mfma_attn ? at<uint32_t>(ws, w.mask) : nullptr; sa.mask_ld = attn_mask_ld(n);
-  if (mfma_attn) {
-    sa.occ = at<uint32_t>(ws, w.occ); sa.occ_ld = prefill_occ_ld(n); sa.occ_rows = (n + 31) / 32;
-    LAUNCH(KID_SELECT, st, launch_zero_u32(sa.occ, prefill_occ_words(sh, n), st));
-  }
   LAUNCH(KID_SELECT, st, launch_select(sa, st));
+  uint32_t* occ = mfma_attn ? at<uint32_t>(ws, w.occ) : nullptr;
+  if (occ) LAUNCH(KID_PREFILL_OCCUPANCY, st, launch_mask_occupancy(sa.mask, sa.mask_ld, sh.B, n, occ, prefill_occ_ld(n), st));
   if (side) {  // join: the attention reads the gate logits and the linear outputs
     hipError_t e = hipEventRecord(side->join, side->s);
     if (e == hipSuccess) e = hipStreamWaitEvent(st, side->join, 0);
@@ -914,7 +913,7 @@ int lisa_prefill(const lisa_shape* shape, int32_t n, const void* q, const void* 
     AttnMaskArgs am{};
     am.sh = sh; am.n = n; am.q = q; am.k_cache = k_cache; am.v_cache = v_cache; am.mask = sa.mask;
     am.mask_ld = sa.mask_ld; am.scale_log2e = 1.4426950408889634f / sqrtf((float)sh.d);
-    am.gate_part = ga.gate_part; am.o_lin = o_lin; am.out = out; am.occ = sa.occ; am.occ_ld = sa.occ_ld;
+    am.gate_part = ga.gate_part; am.o_lin = o_lin; am.out = out; am.occ = occ; am.occ_ld = prefill_occ_ld(n);
     LAUNCH(KID_PREFILL_ATTN, st, launch_attn_prefill_mfma(am, st));
     return LISA_OK;
   }

@@ -50,7 +50,8 @@ enum KernelId {
   KID_MASS_REDUCE = 16,
   KID_INDEXER_KL = 17,
   KID_DROPOUT = 18,
-  KID_COUNT = 19
+  KID_PREFILL_OCCUPANCY = 19,
+  KID_COUNT = 20
 };
 
 // ---------------------------------------------------------------------------
@@ -96,16 +97,14 @@ struct SelectArgs {
   int64_t idx_ld;
   uint32_t* mask;           // nullable [n_rows, mask_ld] selection bitmask
   int64_t mask_ld;
-  // nullable (prefill with a bitmask): tile occupancy, one row per 32 query
-  // rows of a sequence ([B, occ_rows, occ_ld] words, zeroed beforehand); bit
-  // k of word w is set when some row of the group selects a key of key tile
-  // 32 w + k (64 keys per tile)
-  uint32_t* occ;
-  int64_t occ_ld;
-  int occ_rows;
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
+// Key-tile occupancy of a prefill bitmask ([B, n, mask_ld] words): one row of
+// occ_ld words per 32 query rows ([B, ceil(n/32), occ_ld]); bit k of word w
+// is set when some row of the group selects a key of key tile 32 w + k (64
+// keys per tile).
+hipError_t launch_mask_occupancy(const uint32_t* mask, int64_t mask_ld, int B, int n, uint32_t* occ, int64_t occ_ld,
+                                 hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // gathered GQA softmax attention over selected rows, split + combine + gate
