@@ -139,9 +139,13 @@ __global__ __launch_bounds__(256) void k_mask_occupancy(const uint32_t* mask, in
   uint32_t* ob = occ + ((size_t)b * groups + grp) * occ_ld;
   for (int ow = wave; ow < occ_ld; ow += 4) {
     const int w = 64 * ow + lane;
+    // the group's 32 rows at once: one memory round trip per occupancy word
+    uint32_t v[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) v[r] = (w < words && r < r1 - r0) ? mb[(size_t)r * mask_ld + w] : 0u;
     uint32_t acc = 0;
-    if (w < words)
-      for (int r = 0; r < r1 - r0; ++r) acc |= mb[(size_t)r * mask_ld + w];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) acc |= v[r];
     uint64_t nz = __builtin_amdgcn_ballot_w64(acc != 0u);
     nz = (nz | (nz >> 1)) & 0x5555555555555555ull;  // bit 2t: tile t occupied; compact to bit t
     nz = (nz | (nz >> 1)) & 0x3333333333333333ull;
