@@ -110,6 +110,8 @@ typedef struct lisa_shape {
   int32_t dtype;    /* LISA_F32 or LISA_BF16                                     */
   uint32_t flags;   /* LISA_LINEAR_UNNORMALIZED | LISA_SLIDING_WINDOW, or 0      */
 } lisa_shape;
+/* Counts beyond B = 65536, cap or M = 2^26, hidden = 2^20, H_q or H_I = 1024
+ * or d_I = 4096 are rejected with LISA_ERR_UNSUPPORTED. */
 
 /*
  * Bytes of workspace an operation needs.  `n` is the prefill length (tokens
@@ -251,7 +253,7 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n,
  * state.  mean_S, mean_z: in, the mean direction of segments 1..t-1 (not
  * read when t == 1); out, of segments 1..t.  t >= 1 counts segments of k
  * tokens; the caller calls this after every k tokens (decode steps or
- * prefill chunks).  d must be a multiple of 4.  Nothing is allocated; the
+ * prefill chunks); alpha must be finite.  d must be a multiple of 4.  Nothing is allocated; the
  * call is asynchronous on `stream`.
  */
 int lisa_segment_correct(const lisa_shape* shape, float* S, float* z, float* S_start, float* z_start,

@@ -65,6 +65,12 @@ int check_shape(const lisa_shape* s, Shape& o) {
   if (s->B < 1 || s->H_q < 1 || s->H_kv < 1 || s->d < 1 || s->H_I < 1 || s->H_Ik < 1 || s->d_I < 1 ||
       s->H_L < 1 || s->hidden < 1 || s->M < 1 || s->cap < 1)
     return fail(LISA_ERR_INVALID_ARG, "every count must be >= 1");
+  // upper bounds that keep every size and index computation of the library
+  // inside its integer types
+  if (s->B > (1 << 16) || s->cap > (1 << 26) || s->M > (1 << 26) || s->hidden > (1 << 20) || s->H_q > (1 << 10) ||
+      s->H_I > (1 << 10) || s->d_I > (1 << 12))
+    return fail(LISA_ERR_UNSUPPORTED, "a count is too large (B <= 65536, cap and M <= 2^26, hidden <= 2^20, "
+                                      "H_q and H_I <= 1024, d_I <= 4096)");
   if (s->H_q % s->H_kv) return fail(LISA_ERR_INVALID_ARG, "H_q %% H_kv != 0");
   if (s->H_I % s->H_Ik) return fail(LISA_ERR_INVALID_ARG, "H_I %% H_Ik != 0");
   if (s->H_L != s->H_q) return fail(LISA_ERR_INVALID_ARG, "H_L (%d) must equal H_q (%d)", s->H_L, s->H_q);
@@ -358,6 +364,11 @@ int decode_step(const Shape& sh, const int32_t* seq_lens, const void* q, const v
                 const void* x, const void* w_gate, const float* w_idx, void* k_cache, void* v_cache,
                 void* k_idx_cache, float* S, float* z, void* out, int32_t* idx_out, void* ws, size_t ws_bytes,
                 void* stream);
+int decode_check_pointers(const Shape& sh, const int32_t* seq_lens, const void* q, const void* k_new,
+                          const void* v_new, const void* q_idx, const void* k_idx_new, const void* q_lin,
+                          const void* k_lin, const void* v_lin, const void* x, const void* w_gate,
+                          const float* w_idx, void* k_cache, void* v_cache, void* k_idx_cache, float* S, float* z,
+                          void* out, int32_t* idx_out);
 
 }  // namespace
 
@@ -467,6 +478,10 @@ int lisa_decode_step_noalloc(const lisa_shape* shape, const int32_t* seq_lens, c
                 "this shape needs %zu bytes of decode workspace; the allocation-free decode step holds %zu "
                 "(use lisa_decode_step with a caller workspace)",
                 need, (size_t)LISA_DECODE_SCRATCH_BYTES);
+  // every host-side check before the first HIP call
+  if ((rc = decode_check_pointers(sh, seq_lens, q, k_new, v_new, q_idx, k_idx_new, q_lin, k_lin, v_lin, x, w_gate,
+                                  w_idx, k_cache, v_cache, k_idx_cache, S, z, out, idx_out)))
+    return rc;
   void* ws = nullptr;
   if ((rc = decode_scratch(ws))) return rc;
   return decode_step(sh, seq_lens, q, k_new, v_new, q_idx, k_idx_new, q_lin, k_lin, v_lin, x, w_gate, w_idx,
@@ -476,6 +491,23 @@ int lisa_decode_step_noalloc(const lisa_shape* shape, const int32_t* seq_lens, c
 }  // extern "C"
 
 namespace {
+
+// The decode step's tensor arguments: present and 16-byte aligned (the
+// indexer's only outside the sliding-window mode).
+int decode_check_pointers(const Shape& sh, const int32_t* seq_lens, const void* q, const void* k_new,
+                          const void* v_new, const void* q_idx, const void* k_idx_new, const void* q_lin,
+                          const void* k_lin, const void* v_lin, const void* x, const void* w_gate,
+                          const float* w_idx, void* k_cache, void* v_cache, void* k_idx_cache, float* S, float* z,
+                          void* out, int32_t* idx_out) {
+  REQUIRE_PTR(seq_lens); REQUIRE_PTR(q); REQUIRE_PTR(k_new); REQUIRE_PTR(v_new);
+  REQUIRE_PTR(q_lin); REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(x);
+  REQUIRE_PTR(w_gate); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(out); OPTIONAL_PTR(idx_out);
+  if (!(sh.flags & LISA_SLIDING_WINDOW)) {
+    REQUIRE_PTR(q_idx); REQUIRE_PTR(k_idx_new); REQUIRE_PTR(w_idx); REQUIRE_PTR(k_idx_cache);
+  }
+  return LISA_OK;
+}
 
 // The decode step after shape validation: pointer checks, then the launches
 // on the workspace `ws` (caller-owned, or the static scratch).
@@ -490,13 +522,9 @@ int decode_step(const Shape& sh, const int32_t* seq_lens, const void* q, const v
   // but neither scores nor selects, and attends to positions 0 .. L-1 as the
   // window path does (a window of M >= L is the whole prefix).
   const bool take_all = !window && sh.M >= sh.max_len;
-  REQUIRE_PTR(seq_lens); REQUIRE_PTR(q); REQUIRE_PTR(k_new); REQUIRE_PTR(v_new);
-  REQUIRE_PTR(q_lin); REQUIRE_PTR(k_lin); REQUIRE_PTR(v_lin); REQUIRE_PTR(x);
-  REQUIRE_PTR(w_gate); REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache);
-  REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(out); OPTIONAL_PTR(idx_out);
-  if (!window) {
-    REQUIRE_PTR(q_idx); REQUIRE_PTR(k_idx_new); REQUIRE_PTR(w_idx); REQUIRE_PTR(k_idx_cache);
-  }
+  int prc = decode_check_pointers(sh, seq_lens, q, k_new, v_new, q_idx, k_idx_new, q_lin, k_lin, v_lin, x, w_gate,
+                                  w_idx, k_cache, v_cache, k_idx_cache, S, z, out, idx_out);
+  if (prc) return prc;
   REQUIRE_PTR(ws);
   const DecodeWs w = decode_ws(sh);
   if (ws_bytes < w.total) return fail(LISA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
@@ -689,7 +717,7 @@ int lisa_segment_correct(const lisa_shape* shape, float* S, float* z, float* S_s
   int rc = check_shape(shape, sh);
   if (rc) return rc;
   if (t < 1) return fail(LISA_ERR_INVALID_ARG, "segment number %d (must be >= 1)", t);
-  if (!(alpha == alpha)) return fail(LISA_ERR_INVALID_ARG, "alpha is NaN");
+  if (!(fabsf(alpha) < INFINITY)) return fail(LISA_ERR_INVALID_ARG, "alpha is not finite");
   REQUIRE_PTR(S); REQUIRE_PTR(z); REQUIRE_PTR(S_start); REQUIRE_PTR(z_start); REQUIRE_PTR(mean_S);
   REQUIRE_PTR(mean_z);
   if (sh.d % 4) return fail(LISA_ERR_UNSUPPORTED, "head dim %d is not a multiple of 4", sh.d);
