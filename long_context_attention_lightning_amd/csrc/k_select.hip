@@ -28,14 +28,16 @@
 #include "lisa_select.h"
 
 namespace lisa {
-// Row t of sequence b (decode: t = 0).
-template <int THREADS, int ITEMS, bool LKEYS>
+// Row t of sequence b (decode: t = 0).  RANKS: the launch writes index
+// lists (a.idx), which need each selected position's rank; without them
+// only the selection bitmask is written.
+template <int THREADS, int ITEMS, bool LKEYS, bool RANKS = true>
 __device__ __forceinline__ void select_one(const SelectArgs& a, int b, int t, SelShared<THREADS / WAVE>& sm,
                                            KeyStore<THREADS, ITEMS, LKEYS>& ks) {
   const size_t r = (size_t)b * a.rows_per_seq + t;
   const int M = a.M;
   const int tid = threadIdx.x;
-  int32_t* orow = a.idx ? a.idx + (size_t)r * a.idx_ld : nullptr;  // null: bitmask only
+  int32_t* orow = (RANKS && a.idx) ? a.idx + (size_t)r * a.idx_ld : nullptr;  // null: bitmask only
   uint32_t* mrow = a.mask ? a.mask + (size_t)r * a.mask_ld : nullptr;
   // Decode rows always exist and are read up to max_len while the length is
   // still on its way; prefill rows of at most M positions are not stored
@@ -51,7 +53,7 @@ __device__ __forceinline__ void select_one(const SelectArgs& a, int b, int t, Se
   }
   const float* srow = a.scores + ((size_t)b * a.stored_rows + (a.prefill ? max(t - a.first_row, 0) : 0)) * a.ld;
   SelResult<ITEMS> res;
-  select_row<THREADS, ITEMS, LKEYS>(srow, len, M, sm, ks, ld, res);
+  select_row<THREADS, ITEMS, LKEYS, RANKS>(srow, len, M, sm, ks, ld, res);
   if (orow) for_each_selected<THREADS, ITEMS>(res, [&](uint32_t rank, int pos) { if (rank < (uint32_t)M) orow[rank] = pos; });
   if (mrow) {
     // eight consecutive lanes hold the 32 positions of one mask word
@@ -86,7 +88,8 @@ __global__ __launch_bounds__(THREADS) void k_select(SelectArgs a) {
 // short ones fill the tail of the launch.  Keys are recomputed from the
 // score row, so the block holds only the histogram and several blocks share
 // a CU.
-__global__ __launch_bounds__(256) void k_select_rows256(SelectArgs a) {
+template <bool RANKS>  // bitmask only: held to 128 registers, four blocks per CU
+__global__ __launch_bounds__(256, RANKS ? 1 : 4) void k_select_rows256(SelectArgs a) {
   __shared__ SelShared<256 / WAVE> sm;
   __shared__ KeyStore<256, 16, false> ks16;
   __shared__ KeyStore<256, 32, false> ks32;
@@ -102,9 +105,9 @@ __global__ __launch_bounds__(256) void k_select_rows256(SelectArgs a) {
     t = 0;
     len = a.seq_lens[b];
   }
-  if (len <= 256 * 16) select_one<256, 16, false>(a, b, t, sm, ks16);
-  else if (len <= 256 * 32) select_one<256, 32, false>(a, b, t, sm, ks32);
-  else select_one<256, 64, false>(a, b, t, sm, ks64);
+  if (len <= 256 * 16) select_one<256, 16, false, RANKS>(a, b, t, sm, ks16);
+  else if (len <= 256 * 32) select_one<256, 32, false, RANKS>(a, b, t, sm, ks32);
+  else select_one<256, 64, false, RANKS>(a, b, t, sm, ks64);
 }
 
 // Sliding-window index lists ([LISA] Section 3.2 Stage 1): row t gets the
@@ -170,7 +173,10 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.n_rows);
   // one 1024-thread block per row while the rows do not fill the chip
   const bool many = a.prefill || a.n_rows >= 512;
-  if (many && a.max_len > 256 * 16 && a.max_len <= 256 * 64) klaunch(k_select_rows256, grid, dim3(256), 0, st, a);
+  if (many && a.max_len > 256 * 16 && a.max_len <= 256 * 64) {
+    if (a.idx) klaunch(k_select_rows256<true>, grid, dim3(256), 0, st, a);
+    else klaunch(k_select_rows256<false>, grid, dim3(256), 0, st, a);  // bitmask only
+  }
   else if (a.max_len <= 256 * 16) klaunch((k_select<256, 16, true>), grid, dim3(256), 0, st, a);
   else if (a.max_len <= 1024 * 16) klaunch((k_select<1024, 16, true>), grid, dim3(1024), 0, st, a);
   else if (a.max_len <= 1024 * 32) klaunch((k_select<1024, 32, true>), grid, dim3(1024), 0, st, a);

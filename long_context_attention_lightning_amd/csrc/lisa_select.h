@@ -109,7 +109,7 @@ __device__ __forceinline__ int sel_group(int k) {
 // Result of select_row for one thread: bit i of `bits` says whether item i
 // is selected; rank0[k] is the number of selected positions before group k
 // of this lane, i.e. the rank (in ascending position order) of the group's
-// first selected position.
+// first selected position (left unset when the ranks are not asked for).
 template <int ITEMS>
 struct SelResult {
   uint64_t bits;
@@ -138,7 +138,7 @@ __device__ __forceinline__ void select_load(const float* srow, int reach, SelLoa
   ld.v0 = srow[0];
 }
 
-template <int THREADS, int ITEMS, bool LKEYS>
+template <int THREADS, int ITEMS, bool LKEYS, bool RANKS = true>
 __device__ __forceinline__ void select_row(const float* srow, int len, int M, SelShared<THREADS / WAVE>& sm,
                                            KeyStore<THREADS, ITEMS, LKEYS>& ks, const SelLoad<THREADS, ITEMS>& ld,
                                            SelResult<ITEMS>& res) {
@@ -318,6 +318,11 @@ __device__ __forceinline__ void select_row(const float* srow, int len, int M, Se
     }
   }
   selbits &= vmask;
+  if constexpr (!RANKS) {  // the caller wants the selection bits only
+    __syncthreads();
+    res.bits = selbits;
+    return;
+  }
   // ranks: prefix over lanes inside each 256-position group (ballots and
   // mbcnt), then over the groups in position order (group k * NW + wave)
   uint32_t excl[K4];

@@ -146,9 +146,22 @@ def test_prefill_fp32_shared_key_small_heads():
     _full_parity(cfg, prefill_inputs(cfg, n=300, salt=5), 40, "fp32 shared key")
 
 
-def test_prefill_scores_out_and_topk_match_oracle():
-    cfg = QWEN7B_PREFILL_16K.replace(n=600, cap=600)
-    n, M = 600, 100
+SCORE_SHAPES = [
+    # (label, indexer heads, n): the streaming score kernel (query rows in
+    # registers, key tiles walked) for the first three; head shapes without a
+    # streaming instantiation take the per-head tile kernel
+    ("4 heads d64", dict(), 600),
+    ("4 heads d64, n=1500", dict(), 1500),
+    ("2 heads on 1 shared key d32", dict(H_I=2, H_Ik=1, d_I=32), 600),
+    ("4 heads on 2 keys d64", dict(H_I=4, H_Ik=2), 600),
+    ("8 heads d32", dict(H_I=8, H_Ik=8, d_I=32), 600),
+]
+
+
+@pytest.mark.parametrize("label,over,n", SCORE_SHAPES, ids=[s[0] for s in SCORE_SHAPES])
+def test_prefill_scores_out_and_topk_match_oracle(label, over, n):
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n, **over)
+    M = 100
     inp = prefill_inputs(cfg, n=n, salt=2)
     sh = shape_of(cfg, M=M, cap=n)
     T = tdtype(cfg)
@@ -167,7 +180,7 @@ def test_prefill_scores_out_and_topk_match_oracle():
         # the GPU selection of the GPU's own fp32 scores is exact
         exp = oracle.select_topm(sc_h[t, : t + 1].astype(np.float64), M)
         assert idx_h[t, : len(exp)].tolist() == exp.tolist(), t
-    print(f"[scores_out] worst rel err {worst:.3e}")
+    print(f"[scores_out {label}] worst rel err {worst:.3e}")
     assert worst < 1e-5
     assert recall(idx_h, res["idx"].values()) >= RECALL_MIN
 
