@@ -375,7 +375,7 @@ TRAFFIC_KERNELS = {
         "k_lin_seg_sums": ("prefill_linear_sums", ["k_linear_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
         "k_lin_seg_prefix": ("prefill_linear_prefix", ["k_linear_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
         "k_lin_chunks": ("prefill_linear", ["k_linear_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
-        "k_index_scores_mfma": ("prefill_index_scores", ["k_prefill_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+        "k_index_scores_stream": ("prefill_index_scores", ["k_prefill_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
         "k_select_rows256": ("topm_select", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
         "k_mask_occupancy": ("prefill_tile_occupancy", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
         "k_attn_prefill_mfma": ("prefill_attention", ["k_attn_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
