@@ -169,18 +169,27 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[D / 16], const SM& sm, i
   }
 }
 
-// Column sum of phi(K) over the staged chunk for dk = threadIdx.x (< D).
+// Column sums of phi(K) over the staged chunk, shared by every wave: wave w
+// sums dk rows 16 w .. 16 w + 15, lane l row 16 w + l % 16 over the 16 tokens
+// of quarter l / 16; the quarters are then added across lanes.  Lanes 0..15
+// return the sum of row ksum_row(wave, lane) (other lanes: partial values).
+__device__ __forceinline__ int ksum_row(int wave, int lane) { return 16 * wave + (lane & 15); }
+
 template <int D, typename SM>
-__device__ __forceinline__ float chunk_ksum(const SM& sm, int dk) {
+__device__ __forceinline__ float chunk_ksum(const SM& sm, int wave, int lane) {
+  static_assert(D / LinCfg<D>::W == 16, "16 rows per wave");
+  const int dk = ksum_row(wave, lane), c0 = 16 * (lane >> 4);
   float acc = 0.f;
 #pragma unroll
-  for (int c = 0; c < LC; c += 8) {
+  for (int c = 0; c < 16; c += 8) {
     float h[8], l[8];
-    Vec<bf16_t>::load(&sm.kt_hi[dk][c], h);
-    Vec<bf16_t>::load(&sm.kt_lo[dk][c], l);
+    Vec<bf16_t>::load(&sm.kt_hi[dk][c0 + c], h);
+    Vec<bf16_t>::load(&sm.kt_lo[dk][c0 + c], l);
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc += h[u] + l[u];
   }
+  acc += __shfl_xor(acc, 16, WAVE);
+  acc += __shfl_xor(acc, 32, WAVE);
   return acc;
 }
 
@@ -215,7 +224,8 @@ __global__ __launch_bounds__(LinCfg<D>::T) void k_lin_seg_sums(LinearChunkArgs a
   for (int p = 0; p < D / 16; ++p)
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[p][r] = a.in_place ? Sg[tile_off(D, p, wave, lane, r)] : 0.f;
-  float zacc = (a.in_place && tid < D) ? a.z[(size_t)bh * D + tid] : 0.f;
+  const int zrow = ksum_row(wave, lane);  // lanes 0..15 keep z of this row
+  float zacc = (a.in_place && lane < 16) ? a.z[(size_t)bh * D + zrow] : 0.f;
 
   ChunkRegs<D, false> cr;
   if (t_begin < t_end) chunk_load<D, false>(cr, nullptr, kb, vb, tok_stride, t_begin, a.n);
@@ -225,16 +235,16 @@ __global__ __launch_bounds__(LinCfg<D>::T) void k_lin_seg_sums(LinearChunkArgs a
     __syncthreads();
     if (t0 + LC < t_end) chunk_load<D, false>(cr, nullptr, kb, vb, tok_stride, t0 + LC, a.n);
     state_update<D>(S, sm, wave);
-    if (tid < D) zacc += chunk_ksum<D>(sm, tid);
+    zacc += chunk_ksum<D>(sm, wave, lane);
   }
   float* dst = a.in_place ? Sg : a.seg_state + ((size_t)bh * a.nseg + seg) * (D * D + D);
 #pragma unroll
   for (int p = 0; p < D / 16; ++p)
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[tile_off(D, p, wave, lane, r)] = S[p][r];
-  if (tid < D) {
-    if (a.in_place) a.z[(size_t)bh * D + tid] = zacc;
-    else dst[D * D + tid] = zacc;
+  if (lane < 16) {
+    if (a.in_place) a.z[(size_t)bh * D + zrow] = zacc;
+    else dst[D * D + zrow] = zacc;
   }
 }
 
@@ -334,26 +344,32 @@ __global__ __launch_bounds__(LinCfg<D>::T) void k_lin_chunks(LinearChunkArgs a) 
     for (int r = 0; r < 4; ++r) rsum[r] = group_sum(rsum[r], 16);
     if (r16 < 4)
       sm.rs[sub][16 * ib + 4 * g + r16] = r16 == 0 ? rsum[0] : r16 == 1 ? rsum[1] : r16 == 2 ? rsum[2] : rsum[3];
-    if (sub == WPI - 1) {  // phi(q) . z for the 16 rows of block ib
+    {
+      // phi(q) . z, every wave for LC / W rows: lane l takes 16 dims of row
+      // LC / W * wave + l / SL, the SL lanes of a row are then summed
+      constexpr int RPW = LC / LinCfg<D>::W, SL = WAVE / RPW;
+      static_assert(D / SL == 16, "16 dims per lane");
+      const int i = RPW * wave + lane / SL, c0 = 16 * (lane % SL);
       float qz = 0.f;
-      const int i = 16 * ib + r16;
 #pragma unroll
-      for (int c = 0; c < D / 4; c += 8) {
+      for (int c = 0; c < 16; c += 8) {
         float qf[8];
-        Vec<bf16_t>::load(&sm.q[i][(D / 4) * g + c], qf);
+        Vec<bf16_t>::load(&sm.q[i][c0 + c], qf);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) qz = fmaf(qf[u], sm.z[zc][(D / 4) * g + c + u], qz);
+        for (int u = 0; u < 8; ++u) qz = fmaf(qf[u], sm.z[zc][c0 + c + u], qz);
       }
-      qz += __shfl_xor(qz, 16, WAVE);
-      qz += __shfl_xor(qz, 32, WAVE);
-      if (g == 0) sm.rs[WPI][i] = qz;
+#pragma unroll
+      for (int o = 1; o < SL; o <<= 1) qz += __shfl_xor(qz, o, WAVE);
+      if (lane % SL == 0) sm.rs[WPI][i] = qz;
     }
     __syncthreads();  // A and the row sums complete
 
-    // num = A V + phi(Q) S for every query block, the wave's dv block.  S
-    // enters as the B operand straight from the accumulator: lane (r16, g)
-    // holds dk rows 32 pp + 4 g + r and 32 pp + 16 + 4 g + r of column
-    // r16, so phi(Q) is read in that same contraction order.
+    // num^T = V^T A^T + S^T phi(Q)^T for every query block, the wave's dv
+    // block: the operands of num = A V + phi(Q) S in swapped MFMA order, so
+    // that a lane ends up with four consecutive dv columns of one query row
+    // (one float4 store).  S enters straight from the accumulator: lane
+    // (r16, g) holds dk rows 32 pp + 4 g + r and 32 pp + 16 + 4 g + r of
+    // column r16, so phi(Q) is read in that same contraction order.
     uint4 shi[D / 32], slo[D / 32];
 #pragma unroll
     for (int pp = 0; pp < D / 32; ++pp) {
@@ -373,40 +389,35 @@ __global__ __launch_bounds__(LinCfg<D>::T) void k_lin_chunks(LinearChunkArgs a) 
         if (s == 1 && ibq < 2) break;
         const bf16x8 aa = as_bf16x8(lds_read16(&sm.a[16 * ibq + r16][32 * s + 8 * g]));
         const bf16x8 vv = as_bf16x8(lds_read16(&sm.vt[16 * wave + r16][32 * s + 8 * g]));
-        num = mfma16(aa, vv, num);
+        num = mfma16(vv, aa, num);  // [dv][query]
       }
 #pragma unroll
       for (int pp = 0; pp < D / 32; ++pp) {
         const uint2 x0 = *reinterpret_cast<const uint2*>(&sm.q[16 * ibq + r16][32 * pp + 4 * g]);
         const uint2 x1 = *reinterpret_cast<const uint2*>(&sm.q[16 * ibq + r16][32 * pp + 16 + 4 * g]);
         const bf16x8 qa = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
-        num = mfma16(qa, as_bf16x8(shi[pp]), num);
-        num = mfma16(qa, as_bf16x8(slo[pp]), num);
+        num = mfma16(as_bf16x8(shi[pp]), qa, num);
+        num = mfma16(as_bf16x8(slo[pp]), qa, num);
       }
-      // outputs of rows 16 ibq + 4 g + r
-      const int i0 = 16 * ibq + 4 * g;
-      float4 den = *reinterpret_cast<const float4*>(&sm.rs[WPI][i0]);
+      // lane holds row i = 16 ibq + r16, dv columns 16 wave + 4 g .. + 3
+      const int i = 16 * ibq + r16;
+      const int t = t0 + i;
+      float den = sm.rs[WPI][i];
 #pragma unroll
-      for (int u = 0; u < WPI; ++u) {
-        const float4 x = *reinterpret_cast<const float4*>(&sm.rs[u][i0]);
-        den.x += x.x;
-        den.y += x.y;
-        den.z += x.z;
-        den.w += x.w;
-      }
-      const float dd[4] = {den.x, den.y, den.z, den.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + i0 + r;
-        if (t < t_end) {
-          const float inv = normalized ? __builtin_amdgcn_rcpf(dd[r]) : 1.f;
-          a.o_lin[((size_t)b * a.n + t) * tok_stride + (size_t)h * D + 16 * wave + r16] = num[r] * inv;
-        }
+      for (int u = 0; u < WPI; ++u) den += sm.rs[u][i];
+      if (t < t_end) {
+        const float inv = normalized ? __builtin_amdgcn_rcpf(den) : 1.f;
+        *reinterpret_cast<float4*>(a.o_lin + ((size_t)b * a.n + t) * tok_stride + (size_t)h * D + 16 * wave + 4 * g) =
+            make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
       }
     }
     // state and normaliser after the chunk
     state_update<D>(S, sm, wave);
-    if (tid < D) sm.z[zc ^ 1][tid] = sm.z[zc][tid] + chunk_ksum<D>(sm, tid);
+    {
+      const float ks = chunk_ksum<D>(sm, wave, lane);
+      const int dk = ksum_row(wave, lane);
+      if (lane < 16) sm.z[zc ^ 1][dk] = sm.z[zc][dk] + ks;
+    }
     zc ^= 1;
   }
 }
