@@ -199,8 +199,9 @@ int lisa_decode_step_noalloc(const lisa_shape* shape, const int32_t* seq_lens,
  * events, so the call keeps the ordering of `stream` and can be captured in
  * a graph.  The library creates one side stream and two events per device
  * and caller stream on the first call outside a capture, and keeps them
- * until the process ends.  Without one (the first call made inside a
- * capture, sliding-window mode), everything runs on `stream`.
+ * until the process ends; it creates at most 32 such pairs in a process.
+ * Without one (the first call made inside a capture, more than 32 caller
+ * streams, sliding-window mode), everything runs on `stream`.
  */
 int lisa_prefill(const lisa_shape* shape, int32_t n,
                  const void* q, const void* k_cache, const void* v_cache,

@@ -264,9 +264,13 @@ template <typename P> P* at(void* ws, size_t off) { return reinterpret_cast<P*>(
 // stream (default priority, non-blocking) that joins back before the
 // attention, so they overlap the indexer and the select.  One side stream
 // and event pair per (device, caller stream), created on first use outside
-// a graph capture; while none exists (or creation fails) the work stays on
-// the caller's stream.
+// a graph capture and kept until the process ends; at most
+// kMaxSideStreams of them exist.  While none exists for a caller stream
+// (table full, capture, or creation failed) the work stays on the caller's
+// stream, which changes the timing only.
 // ---------------------------------------------------------------------------
+constexpr size_t kMaxSideStreams = 32;
+
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
@@ -280,6 +284,7 @@ SideStream* side_stream(hipStream_t caller) {
   std::lock_guard<std::mutex> lock(mu);
   auto it = table.find({dev, caller});
   if (it != table.end()) return &it->second;
+  if (table.size() >= kMaxSideStreams) return nullptr;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
   SideStream ss;
