@@ -97,8 +97,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   const int r16 = lane & 15, g = lane >> 4;
   // Work units are (query tile of AQ rows, head of the KV group) pairs,
   // numbered head-fastest from the last query tile down; block k takes
-  // units 4k .. 4k + 3, one per wave (at most two adjacent query tiles, so
-  // the staged K/V tiles serve every wave), longest causal rows first.
+  // units 4k .. 4k + 3, one per wave (adjacent query tiles: at most two for
+  // GQA groups of two or more heads, four for one; the staged K/V tiles
+  // serve every wave), longest causal rows first.
   const int nqt = (n + AQ - 1) / AQ;
   const int units = nqt * G;
   const int per = sh.B * sh.H_kv;
@@ -125,23 +126,30 @@ __global__ __launch_bounds__(256, 2) void k_attn_prefill_mfma(AttnMaskArgs a) { 
   const int nkt = tmax / AK + 1;
 
   // The key tiles to walk: from kt0 in window mode; otherwise the tiles in
-  // which some row of the block's (at most two) query tiles selects a key,
-  // as the select kernel recorded them.  For spread-out selections that is
-  // every causal tile; clustered ones (recent keys, sinks) skip the rest.
+  // which some row of the block's query tiles selects a key, as the
+  // occupancy pass recorded them per group of 32 query rows.  For
+  // spread-out selections that is every causal tile; clustered ones (recent
+  // keys, sinks) skip the rest.  The block's rows are groups g_lo .. g_hi:
+  // two groups for GQA groups of two or more heads, four with one head.
   int count = 0;
   {
-    const uint32_t* occ_hi = nullptr;
-    const uint32_t* occ_lo = nullptr;
+    const uint32_t* occ_b = nullptr;
+    int g_lo = 0, g_hi = -1;
     if (!a.window && a.occ) {
-      const size_t occ_rows = (size_t)(n + AQ - 1) / AQ;
+      const int occ_rows = (n + 31) / 32;
       const int T0_high = (nqt - 1 - (4 * kblk) / G) * AQ;
-      occ_hi = a.occ + ((size_t)b * occ_rows + T0_high / AQ) * a.occ_ld;
-      occ_lo = a.occ + ((size_t)b * occ_rows + T0_low / AQ) * a.occ_ld;
+      g_lo = T0_low / 32;
+      g_hi = min((T0_high + AQ - 1) / 32, occ_rows - 1);
+      occ_b = a.occ + (size_t)b * occ_rows * a.occ_ld;
     }
     for (int base = 0; base < nkt; base += 256) {
       const int tile = base + tid;
       bool on = tile < nkt && tile >= kt0;
-      if (on && occ_hi) on = ((occ_hi[tile >> 5] | occ_lo[tile >> 5]) >> (tile & 31)) & 1u;
+      if (on && occ_b) {
+        uint32_t w = 0u;
+        for (int gq = g_lo; gq <= g_hi; ++gq) w |= occ_b[(size_t)gq * a.occ_ld + (tile >> 5)];
+        on = (w >> (tile & 31)) & 1u;
+      }
       const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
       if (lane == 0) tile_count[wave] = __builtin_popcountll(bal);
       __syncthreads();

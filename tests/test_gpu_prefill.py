@@ -103,15 +103,21 @@ def test_prefill_bf16_offset_fallback():
     _full_parity(cfg, inp, M, "offset fallback")
 
 
-def test_prefill_clustered_selection():
+@pytest.mark.parametrize("heads", [dict(), dict(H_q=4, H_kv=4, H_L=4)], ids=["gqa7", "mha"])
+def test_prefill_clustered_selection(heads):
     """Selections clustered in a few key tiles: a sink tile [0, 64) and a band
     [640, 704) score positive for every query, every other key scores 0, and
     the select breaks the ties at 0 toward the larger position, so each row
     takes the two clusters plus its most recent keys.  Most key tiles are
     then selected by no row of a block; the attention skips them and must
-    still match the oracle on every sampled row."""
+    still match the oracle on every sampled row.  Rows [1696, 1760) also
+    score a third cluster [1280, 1344) above the other two, which no row
+    within 32 rows of that band selects.  With one query head per KV head
+    (mha) an attention block spans four query tiles of 32 rows, and for the
+    block of rows [1664, 1792) only its two middle tiles select that
+    cluster's key tile, which it must still walk."""
     n, M = 2048, 256
-    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n, M=M)
+    cfg = QWEN7B_PREFILL_16K.replace(n=n, cap=n, M=M, **heads)
     inp = prefill_inputs(cfg, n=n, salt=58)
     from lisa_inputs import round_bf16
     q_idx = np.zeros_like(inp["q_idx"])
@@ -120,13 +126,21 @@ def test_prefill_clustered_selection():
     for lo, hi in ((0, 64), (640, 704)):
         j = np.arange(lo, hi)
         k_idx[:, lo:hi, :, 0] = (1.0 + (j % 64) / 64.0)[None, :, None]  # distinct in bf16
+    band, third = (1696, 1760), (1280, 1344)
+    q_idx[:, band[0]:band[1], :, 1] = 1.0
+    k_idx[:, third[0]:third[1], :, 1] = 2.0  # scores 4.0 for the band's rows, above the others' < 4
     inp["q_idx"], inp["k_idx"] = q_idx, round_bf16(k_idx)
     inp["w_idx"] = np.full_like(inp["w_idx"], 0.5)
-    rows = [0, 63, 64, 255, 256, 300, 639, 640, 703, 704, 705, 831, 832, 1000, 1337, 1500, 2000, 2047]
+    rows = [0, 63, 64, 255, 256, 300, 639, 640, 703, 704, 705, 831, 832, 1000, 1337, 1500,
+            1663, 1664, 1695, 1696, 1700, 1727, 1759, 1760, 1791, 2000, 2047]
     ref = oracle.prefill_rows(inp, M, rows)
     clusters = set(range(64)) | set(range(640, 704))
-    for t in (1000, 2047):  # construction holds: both clusters, then the most recent keys
+    for t in (1000, 1695, 2047):  # construction holds: both clusters, then the most recent keys
         want = clusters | set(range(t - (M - len(clusters)) + 1, t + 1))
+        assert set(int(v) for v in ref["idx"][t]) == want, t
+    for t in (1700, 1759):  # the band: the third cluster too
+        c3 = clusters | set(range(*third))
+        want = c3 | set(range(t - (M - len(c3)) + 1, t + 1))
         assert set(int(v) for v in ref["idx"][t]) == want, t
     g = gpu_prefill(cfg, inp, M=M)
     for t in rows:
