@@ -17,6 +17,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # packed fp32 VALU ops are disabled for every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar kernel arguments (up to 16 dwords) are preloaded into
+    # SGPRs at wave launch instead of being read from the argument segment
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -25,8 +25,14 @@ namespace lisa {
 constexpr int FS_THREADS = 512;  // 8 waves: 256 registers per lane, no spills
 constexpr int FS_MAX_SPLIT = 64;  // positions per split
 
+// The values the block needs first come as leading scalar arguments, which
+// the compiler lets the hardware preload into SGPRs at wave launch (the
+// structs after them are read from the kernel-argument segment, a memory
+// round trip, while the score row is already on its way).
 template <typename T, int D, int GT, int ITEMS>
-__global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, SelectArgs sa) {
+__global__ __launch_bounds__(FS_THREADS) void k_select_attend(const float* scores, int64_t sld, const int32_t* seq_lens,
+                                                              int max_len, int nsplit, int H_kv, AttnArgs a,
+                                                              SelectArgs sa) {
   constexpr int NW = FS_THREADS / WAVE;
   constexpr bool MF = sizeof(T) == 2;  // bf16: MFMA split attention
   // splits of at most FS_MAX_SPLIT entries: two attending waves of 32
@@ -46,15 +52,15 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, Select
 
   const Shape& sh = a.sh;
   int blk = blockIdx.x;
-  const int s = blk % a.nsplit;
-  blk /= a.nsplit;
-  const int g = blk % sh.H_kv;
-  const int b = blk / sh.H_kv;  // decode: one row per sequence
+  const int s = blk % nsplit;
+  blk /= nsplit;
+  const int g = blk % H_kv;
+  const int b = blk / H_kv;  // decode: one row per sequence
   // the score row is read up to max_len while the sequence length loads
-  const float* srow = sa.scores + (size_t)b * sa.ld;
+  const float* srow = scores + (size_t)b * sld;
   RunLoad<ITEMS> ld;
-  run_load<FS_THREADS, ITEMS>(srow, sa.max_len, ld);
-  const int len = a.seq_lens[b];
+  run_load<FS_THREADS, ITEMS>(srow, max_len, ld);
+  const int len = seq_lens[b];
   const int M = sh.M;
   const int m = min(M, len);
   const int i0 = s * a.split_len;
@@ -87,16 +93,19 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(AttnArgs a, Select
   else attend_split<T, D, GT, FS_THREADS, 2>(a, b, g, s, len, i0, i1, pos_of, u.att);
 }
 
+#define FS_LEAD (const float*)sa.scores, (int64_t)sa.ld, (const int32_t*)a.seq_lens, sa.max_len, a.nsplit, a.sh.H_kv
+
 template <typename T, int D, int ITEMS>
 static hipError_t launch_fs_tdi(const AttnArgs& a, const SelectArgs& sa, dim3 grid, hipStream_t st) {
   const int G = a.sh.H_q / a.sh.H_kv;
-  if (G <= 2) klaunch((k_select_attend<T, D, 2, ITEMS>), grid, dim3(FS_THREADS), 0, st, a, sa);
-  else if (G <= 4) klaunch((k_select_attend<T, D, 4, ITEMS>), grid, dim3(FS_THREADS), 0, st, a, sa);
-  else if (G <= 5) klaunch((k_select_attend<T, D, 5, ITEMS>), grid, dim3(FS_THREADS), 0, st, a, sa);
-  else if (G <= 7) klaunch((k_select_attend<T, D, 7, ITEMS>), grid, dim3(FS_THREADS), 0, st, a, sa);
-  else klaunch((k_select_attend<T, D, 8, ITEMS>), grid, dim3(FS_THREADS), 0, st, a, sa);
+  if (G <= 2) klaunch((k_select_attend<T, D, 2, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  else if (G <= 4) klaunch((k_select_attend<T, D, 4, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  else if (G <= 5) klaunch((k_select_attend<T, D, 5, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  else if (G <= 7) klaunch((k_select_attend<T, D, 7, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  else klaunch((k_select_attend<T, D, 8, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
   return hipGetLastError();
 }
+#undef FS_LEAD
 
 template <typename T, int D>
 static hipError_t launch_fs_td(const AttnArgs& a, const SelectArgs& sa, dim3 grid, hipStream_t st) {
