@@ -379,6 +379,21 @@ TRAFFIC_KERNELS = {
         "k_select_rows256": ("topm_select", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
         "k_mask_occupancy": ("prefill_tile_occupancy", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
         "k_attn_prefill_mfma": ("prefill_attention", ["k_attn_mfma.hip", "lisa_mfma.h", "lisa_prefill.h"] + _COMMON),
+        "k_kl_mfma": ("indexer_kl", ["k_indexer_kl.hip", "lisa_mfma.h"] + _COMMON),
+        "k_kl_loss": ("indexer_kl_loss", ["k_indexer_kl.hip", "lisa_mfma.h"] + _COMMON),
+        "k_dropout_compact": ("candidate_dropout_compact", ["k_dropout.hip"] + _COMMON),
+        "k_dropout_gather": ("candidate_dropout_gather", ["k_dropout.hip"] + _COMMON),
+    },
+    # (a key "symbol|<N" or "symbol|>=N" would take only the dispatches of
+    # fewer / at least N work-items of a kernel that serves two steps)
+    "batched": {
+        "k_decode_phase_a": ("decode_phase_a", ["k_decode.hip", "lisa_attend.h", "lisa_mfma.h"] + _COMMON),
+        "k_select": ("topm_select", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
+        "k_attention": ("gather_attention", ["k_decode.hip", "lisa_attend.h", "lisa_mfma.h"] + _COMMON),
+        "k_attn_combine": ("attention_combine", ["k_decode.hip", "lisa_attend.h", "lisa_mfma.h"] + _COMMON),
+        "k_mass_logits_mfma": ("mass_logits", ["k_mass.hip", "lisa_mfma.h"] + _COMMON),
+        "k_select_rows256": ("mass_select", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
+        "k_mass_reduce": ("mass_reduce", ["k_mass.hip", "lisa_mfma.h"] + _COMMON),
     },
 }
 
@@ -386,6 +401,7 @@ TRAFFIC_KERNELS = {
 TRAFFIC_WORKLOAD = {
     "decode": "decode step, Qwen-7B-shaped layer, batch 1, 16384 tokens, M = 2048",
     "prefill": "causal prefill, Qwen-7B-shaped layer, 16384 tokens, M = 2048",
+    "batched": "decode step, Qwen-7B-shaped layer, batch 32, context lengths 4096..16384 (seeded), M = 2048",
 }
 
 
@@ -403,21 +419,31 @@ def write_traffic(leg, fetch_csv, write_csv):
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
-            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            key = (r["Dispatch_Id"], r["Kernel_Name"], int(r["Grid_Size"]))
             vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
         return vals
+
+    def selected(sel, kernel, grid):
+        sym, _, cond = sel.partition("|")
+        if not re.search(r"lisa::%s\b" % sym, kernel):
+            return False
+        if cond.startswith(">="):
+            return grid >= int(cond[2:])
+        if cond.startswith("<"):
+            return grid < int(cond[1:])
+        return True
 
     want = 256 << 20
     out = {}
     for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
         vals = per_kernel(path, counter)
         # the calibration copies: torch.mul(src, 1.0, out=dst) on 64 Mi floats
-        copies = [v for (d, k), v in vals.items() if "AUnaryFunctor<float, float, float" in k and v * 1024 > want / 4]
+        copies = [v for (d, k, _), v in vals.items() if "AUnaryFunctor<float, float, float" in k and v * 1024 > want / 4]
         if not copies:
             sys.exit(f"{path}: no calibration copy found (run with --copy-calibration)")
         factor = want / (1024.0 * float(np.median(copies)))
         for sym, (name, _) in TRAFFIC_KERNELS[leg].items():
-            got = [v for (d, k), v in vals.items() if re.search(r"lisa::%s\b" % sym, k)]
+            got = [v for (d, k, gs), v in vals.items() if selected(sym, k, gs)]
             if got:
                 out.setdefault(name, {})[counter] = (float(np.mean(got)), factor, len(got))
     path = os.path.join(ROOT, "profiles", "traffic.json")
