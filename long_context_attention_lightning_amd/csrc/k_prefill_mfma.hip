@@ -312,7 +312,7 @@ hipError_t launch_index_scores_mfma(const IndexScoreArgs& a, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // gate logits: W_g [hidden, H_q] is first transposed into [H_pad, hidden]
 // (H_pad = H_q rounded up to 16, zero rows) so that both MFMA operands are
-// 16-byte row reads; block = 64 rows, wave = 16 rows x H_pad heads.
+// 16-byte row reads; block = 16 rows x H_pad heads (below).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gate_transpose(GateArgs a) {
   const Shape& sh = a.sh;
@@ -323,49 +323,56 @@ __global__ __launch_bounds__(256) void k_gate_transpose(GateArgs a) {
   a.w_t[e] = h < sh.H_q ? ((const bf16_t*)a.w_gate)[(size_t)c * sh.H_q + h] : (bf16_t)0;
 }
 
+// Block = 16 rows; its four waves split the hidden dimension (wave w takes
+// the w-th quarter of the 32-wide contraction steps) so that four waves per
+// SIMD keep loads in flight, and their partial logits are summed in LDS.
 template <int NH>  // head tiles of 16
 __global__ __launch_bounds__(256) void k_gate_mfma(GateArgs a) {
+  __shared__ float red[4][16][16 * NH + 1];
   const Shape& sh = a.sh;
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const int r16 = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.x * 64 + 16 * wave;
-  if (row0 >= a.n_rows) return;
+  const int row0 = blockIdx.x * 16;
   const int row = min(row0 + r16, a.n_rows - 1);
   const bf16_t* x = (const bf16_t*)a.x + (size_t)row * sh.hidden + 8 * g;
   const bf16_t* w = a.w_t + (size_t)r16 * sh.hidden + 8 * g;
+  const int steps = sh.hidden / 32;
+  const int s0 = steps * wave / 4, s1 = steps * (wave + 1) / 4;
   f32x4 acc[NH];
 #pragma unroll
   for (int q = 0; q < NH; ++q) acc[q] = zero4();
-  int c = 0;
-  for (; c + 64 <= sh.hidden; c += 64) {  // two K steps per iteration, loads first
-    uint4 xv[2], wv[2][NH];
+  int st = s0;
+  for (; st + 4 <= s1; st += 4) {  // four contraction steps per iteration, loads first
+    uint4 xv[4], wv[4][NH];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      xv[s] = ld16(x + c + 32 * s);
+    for (int u = 0; u < 4; ++u) {
+      const int c = 32 * (st + u);
+      xv[u] = ld16(x + c);
 #pragma unroll
-      for (int q = 0; q < NH; ++q) wv[s][q] = ld16(w + (size_t)16 * q * sh.hidden + c + 32 * s);
+      for (int q = 0; q < NH; ++q) wv[u][q] = ld16(w + (size_t)16 * q * sh.hidden + c);
     }
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int q = 0; q < NH; ++q) acc[q] = mfma16(as_bf16x8(wv[s][q]), as_bf16x8(xv[s]), acc[q]);
+      for (int q = 0; q < NH; ++q) acc[q] = mfma16(as_bf16x8(wv[u][q]), as_bf16x8(xv[u]), acc[q]);
   }
-  for (; c < sh.hidden; c += 32) {
+  for (; st < s1; ++st) {
+    const int c = 32 * st;
     const uint4 xv = ld16(x + c);
 #pragma unroll
     for (int q = 0; q < NH; ++q)
       acc[q] = mfma16(as_bf16x8(ld16(w + (size_t)16 * q * sh.hidden + c)), as_bf16x8(xv), acc[q]);
   }
-  // lane holds logit[row0 + r16][h = 16 q + 4 g + r]
-  if (row0 + r16 < a.n_rows) {
-    float* o = a.gate_part + (size_t)(row0 + r16) * sh.H_q;
+  // lane holds the partial logit[row0 + r16][h = 16 q + 4 g + r]
 #pragma unroll
-    for (int q = 0; q < NH; ++q)
+  for (int q = 0; q < NH; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 16 * q + 4 * g + r;
-        if (h < sh.H_q) o[h] = acc[q][r];
-      }
+    for (int r = 0; r < 4; ++r) red[wave][r16][16 * q + 4 * g + r] = acc[q][r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * sh.H_q; e += 256) {
+    const int rr = e / sh.H_q, h = e % sh.H_q;
+    if (row0 + rr < a.n_rows)
+      a.gate_part[(size_t)(row0 + rr) * sh.H_q + h] = red[0][rr][h] + red[1][rr][h] + red[2][rr][h] + red[3][rr][h];
   }
 }
 
@@ -381,7 +388,7 @@ hipError_t launch_gate_transpose(const GateArgs& a, hipStream_t st) {
 
 hipError_t launch_gate_mfma(const GateArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.n_rows + 63) / 64));
+  const dim3 grid((unsigned)((a.n_rows + 15) / 16));
   switch ((a.sh.H_q + 15) / 16) {
     case 1: klaunch(k_gate_mfma<1>, grid, dim3(256), 0, st, a); break;
     case 2: klaunch(k_gate_mfma<2>, grid, dim3(256), 0, st, a); break;
