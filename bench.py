@@ -572,14 +572,15 @@ def main():
                    "indexer": f"{cfg.H_I}x{cfg.d_I}", "buffer_sets": args.nbuf},
         "roofline": roof,
         "cpu_baseline": cpu,
-        # the headline figures at top level (a reader that keeps only top-level
-        # keys still has them); every detail stays under "extra"
-        "decode": summary_decode(extra),
-        "prefill": summary_prefill(extra),
-        "batched_decode": summary_leg(extra.get("batched_decode")),
+        # every detail under "extra"; the headline figures at top level after it,
+        # so that they also end the line (a reader that keeps only the end of
+        # the output, or only top-level keys, still has them), the C1 step last
+        "extra": extra,
         "m_sweep_decode": {k: summary_leg(v) for k, v in (extra.get("m_sweep_decode") or {}).items()
                            if isinstance(v, dict)} or None,
-        "extra": extra,
+        "batched_decode": summary_leg(extra.get("batched_decode")),
+        "prefill": summary_prefill(extra),
+        "decode": summary_decode(extra),
     }
     print(json.dumps(rec), flush=True)
 
