@@ -25,7 +25,10 @@ struct SelShared {
 
 // Block-wide min of a and max of b (uniform results): one LDS slot per
 // wave, then every wave reduces the NW slots with lane-parallel reads.
-template <int NW>
+// TRAIL: end with a barrier, so that the slots may be rewritten at once
+// (without it, the caller must pass a barrier before sm.wa or sm.wb is
+// written again).
+template <int NW, bool TRAIL = true>
 __device__ __forceinline__ void block_min_max(SelShared<NW>& sm, uint32_t a, uint32_t b, uint32_t& mn,
                                               uint32_t& mx) {
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
@@ -38,11 +41,12 @@ __device__ __forceinline__ void block_min_max(SelShared<NW>& sm, uint32_t a, uin
   __syncthreads();
   mn = wave_min_u32(sm.wa[lane % NW]);
   mx = wave_max_u32(sm.wb[lane % NW]);
-  __syncthreads();
+  if constexpr (TRAIL) __syncthreads();
 }
 
 // Block-wide inclusive prefix sum in thread order, and the block total.
-template <int NW>
+// TRAIL as for block_min_max (for sm.wa).
+template <int NW, bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_incl_scan(SelShared<NW>& sm, uint32_t v, uint32_t& total) {
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
   const uint32_t inc = wave_incl_scan_u32(v);
@@ -51,14 +55,16 @@ __device__ __forceinline__ uint32_t block_incl_scan(SelShared<NW>& sm, uint32_t 
   const uint32_t wi = wave_incl_scan_u32(lane < NW ? sm.wa[lane] : 0u);  // prefix over wave totals
   const uint32_t all = rl(wi, NW - 1);
   const uint32_t before = wave == 0 ? 0u : __builtin_amdgcn_readlane((int)wi, wave - 1);
-  __syncthreads();
+  if constexpr (TRAIL) __syncthreads();
   total = all;
   return before + inc;
 }
 
 // Find the bin holding the need-th largest element (bins counted from the
 // top).  Thread t owns the NBINS / THREADS consecutive bins from t * that.
-template <int THREADS>
+// TRAIL: end with a barrier (without it, the caller must pass a barrier
+// before sm.found_*, sm.wa or sm.hist is written again).
+template <int THREADS, bool TRAIL = true>
 __device__ __forceinline__ void find_bin(SelShared<THREADS / WAVE>& sm, uint32_t need, uint32_t& bin,
                                          uint32_t& need_in, uint32_t& cnt) {
   constexpr int BPT = NBINS / THREADS;
@@ -71,7 +77,8 @@ __device__ __forceinline__ void find_bin(SelShared<THREADS / WAVE>& sm, uint32_t
     tot += h[i];
   }
   uint32_t all;
-  const uint32_t inc = block_incl_scan(sm, tot, all);
+  // the barrier below (found_*) also orders the scan's reads of sm.wa
+  const uint32_t inc = block_incl_scan<THREADS / WAVE, TRAIL>(sm, tot, all);
   uint32_t above = all - inc;  // elements in bins of higher threads
 #pragma unroll
   for (int i = BPT - 1; i >= 0; --i) {
@@ -86,7 +93,7 @@ __device__ __forceinline__ void find_bin(SelShared<THREADS / WAVE>& sm, uint32_t
   bin = sm.found_bin;
   need_in = sm.found_need;
   cnt = sm.found_cnt;
-  __syncthreads();
+  if constexpr (TRAIL) __syncthreads();
 }
 
 // Keys of the row: in LDS when the row fits (LKEYS), else recomputed from
@@ -455,8 +462,14 @@ __device__ __forceinline__ void select_row_runs(const float* srow, int len, int 
     fmx = fmaxf(fmx, sv[k]);
   }
   if (tid == 0) sm.cand_n = 0u;
+  // the histogram is cleared here; the min/max barrier orders it before
+  // the histogram pass
+#pragma unroll
+  for (int i = 0; i < NBINS / THREADS; ++i) sm.hist[tid + i * THREADS] = 0u;
   uint32_t lo, hi;  // key range of the boundary set
-  block_min_max(sm, score_key(fmn), score_key(fmx), lo, hi);
+  // no trailing barrier: with value bins, the next writes of sm.wa come
+  // after the histogram barrier; without, the barrier is taken below
+  block_min_max<THREADS / WAVE, false>(sm, score_key(fmn), score_key(fmx), lo, hi);
 
   // Boundary set: elements of value bin bsel (every element without the
   // value pass), narrowed later to keys in [lo, hi] and, once lo == hi,
@@ -472,16 +485,17 @@ __device__ __forceinline__ void select_row_runs(const float* srow, int len, int 
     const float inv_w = (float)NBINS / (vmax - vmin);
     if (lo != hi && inv_w > 0.f && inv_w < 1e30f) {
 #pragma unroll
-      for (int i = 0; i < NBINS / THREADS; ++i) sm.hist[tid + i * THREADS] = 0u;
-#pragma unroll
       for (int k = 0; k < ITEMS; ++k) bins[k] = min((uint32_t)((sv[k] - vmin) * inv_w), (uint32_t)(NBINS - 1));
-      __syncthreads();
 #pragma unroll
       for (int k = 0; k < ITEMS; ++k)
         if (k < nval) atomicAdd(&sm.hist[bins[k]], 1u);
       __syncthreads();
-      find_bin<THREADS>(sm, need, bsel, need, cnt);
+      // no trailing barriers: sm.found_*, sm.wa and sm.hist are written
+      // again only after later barriers (the boundary gather's, the
+      // narrowing histogram's, the final scan's)
+      find_bin<THREADS, false>(sm, need, bsel, need, cnt);
     } else {
+      __syncthreads();  // the min/max slots are read before they can be rewritten
 #pragma unroll
       for (int k = 0; k < ITEMS; ++k) bins[k] = 0u;
     }
@@ -591,7 +605,9 @@ __device__ __forceinline__ void select_row_runs(const float* srow, int len, int 
   selbits &= vmask;
   const uint32_t nsel = (uint32_t)__builtin_popcountll(selbits);
   uint32_t total;
-  uint32_t o = block_incl_scan(sm, nsel, total) - nsel;
+  // no trailing barrier: the callers write no shared selection state
+  // before their own barrier
+  uint32_t o = block_incl_scan<THREADS / WAVE, false>(sm, nsel, total) - nsel;
   selbits_out = selbits;
   o_out = o;
   p0_out = p0;
