@@ -161,9 +161,16 @@ hipError_t launch_select_runs(const SelectArgs& sa, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Every block of the fused launch selects its whole row, and its LDS (the
+// key store alone is 64 KB) holds it to one block per CU, so the launch pays
+// off only while all its blocks run at once: at most one per CU of the
+// MI355X (256).  A second wave of blocks would repeat the select; the
+// separate select and gather launches take over there.
+constexpr size_t FS_MAX_BLOCKS = 256;
+
 bool select_attend_supported(const Shape& sh, int nsplit, int split_len) {
   return sh.max_len <= FS_THREADS * 64 && split_len <= FS_MAX_SPLIT && nsplit <= AT_MAX_SPLITS &&
-         (size_t)sh.B * sh.H_kv * nsplit <= 512;
+         (size_t)sh.B * sh.H_kv * nsplit <= FS_MAX_BLOCKS;
 }
 
 hipError_t launch_select_attend(const AttnArgs& a, const SelectArgs& sa, hipStream_t st) {

@@ -120,7 +120,7 @@ def decode_select_core(B, H_kv, d, M, max_len):
     the fused select + attention launch, few sequences with rows of up to
     32K) or 'general' (the separate select launch)."""
     sl, ns = decode_split(min(M, max_len), B, H_kv)
-    if max_len <= 32768 and sl <= 64 and ns <= 32 and B * H_kv * ns <= 512:
+    if max_len <= 32768 and sl <= 64 and ns <= 32 and B * H_kv * ns <= 256:
         return "runs"
     return "general"
 
