@@ -1,7 +1,7 @@
 // Fused top-M selection and gathered attention for decode steps of a few
-// sequences ("LISA", arXiv 2607.19358v1, Section 3.2 Stage 2: select the M
-// positions with the largest summed indexer score, then softmax attention
-// over those cached rows).
+// sequences ("LISA", arXiv 2607.19358v1, Section 3.2 Stage 2: each query
+// keeps the M cached positions that score highest under the indexer, its
+// heads' scores added, and softmax attention runs over those rows only).
 //
 // With one or a few sequences a separate select kernel runs one block per
 // row: one CU has to pull the whole score row in, at the rate its own memory

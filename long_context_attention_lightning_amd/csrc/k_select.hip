@@ -1,5 +1,6 @@
 // Top-M selection of indexer score rows ("LISA", arXiv 2607.19358v1,
-// Section 3.2 Stage 2: the M positions with the largest summed score).
+// Section 3.2 Stage 2: per query, the M positions ranked highest by the
+// indexer score summed over its heads).
 //
 // One block per row; each thread keeps the scores of its run of ITEMS
 // consecutive positions in registers.  The order is (score descending,

@@ -1,7 +1,8 @@
 """Bit-exact top-M selection by each of the library's two select cores,
 fed the oracle's fp32 score rows ("LISA", arXiv 2607.19358v1, Section 3.2
-Stage 2: the M positions with the largest summed indexer score; ties to the
-later position, -0.0 equal to +0.0, ascending output, -1 padding).
+Stage 2: per query the M positions ranked highest by the head-summed indexer
+score; ties to the later position, -0.0 equal to +0.0, ascending output, -1
+padding).
 
 The decode step selects with the core its shape routes to: the core inside
 the fused select + attention launch ('runs': thread-contiguous runs, keys
