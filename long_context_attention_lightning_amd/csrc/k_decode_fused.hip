@@ -23,20 +23,27 @@
 namespace lisa {
 
 constexpr int FS_THREADS = 512;  // 8 waves: 256 registers per lane, no spills
-constexpr int FS_MAX_SPLIT = 64;  // positions per split
+constexpr int FS_MAX_SPLIT = 64;  // positions per split: two attending waves of 32
+// Wide splits (bf16, head dim 128): up to 512 positions, every wave attends
+// (32 entries per wave and round), for launches that would need more than one
+// block per CU with 64-position splits.
+constexpr int FS_WIDE_SPLIT = 512;
 
 // The values the block needs first come as leading scalar arguments, which
 // the compiler lets the hardware preload into SGPRs at wave launch (the
 // structs after them are read from the kernel-argument segment, a memory
 // round trip, while the score row is already on its way).
-template <typename T, int D, int GT, int ITEMS>
+template <typename T, int D, int GT, int ITEMS, int MAXS>
 __global__ __launch_bounds__(FS_THREADS) void k_select_attend(const float* scores, int64_t sld, const int32_t* seq_lens,
                                                               int max_len, int nsplit, int H_kv, AttnArgs a,
                                                               SelectArgs sa) {
   constexpr int NW = FS_THREADS / WAVE;
   constexpr bool MF = sizeof(T) == 2;  // bf16: MFMA split attention
-  // splits of at most FS_MAX_SPLIT entries: two attending waves of 32
-  using AttT = typename std::conditional<MF, AttnMfmaShared<D, GT, FS_MAX_SPLIT / 32>, AttnMergeShared<NW, GT, D>>::type;
+  // splits of at most MAXS entries: MAXS / 32 attending waves of 32 (all
+  // eight for wide splits, which take several rounds)
+  constexpr int NWA = MAXS / 32 < NW ? MAXS / 32 : NW;
+  static_assert(MAXS <= FS_MAX_SPLIT || MF, "wide splits attend on MFMA");
+  using AttT = typename std::conditional<MF, AttnMfmaShared<D, GT, NWA>, AttnMergeShared<NW, GT, D>>::type;
   struct SelPart {
     SelShared<NW> sm;
     KeyStore<FS_THREADS, ITEMS, true> ks;
@@ -48,7 +55,7 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(const float* score
     AttT att;  // used only after the selection is complete
   };
   __shared__ Shared u;
-  __shared__ int plist[FS_MAX_SPLIT];
+  __shared__ int plist[MAXS];
 
   const Shape& sh = a.sh;
   int blk = blockIdx.x;
@@ -89,28 +96,35 @@ __global__ __launch_bounds__(FS_THREADS) void k_select_attend(const float* score
     for (int k = m + (int)threadIdx.x; k < M; k += FS_THREADS) orow[k] = -1;
   __syncthreads();
   auto pos_of = [&](int i) { return plist[i - i0]; };
-  if constexpr (MF) attend_split_mfma<D, GT, FS_THREADS, FS_MAX_SPLIT / 32>(a, b, g, s, len, i0, i1, pos_of, u.att);
+  if constexpr (MF) attend_split_mfma<D, GT, FS_THREADS, NWA>(a, b, g, s, len, i0, i1, pos_of, u.att);
   else attend_split<T, D, GT, FS_THREADS, 2>(a, b, g, s, len, i0, i1, pos_of, u.att);
 }
 
 #define FS_LEAD (const float*)sa.scores, (int64_t)sa.ld, (const int32_t*)a.seq_lens, sa.max_len, a.nsplit, a.sh.H_kv
 
-template <typename T, int D, int ITEMS>
+template <typename T, int D, int ITEMS, int MAXS>
 static hipError_t launch_fs_tdi(const AttnArgs& a, const SelectArgs& sa, dim3 grid, hipStream_t st) {
   const int G = a.sh.H_q / a.sh.H_kv;
-  if (G <= 2) klaunch((k_select_attend<T, D, 2, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
-  else if (G <= 4) klaunch((k_select_attend<T, D, 4, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
-  else if (G <= 5) klaunch((k_select_attend<T, D, 5, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
-  else if (G <= 7) klaunch((k_select_attend<T, D, 7, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
-  else klaunch((k_select_attend<T, D, 8, ITEMS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  if (G <= 2) klaunch((k_select_attend<T, D, 2, ITEMS, MAXS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  else if (G <= 4) klaunch((k_select_attend<T, D, 4, ITEMS, MAXS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  else if (G <= 5) klaunch((k_select_attend<T, D, 5, ITEMS, MAXS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  else if (G <= 7) klaunch((k_select_attend<T, D, 7, ITEMS, MAXS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
+  else klaunch((k_select_attend<T, D, 8, ITEMS, MAXS>), grid, dim3(FS_THREADS), 0, st, FS_LEAD, a, sa);
   return hipGetLastError();
 }
 #undef FS_LEAD
 
 template <typename T, int D>
 static hipError_t launch_fs_td(const AttnArgs& a, const SelectArgs& sa, dim3 grid, hipStream_t st) {
-  if (sa.max_len <= FS_THREADS * 32) return launch_fs_tdi<T, D, 32>(a, sa, grid, st);
-  return launch_fs_tdi<T, D, 64>(a, sa, grid, st);
+  if (a.split_len > FS_MAX_SPLIT) {
+    if constexpr (sizeof(T) == 2 && D == 128) {
+      if (sa.max_len <= FS_THREADS * 32) return launch_fs_tdi<T, D, 32, FS_WIDE_SPLIT>(a, sa, grid, st);
+      return launch_fs_tdi<T, D, 64, FS_WIDE_SPLIT>(a, sa, grid, st);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (sa.max_len <= FS_THREADS * 32) return launch_fs_tdi<T, D, 32, FS_MAX_SPLIT>(a, sa, grid, st);
+  return launch_fs_tdi<T, D, 64, FS_MAX_SPLIT>(a, sa, grid, st);
 }
 
 template <typename T>
@@ -169,8 +183,17 @@ hipError_t launch_select_runs(const SelectArgs& sa, hipStream_t st) {
 constexpr size_t FS_MAX_BLOCKS = 256;
 
 bool select_attend_supported(const Shape& sh, int nsplit, int split_len) {
-  return sh.max_len <= FS_THREADS * 64 && split_len <= FS_MAX_SPLIT && nsplit <= AT_MAX_SPLITS &&
+  const bool wide_ok = sh.dtype != 0 && sh.d == 128 && split_len <= FS_WIDE_SPLIT;
+  return sh.max_len <= FS_THREADS * 64 && (split_len <= FS_MAX_SPLIT || wide_ok) && nsplit <= AT_MAX_SPLITS &&
          (size_t)sh.B * sh.H_kv * nsplit <= FS_MAX_BLOCKS;
+}
+
+int select_attend_wide_split(const Shape& sh, int positions) {
+  for (int sl = 2 * FS_MAX_SPLIT; sl <= FS_WIDE_SPLIT; sl *= 2) {
+    const int ns = (positions + sl - 1) / sl;
+    if (select_attend_supported(sh, ns, sl)) return sl;
+  }
+  return 0;
 }
 
 hipError_t launch_select_attend(const AttnArgs& a, const SelectArgs& sa, hipStream_t st) {

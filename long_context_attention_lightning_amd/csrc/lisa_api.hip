@@ -144,10 +144,24 @@ bool decode_fused(const Shape& sh, int nsplit, int split_len) {
   return select_attend_supported(sh, nsplit, split_len);
 }
 
+// Splits of the decode step's attention: decode_split's, or, where those
+// would take more fused select + attention blocks than the chip runs at once
+// (one per CU), the shortest wide split that fits the fused launch.
+void decode_step_split(const Shape& sh, int& nsplit, int& split_len) {
+  const int positions = sh.M < sh.max_len ? sh.M : sh.max_len;
+  decode_split(sh, positions, nsplit, split_len);
+  if ((sh.flags & LISA_SLIDING_WINDOW) || sh.M >= sh.max_len || decode_fused(sh, nsplit, split_len)) return;
+  const int wide = select_attend_wide_split(sh, positions);
+  if (wide) {
+    split_len = wide;
+    nsplit = (positions + wide - 1) / wide;
+  }
+}
+
 DecodeWs decode_ws(const Shape& sh) {
   DecodeWs w;
   Layout L;
-  decode_split(sh, sh.M < sh.max_len ? sh.M : sh.max_len, w.nsplit, w.split_len);
+  decode_step_split(sh, w.nsplit, w.split_len);
   w.scores = L.take((size_t)sh.B * decode_scores_ld(sh) * 4);
   w.idx = L.take((size_t)sh.B * sh.M * 4);
   w.o_lin = L.take((size_t)sh.B * sh.H_L * sh.d * 4);
@@ -684,7 +698,7 @@ int lisa_indexer_topk(const lisa_shape* shape, int rows_mode, int32_t n, const i
   if (dec) {
     // the core the decode step of this shape selects with
     int nsplit, split_len;
-    decode_split(sh, sh.M < sh.max_len ? sh.M : sh.max_len, nsplit, split_len);
+    decode_step_split(sh, nsplit, split_len);
     if (decode_fused(sh, nsplit, split_len)) {
       LAUNCH(KID_SELECT, st, launch_select_runs(sa, st));
       return LISA_OK;

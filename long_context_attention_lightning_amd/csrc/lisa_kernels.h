@@ -217,6 +217,9 @@ size_t attention_partial_floats(const Shape& sh, int n_rows, int nsplit);
 // Decode with few sequences: selection and split attention in one launch
 // (every split block selects the whole row; split partials as above).
 bool select_attend_supported(const Shape& sh, int nsplit, int split_len);
+// The shortest wide split (above 64 positions) with which a fused launch over
+// `positions` selected entries fits, or 0.
+int select_attend_wide_split(const Shape& sh, int positions);
 hipError_t launch_select_attend(const AttnArgs& a, const SelectArgs& sa, hipStream_t st);
 // the selection core of launch_select_attend alone (decode rows, full index lists)
 hipError_t launch_select_runs(const SelectArgs& sa, hipStream_t st);

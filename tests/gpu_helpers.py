@@ -115,12 +115,33 @@ def decode_split(P, B, H_kv):
     return sl, -(-P // sl)
 
 
-def decode_select_core(B, H_kv, d, M, max_len):
+def decode_step_split(B, H_kv, d, M, max_len, bf16=True):
+    """The decode step's attention splits (the library's rule): decode_split's,
+    or where those need more than 256 fused blocks, the shortest wide split
+    (128..512 positions, bf16 and head dim 128) that fits 256."""
+    P = min(M, max_len)
+    sl, ns = decode_split(P, B, H_kv)
+    if M >= max_len or _fused_fits(B, H_kv, d, max_len, sl, ns, bf16):
+        return sl, ns
+    w = 128
+    while w <= 512:
+        if _fused_fits(B, H_kv, d, max_len, w, -(-P // w), bf16):
+            return w, -(-P // w)
+        w *= 2
+    return sl, ns
+
+
+def _fused_fits(B, H_kv, d, max_len, sl, ns, bf16):
+    wide_ok = bf16 and d == 128 and sl <= 512
+    return max_len <= 32768 and (sl <= 64 or wide_ok) and ns <= 32 and B * H_kv * ns <= 256
+
+
+def decode_select_core(B, H_kv, d, M, max_len, bf16=True):
     """Which select core the decode step of this shape runs: 'runs' (inside
     the fused select + attention launch, few sequences with rows of up to
     32K) or 'general' (the separate select launch)."""
-    sl, ns = decode_split(min(M, max_len), B, H_kv)
-    if max_len <= 32768 and sl <= 64 and ns <= 32 and B * H_kv * ns <= 256:
+    sl, ns = decode_step_split(B, H_kv, d, M, max_len, bf16)
+    if _fused_fits(B, H_kv, d, max_len, sl, ns, bf16):
         return "runs"
     return "general"
 

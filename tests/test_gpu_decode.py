@@ -134,13 +134,15 @@ def test_decode_is_deterministic():
     assert np.array_equal(a["S"], b["S"]) and np.array_equal(a["idx"], b["idx"])
 
 
-@pytest.mark.parametrize("M", [512, 2048, 6000], ids=["fused select", "separate select", "every position"])
+@pytest.mark.parametrize("M", [512, 2048, 4600, 6000],
+                         ids=["fused select", "wide fused select", "separate select", "every position"])
 def test_decode_graph_replays_match_eager(M):
     """A decode step of eight sequences captured in a graph: every replay must
     reproduce the eager step bit for bit (output, index list, state, caches),
     with eager work (state resets) between the replays.  M = 512 takes the
-    fused select + attention, 2048 the separate select and gather, 6000
-    (>= every length) the path without scoring."""
+    fused select + attention with 64-position splits, 2048 the same launch
+    with 256-position splits on all eight waves, 4600 the separate select and
+    gather, 6000 (>= every length) the path without scoring."""
     cfg = QWEN7B_RAGGED_DECODE.replace(B=8, L_lo=1000, L_hi=5000, cap=5000)
     inp = decode_inputs(cfg, salt=78)
     seq = inp["seq_lens"]
@@ -191,7 +193,8 @@ def test_decode_graph_replays_match_eager(M):
     assert_state_close(host(e["S"]), host(e["z"]), ref["S"], ref["z"], f"eager decode M={M}")
 
 
-@pytest.mark.parametrize("M", [512, 2048, 6000], ids=["fused select", "separate select", "every position"])
+@pytest.mark.parametrize("M", [512, 2048, 4600, 6000],
+                         ids=["fused select", "wide fused select", "separate select", "every position"])
 def test_decode_without_index_list_matches(M):
     """idx_out is optional: without it the step must produce the same output,
     state and caches bit for bit (the fused kernel then keeps the selection in
