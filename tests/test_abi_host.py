@@ -51,7 +51,8 @@ def test_workspace_sizes(lib):
     assert dec > 16384 * 4          # holds at least one score row
     pre = L.lisa_workspace_bytes(sh, L.LISA_OP_PREFILL, 16384)
     assert pre > (16384 - 2048) * 16384 * 4
-    assert L.lisa_workspace_bytes(_qwen7b_decode_shape(B=32), L.LISA_OP_DECODE) > 30 * dec // 2
+    # batch 32: one score row per sequence at least
+    assert L.lisa_workspace_bytes(_qwen7b_decode_shape(B=32), L.LISA_OP_DECODE) > 32 * 16384 * 4
     assert L.lisa_workspace_bytes(sh, L.LISA_OP_DENSE_DECODE) > 0
     assert L.lisa_workspace_bytes(sh, L.LISA_OP_TOPK_PREFILL, 4096) > 0
     assert L.lisa_workspace_bytes(sh, 99) == 0

@@ -134,16 +134,20 @@ def test_decode_is_deterministic():
     assert np.array_equal(a["S"], b["S"]) and np.array_equal(a["idx"], b["idx"])
 
 
-@pytest.mark.parametrize("M", [512, 2048, 4600, 6000],
-                         ids=["fused select", "wide fused select", "separate select", "every position"])
-def test_decode_graph_replays_match_eager(M):
-    """A decode step of eight sequences captured in a graph: every replay must
-    reproduce the eager step bit for bit (output, index list, state, caches),
-    with eager work (state resets) between the replays.  M = 512 takes the
-    fused select + attention with 64-position splits, 2048 the same launch
-    with 256-position splits on all eight waves, 4600 the separate select and
-    gather, 6000 (>= every length) the path without scoring."""
-    cfg = QWEN7B_RAGGED_DECODE.replace(B=8, L_lo=1000, L_hi=5000, cap=5000)
+ROUTES = [(512, 8), (2048, 8), (2048, 40), (6000, 8)]
+ROUTE_IDS = ["fused select", "wide fused select", "separate select", "every position"]
+
+
+@pytest.mark.parametrize("M,B", ROUTES, ids=ROUTE_IDS)
+def test_decode_graph_replays_match_eager(M, B):
+    """A decode step captured in a graph: every replay must reproduce the
+    eager step bit for bit (output, index list, state, caches), with eager
+    work (state resets) between the replays.  Eight sequences at M = 512 take
+    the fused select + attention with 64-position splits, at 2048 the same
+    launch with 256-position splits on all eight waves; forty sequences at
+    2048 take the separate select and gather; M = 6000 (>= every length) the
+    path without scoring."""
+    cfg = QWEN7B_RAGGED_DECODE.replace(B=B, L_lo=1000, L_hi=5000, cap=5000)
     inp = decode_inputs(cfg, salt=78)
     seq = inp["seq_lens"]
     T = tdtype(cfg)
@@ -193,14 +197,13 @@ def test_decode_graph_replays_match_eager(M):
     assert_state_close(host(e["S"]), host(e["z"]), ref["S"], ref["z"], f"eager decode M={M}")
 
 
-@pytest.mark.parametrize("M", [512, 2048, 4600, 6000],
-                         ids=["fused select", "wide fused select", "separate select", "every position"])
-def test_decode_without_index_list_matches(M):
+@pytest.mark.parametrize("M,B", ROUTES, ids=ROUTE_IDS)
+def test_decode_without_index_list_matches(M, B):
     """idx_out is optional: without it the step must produce the same output,
     state and caches bit for bit (the fused kernel then keeps the selection in
     LDS, the separate select writes it to the workspace, and the path without
     scoring writes none)."""
-    cfg = QWEN7B_RAGGED_DECODE.replace(B=8, L_lo=1000, L_hi=5000, cap=5000)
+    cfg = QWEN7B_RAGGED_DECODE.replace(B=B, L_lo=1000, L_hi=5000, cap=5000)
     inp = decode_inputs(cfg, salt=79)
     seq = inp["seq_lens"]
     T = tdtype(cfg)

@@ -50,8 +50,8 @@ def test_noalloc_matches_workspace_step_twice_then_smaller():
 
 
 def test_noalloc_rejects_a_shape_beyond_the_scratch():
-    cfg = QWEN7B_RAGGED_DECODE  # batch 32 at up to 16K tokens needs far more than 4 MiB
-    sh = shape_of(cfg, max_len=16384, cap=16384, B=32)
+    cfg = QWEN7B_RAGGED_DECODE  # batch 32 at up to 32K tokens: its score rows alone take 4 MiB
+    sh = shape_of(cfg, max_len=32768, cap=32768, B=32)
     assert L.lisa_workspace_bytes(sh, L.LISA_OP_DECODE, 0) > L.LISA_DECODE_SCRATCH_BYTES
     import ctypes
     lib = L.library()  # the size check comes before any pointer is looked at
