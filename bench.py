@@ -388,8 +388,8 @@ TRAFFIC_KERNELS = {
     # fewer / at least N work-items of a kernel that serves two steps)
     "batched": {
         "k_decode_phase_a": ("decode_phase_a", ["k_decode.hip", "lisa_attend.h", "lisa_mfma.h"] + _COMMON),
-        "k_select": ("topm_select", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
-        "k_attention": ("gather_attention", ["k_decode.hip", "lisa_attend.h", "lisa_mfma.h"] + _COMMON),
+        "k_select_attend": ("select_attention", ["k_decode_fused.hip", "lisa_select.h", "lisa_attend.h",
+                                                 "lisa_mfma.h"] + _COMMON),
         "k_attn_combine": ("attention_combine", ["k_decode.hip", "lisa_attend.h", "lisa_mfma.h"] + _COMMON),
         "k_mass_logits_mfma": ("mass_logits", ["k_mass.hip", "lisa_mfma.h"] + _COMMON),
         "k_select_rows256": ("mass_select", ["k_select.hip", "lisa_select.h", "lisa_prefill.h"] + _COMMON),
