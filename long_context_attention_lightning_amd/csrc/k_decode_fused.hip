@@ -24,10 +24,10 @@ namespace lisa {
 
 constexpr int FS_THREADS = 512;  // 8 waves: 256 registers per lane, no spills
 constexpr int FS_MAX_SPLIT = 64;  // positions per split: two attending waves of 32
-// Wide splits (bf16, head dim 128): up to 1024 positions, every wave attends
+// Wide splits (bf16, head dim 128): up to 2048 positions, every wave attends
 // (32 entries per wave and round), for launches that would need more than one
 // block per CU with 64-position splits.
-constexpr int FS_WIDE_SPLIT = 1024;
+constexpr int FS_WIDE_SPLIT = 2048;
 
 // The values the block needs first come as leading scalar arguments, which
 // the compiler lets the hardware preload into SGPRs at wave launch (the

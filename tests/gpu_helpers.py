@@ -118,13 +118,13 @@ def decode_split(P, B, H_kv):
 def decode_step_split(B, H_kv, d, M, max_len, bf16=True):
     """The decode step's attention splits (the library's rule): decode_split's,
     or where those need more than 256 fused blocks, the shortest wide split
-    (128..1024 positions, bf16 and head dim 128) that fits 256."""
+    (128..2048 positions, bf16 and head dim 128) that fits 256."""
     P = min(M, max_len)
     sl, ns = decode_split(P, B, H_kv)
     if M >= max_len or _fused_fits(B, H_kv, d, max_len, sl, ns, bf16):
         return sl, ns
     w = 128
-    while w <= 1024:
+    while w <= 2048:
         if _fused_fits(B, H_kv, d, max_len, w, -(-P // w), bf16):
             return w, -(-P // w)
         w *= 2
@@ -132,7 +132,7 @@ def decode_step_split(B, H_kv, d, M, max_len, bf16=True):
 
 
 def _fused_fits(B, H_kv, d, max_len, sl, ns, bf16):
-    wide_ok = bf16 and d == 128 and sl <= 1024
+    wide_ok = bf16 and d == 128 and sl <= 2048
     return max_len <= 32768 and (sl <= 64 or wide_ok) and ns <= 32 and B * H_kv * ns <= 256
 
 
