@@ -1,18 +1,20 @@
-// Fused top-M selection and gathered attention for decode steps of a few
-// sequences ("LISA", arXiv 2607.19358v1, Section 3.2 Stage 2: each query
-// keeps the M cached positions that score highest under the indexer, its
-// heads' scores added, and softmax attention runs over those rows only).
+// Fused top-M selection and gathered attention for decode steps
+// ("LISA", arXiv 2607.19358v1, Section 3.2 Stage 2: each query keeps the M
+// cached positions that score highest under the indexer, its heads' scores
+// added, and softmax attention runs over those rows only).
 //
-// With one or a few sequences a separate select kernel runs one block per
-// row: one CU has to pull the whole score row in, at the rate its own memory
-// parallelism allows, and the gather kernel after it waits for another
-// launch and for the index list to travel through memory.  Here every
-// (sequence, KV head, split) block selects the whole row itself.  The
-// selection is exact and deterministic, so all blocks of a row agree.  Each
-// block keeps the positions of its own split of the ascending selection in
-// LDS and gathers them right away; the blocks of a row read the same score
-// row concurrently from the shared caches.  Each block writes its own slice of
-// the index list (KV head 0), so no block writes the whole list.
+// A separate select kernel runs one block per row: one CU has to pull the
+// whole score row in, at the rate its own memory parallelism allows, and the
+// gather kernel after it waits for another launch and for the index list to
+// travel through memory.  Here every (sequence, KV head, split) block selects
+// the whole row itself.  The selection is exact and deterministic, so all
+// blocks of a row agree.  Each block keeps the positions of its own split of
+// the ascending selection in LDS and gathers them right away; the blocks of a
+// row read the same score row concurrently from the shared caches.  Each
+// block writes its own slice of the index list (KV head 0), so no block
+// writes the whole list.  The launch is used while its blocks fit one per CU
+// (with 64-position splits for a few sequences, with wide splits of up to
+// 2048 positions for batches of tens of sequences).
 #include <type_traits>
 
 #include "lisa_attend.h"
