@@ -229,3 +229,22 @@ def test_decode_without_index_list_matches(M, B):
     for a, b in zip(k1, k2):
         assert torch.equal(a, b)
     assert_out_close(cfg, host(o2), oracle.decode_step(inp, M)["out"], f"no index list M={M}")
+
+
+@pytest.mark.parametrize("H_q", [16, 32, 64], ids=["G2", "G4", "G8"])
+@pytest.mark.parametrize("B", [2, 8], ids=["narrow splits", "wide splits"])
+def test_decode_fused_routes_gqa_groups(B, H_q):
+    """The fused select + attention at 8 KV heads with 2, 4 and 8 query heads
+    per KV head: two sequences take 64-position splits, eight take wide
+    splits (256 positions on all eight waves) so that the launch stays at one
+    block per CU; both against the oracle."""
+    from gpu_helpers import decode_select_core, decode_step_split
+    cfg = QWEN7B_RAGGED_DECODE.replace(B=B, L_lo=1500, L_hi=4000, cap=4000, H_q=H_q, H_kv=8, H_L=H_q,
+                                       hidden=512)
+    M = 1024
+    inp = decode_inputs(cfg, seed_id=30 + H_q)
+    L_max = int(inp["seq_lens"].max())
+    sl, ns = decode_step_split(B, 8, cfg.d, M, L_max)
+    assert decode_select_core(B, 8, cfg.d, M, L_max) == "runs"
+    assert (sl > 64) == (B == 8), (sl, ns)
+    _parity(cfg, inp, M, f"G={H_q // 8} B={B} split {sl}")
